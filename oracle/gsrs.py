@@ -1,0 +1,162 @@
+"""GSRS fused block importance and Top-p selection, fp64 (test infrastructure only).
+
+Restates "Sparse Attention for Video Generation Acceleration via Growing
+Sparsity and Reduced Search" (GSRS).  The page's display equations were lost in
+extraction; the readings below follow its prose:
+
+* Phase 1 (§5.3, Appendix A.2): for query row i and evaluated key block v,
+  G_iv = m_iv + log r_iv with m_iv the block maximum of z_ij over the valid keys
+  of v and r_iv = sum_j exp(z_ij - m_iv); this is the block log-sum-exp.  A block
+  without valid keys gives -inf.
+* Row normaliser: L_i = log sum over all evaluated keys of exp(z_ij).
+* Phase 2: W_uv = (1 / B_u) sum over the valid rows i of query block u of
+  exp(G_iv - L_i), B_u the number of valid rows; rows with L_i = -inf add 0
+  (note on fully masked rows to Algorithm 2).  Hence sum_v W_uv = 1.
+* Top-p (Algorithm 3, "retained until their cumulative importance exceeds a
+  threshold p"): candidates of a row sorted by descending W (equal W: lower
+  block id first); the running total is accumulated in fp64 in that order and a
+  block is kept while the total *before* it is <= p, so the block whose
+  addition first takes the total above p is the last one kept.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def _valid_keys(v: int, seq_len: int, block: int) -> np.ndarray:
+    return np.arange(v * block, min((v + 1) * block, seq_len))
+
+
+def block_lse(q: np.ndarray, k: np.ndarray, row_ptr: np.ndarray, col_idx: np.ndarray,
+              seq_len: int, block: int, scale: float):
+    """Phase 1: G [nnz, block] (CSR order) and the row LSE [H, L_pad] over the evaluated keys.
+
+    Query rows >= L are NaN in both outputs.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    H, lp, _ = q.shape
+    mb = lp // block
+    nnz = int(row_ptr[-1])
+    g = np.full((nnz, block), np.nan)
+    lse = np.full((H, lp), np.nan)
+    for h in range(H):
+        for u in range(mb):
+            r0, r1 = u * block, min((u + 1) * block, seq_len)
+            if r1 <= r0:
+                continue
+            lo, hi = int(row_ptr[h * mb + u]), int(row_ptr[h * mb + u + 1])
+            if hi == lo:
+                lse[h, r0:r1] = -np.inf
+                continue
+            qs = q[h, r0:r1]
+            allz = []
+            for e in range(lo, hi):
+                keys = _valid_keys(int(col_idx[e]), seq_len, block)
+                z = scale * (qs @ k[h, keys].T)
+                allz.append(z)
+                if keys.size == 0:
+                    g[e, : r1 - r0] = -np.inf
+                    continue
+                m = z.max(axis=1)
+                g[e, : r1 - r0] = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+            z = np.concatenate(allz, axis=1)
+            m = z.max(axis=1)
+            lse[h, r0:r1] = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+    return g, lse
+
+
+def block_importance(g: np.ndarray, lse: np.ndarray, row_ptr: np.ndarray, seq_len: int,
+                     block: int) -> np.ndarray:
+    """Phase 2: W [nnz] from G and the row LSE."""
+    H, lp = lse.shape
+    mb = lp // block
+    w = np.zeros(g.shape[0])
+    for h in range(H):
+        for u in range(mb):
+            r0, r1 = u * block, min((u + 1) * block, seq_len)
+            nrows = r1 - r0
+            if nrows <= 0:
+                continue
+            l_rows = np.asarray(lse[h, r0:r1], dtype=np.float64)
+            live = np.isfinite(l_rows)
+            for e in range(int(row_ptr[h * mb + u]), int(row_ptr[h * mb + u + 1])):
+                gi = np.asarray(g[e, :nrows], dtype=np.float64)
+                terms = np.where(live, np.exp(np.where(live, gi - l_rows, 0.0)), 0.0)
+                terms = np.where(np.isneginf(gi), 0.0, terms)
+                w[e] = terms.sum() / nrows
+    return w
+
+
+def block_importance_from_probs(q: np.ndarray, k: np.ndarray, row_ptr: np.ndarray,
+                                col_idx: np.ndarray, seq_len: int, block: int,
+                                scale: float) -> np.ndarray:
+    """W from explicit attention probabilities A_ij = exp(z_ij - L_i) (GSRS eq. (5)).
+
+    The block importance as defined: the attention weight of row i on the keys
+    of block v, normalised over the evaluated keys, averaged over the rows of u.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    H, lp, _ = q.shape
+    mb = lp // block
+    w = np.zeros(int(row_ptr[-1]))
+    for h in range(H):
+        for u in range(mb):
+            r0, r1 = u * block, min((u + 1) * block, seq_len)
+            lo, hi = int(row_ptr[h * mb + u]), int(row_ptr[h * mb + u + 1])
+            if r1 <= r0 or hi == lo:
+                continue
+            blocks = [int(col_idx[e]) for e in range(lo, hi)]
+            keys = np.concatenate([_valid_keys(v, seq_len, block) for v in blocks])
+            z = scale * (q[h, r0:r1] @ k[h, keys].T)
+            z = z - z.max(axis=1, keepdims=True)
+            a = np.exp(z)
+            a = a / a.sum(axis=1, keepdims=True)
+            col = 0
+            for e, v in zip(range(lo, hi), blocks):
+                n = _valid_keys(v, seq_len, block).size
+                w[e] = a[:, col:col + n].sum() / (r1 - r0)
+                col += n
+    return w
+
+
+def cached_lse_scores(g: np.ndarray, lse_old: np.ndarray, row_ptr: np.ndarray,
+                      seq_len: int, block: int) -> np.ndarray:
+    """Per-row block scores exp(G_iv - L_i^old) with a stale row normaliser.
+
+    GSRS Appendix (AdaSpa comparison): these sum to exp(L_i - L_i^old) per row,
+    not to 1.  Returned as [nnz, block] (NaN on padding rows).
+    """
+    H, lp = lse_old.shape
+    mb = lp // block
+    s = np.full(g.shape, np.nan)
+    for h in range(H):
+        for u in range(mb):
+            r0, r1 = u * block, min((u + 1) * block, seq_len)
+            for e in range(int(row_ptr[h * mb + u]), int(row_ptr[h * mb + u + 1])):
+                s[e, : r1 - r0] = np.exp(g[e, : r1 - r0] - lse_old[h, r0:r1])
+    return s
+
+
+def topp_select(w: np.ndarray, row_ptr: np.ndarray, col_idx: np.ndarray, heads: int,
+                mb: int, nb: int, p: float) -> np.ndarray:
+    """GSRS Algorithm 3 per query-block row: mask [H, MB, NB] of the kept blocks."""
+    out = np.zeros((heads, mb, nb), dtype=np.uint8)
+    w = np.asarray(w)
+    for h in range(heads):
+        for u in range(mb):
+            lo, hi = int(row_ptr[h * mb + u]), int(row_ptr[h * mb + u + 1])
+            if hi == lo:
+                continue
+            cand = np.asarray(col_idx[lo:hi], dtype=np.int64)
+            ww = w[lo:hi].astype(np.float64)
+            order = np.lexsort((cand, -ww))  # by -W, then by block id
+            acc = 0.0
+            for j in order:
+                if acc > p:
+                    break
+                out[h, u, cand[j]] = 1
+                acc += float(ww[j])
+    return out

@@ -1,0 +1,154 @@
+"""Pins of the GSRS oracle (fused block importance and Top-p).
+
+* sum_v W_uv = 1 for every query block with a non-empty candidate set (GSRS,
+  Appendix A.2).
+* W from G and the row LSE equals W computed from explicit attention
+  probabilities (the definition of block importance).
+* G and the row LSE against scipy.special.logsumexp; log sum_v exp(G_iv) = L_i.
+* Negative test: a stale row normaliser (AdaSpa's cached LSE) gives per-row
+  sums exp(L_i - L_i_old) != 1.
+* Top-p: brute force over prefixes, one-hot and uniform weights, p = 1 keeps
+  everything, a second selection restricted to the first selection is a subset.
+"""
+
+import math
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp
+
+import oracle
+
+
+def _case(seed, H=2, L=200, d=16, b=32, density=0.5, empty=(2,)):
+    rng = np.random.default_rng(seed)
+    nb = -(-L // b)
+    lp = nb * b
+    q, k = (np.zeros((H, lp, d)) for _ in range(2))
+    q[:, :L] = rng.standard_normal((H, L, d)) * 1.5
+    k[:, :L] = rng.standard_normal((H, L, d))
+    mask = (rng.random((H, nb, nb)) < density).astype(np.uint8)
+    for r in empty:
+        mask[:, r] = 0
+    return q, k, mask, L, b, 1.0 / math.sqrt(d)
+
+
+def test_block_weights_sum_to_one_and_match_probabilities():
+    q, k, mask, L, b, s = _case(1)
+    row_ptr, col_idx, _, _, _ = oracle.block_index(mask)
+    g, lse = oracle.block_lse(q, k, row_ptr, col_idx, L, b, s)
+    w = oracle.block_importance(g, lse, row_ptr, L, b)
+    wp = oracle.block_importance_from_probs(q, k, row_ptr, col_idx, L, b, s)
+    np.testing.assert_allclose(w, wp, rtol=0, atol=1e-13)
+    H, mb = mask.shape[0], mask.shape[1]
+    for r in range(H * mb):
+        lo, hi = row_ptr[r], row_ptr[r + 1]
+        if hi > lo:
+            assert abs(w[lo:hi].sum() - 1.0) < 1e-12
+    # the empty query block has -inf LSE on its valid rows
+    assert np.all(np.isneginf(lse[:, 2 * b:3 * b]))
+
+
+def test_block_lse_against_logsumexp():
+    q, k, mask, L, b, s = _case(2, H=1, L=150, empty=())
+    row_ptr, col_idx, _, _, _ = oracle.block_index(mask)
+    g, lse = oracle.block_lse(q, k, row_ptr, col_idx, L, b, s)
+    mb = mask.shape[1]
+    for u in range(mb):
+        r0, r1 = u * b, min((u + 1) * b, L)
+        lo, hi = row_ptr[u], row_ptr[u + 1]
+        if hi == lo:
+            continue
+        for e in range(lo, hi):
+            v = col_idx[e]
+            keys = np.arange(v * b, min((v + 1) * b, L))
+            z = s * q[0, r0:r1] @ k[0, keys].T
+            np.testing.assert_allclose(g[e, :r1 - r0], logsumexp(z, axis=1), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(logsumexp(g[lo:hi, :r1 - r0], axis=0), lse[0, r0:r1],
+                                   rtol=0, atol=1e-12)
+    # the row LSE is the attention oracle's LSE
+    _, lse2 = oracle.masked_attention(q, k, k, mask, L, b, s)
+    np.testing.assert_allclose(lse[0, :L], lse2[0, :L], rtol=0, atol=1e-12)
+
+
+def test_cached_lse_scores_do_not_sum_to_one():
+    q, k, mask, L, b, s = _case(3, H=1, empty=())
+    row_ptr, col_idx, _, _, _ = oracle.block_index(mask)
+    g, lse = oracle.block_lse(q, k, row_ptr, col_idx, L, b, s)
+    _, lse_old = oracle.block_lse(q * 0.8, k, row_ptr, col_idx, L, b, s)
+    sc = oracle.cached_lse_scores(g, lse_old, row_ptr, L, b)
+    mb = mask.shape[1]
+    u = int(np.flatnonzero(np.diff(row_ptr) > 0)[0])
+    r0 = u * b
+    rowsum = np.nansum(sc[row_ptr[u]:row_ptr[u + 1]], axis=0)[:b]
+    alpha = np.exp(lse[0, r0:r0 + b] - lse_old[0, r0:r0 + b])
+    np.testing.assert_allclose(rowsum, alpha, rtol=1e-12)
+    assert np.max(np.abs(rowsum - 1.0)) > 1e-3
+    assert mb > 0
+
+
+def _brute_topp(w, p):
+    """Shortest prefix of the sorted order whose sum exceeds p (all if none)."""
+    order = sorted(range(len(w)), key=lambda j: (-w[j], j))
+    for n in range(1, len(order) + 1):
+        total = 0.0
+        for j in order[:n]:
+            total += float(w[j])
+        if total > p:
+            return set(order[:n])
+    return set(order)
+
+
+def _one_row(w, p):
+    w = np.asarray(w, dtype=np.float32)
+    row_ptr = np.array([0, len(w)])
+    col = np.arange(len(w))
+    m = oracle.topp_select(w, row_ptr, col, 1, 1, len(w), p)
+    return set(np.flatnonzero(m[0, 0]).tolist())
+
+
+def test_topp_against_prefix_brute_force():
+    rng = np.random.default_rng(4)
+    for trial in range(200):
+        n = int(rng.integers(1, 12))
+        w = rng.random(n).astype(np.float32)
+        if trial % 3 == 0:
+            w[rng.integers(0, n, size=n // 2)] = w[0]      # ties
+        w = (w / w.sum()).astype(np.float32)
+        p = float(rng.choice([0.3, 0.5, 0.8, 0.9, 0.95]))
+        assert _one_row(w, p) == _brute_topp(w, p)
+
+
+def test_topp_special_cases():
+    assert _one_row([0, 0, 1, 0], 0.9) == {2}
+    assert _one_row([0.25, 0.25, 0.25, 0.25], 1.0) == {0, 1, 2, 3}
+    # equal weights: ties go to the lower block id
+    assert _one_row([0.25, 0.25, 0.25, 0.25], 0.3) == {0, 1}
+    # exactly p after two blocks: "exceeds p" needs the third
+    assert _one_row([0.25, 0.25, 0.25, 0.25], 0.5) == {0, 1, 2}
+    # uniform float32 weights: the fp64 running sum of float32(1/100) stays below 0.9
+    # after 90 blocks, so the 91st is the one that crosses
+    assert len(_one_row([np.float32(0.01)] * 100, 0.9)) == 91
+
+
+def test_topp_restricted_to_candidates_is_subset():
+    q, k, mask, L, b, s = _case(5, H=2, L=256, density=0.7, empty=())
+    row_ptr, col_idx, _, _, _ = oracle.block_index(mask)
+    g, lse = oracle.block_lse(q, k, row_ptr, col_idx, L, b, s)
+    w = oracle.block_importance(g, lse, row_ptr, L, b).astype(np.float32)
+    H, mb, nb = mask.shape
+    s1 = oracle.topp_select(w, row_ptr, col_idx, H, mb, nb, 0.9)
+    assert np.all(s1 <= mask)
+    rp1, ci1, _, _, _ = oracle.block_index(s1)
+    g1, l1 = oracle.block_lse(q, k, rp1, ci1, L, b, s)
+    w1 = oracle.block_importance(g1, l1, rp1, L, b).astype(np.float32)
+    s2 = oracle.topp_select(w1, rp1, ci1, H, mb, nb, 0.8)
+    assert np.all(s2 <= s1)
+    assert s2.sum() < s1.sum()
+
+
+@pytest.mark.parametrize("p", [0.0, 1.0])
+def test_topp_extremes(p):
+    w = np.array([0.1, 0.6, 0.3], dtype=np.float32)
+    got = _one_row(w, p)
+    assert got == ({1} if p == 0.0 else {0, 1, 2})

@@ -1,0 +1,61 @@
+"""Input generators: determinism, shapes, densities, token-order properties."""
+
+import numpy as np
+import torch
+
+import synth
+
+
+def test_tiny_workload_recipe():
+    w = synth.make_workload("tiny")
+    assert w.q.shape == (1, 1024, 64) and w.q.dtype == torch.bfloat16
+    assert w.mask.shape == (1, 16, 16)
+    assert int(w.mask[0, 7].sum()) == 0
+    diag = torch.diagonal(w.mask[0])
+    assert int(diag.sum()) == 15          # all but the fully masked block 7
+    assert 0.4 < float(w.mask.float().mean()) < 0.65
+    w2 = synth.make_workload("tiny")
+    assert torch.equal(w.q, w2.q) and torch.equal(w.mask, w2.mask) and torch.equal(w.x0, w2.x0)
+    assert float(w.x0.min()) >= -1.0 and float(w.x0.max()) < 1.0
+
+
+def test_layer16k_density_and_padding():
+    w = synth.make_workload("layer16k", heads=3)
+    assert w.q.shape == (3, 16384, 128)
+    dens = float(w.mask.float().mean())
+    assert 0.17 < dens < 0.23
+    nnz = w.mask.sum(-1)
+    assert int(nnz.min()) >= 9 and int(nnz.max()) > 2 * int(nnz.min())
+    assert torch.all(torch.diagonal(w.mask, dim1=1, dim2=2) == 1)
+
+
+def test_wan_shape_padding_and_topk():
+    w = synth.make_workload("wan75k", heads=2)
+    assert w.seq_len == 75600 and w.q.shape == (2, 75648, 128)
+    assert torch.all(w.q[:, 75600:] == 0) and torch.all(w.v[:, 75600:] == 0)
+    nb = 591
+    assert w.mask.shape == (2, nb, nb)
+    for h in range(2):
+        nnz = w.mask[h].sum(-1)
+        assert torch.all(torch.diagonal(w.mask[h]) == 1)
+        # k per head in [30, 147], plus the diagonal when it is not among the top k
+        assert 30 <= int(nnz.min()) and int(nnz.max()) <= 148
+        assert int(nnz.max()) - int(nnz.min()) <= 1
+
+
+def test_video_hilbert_order_is_a_local_bijection():
+    o = synth.video_hilbert_order(33, 45, 80)
+    assert np.array_equal(np.sort(o), np.arange(33 * 45 * 80))
+    t, y, x = o // 3600, (o % 3600) // 80, o % 80
+    step = np.abs(np.diff(t)) + np.abs(np.diff(y)) + np.abs(np.diff(x))
+    assert (step == 1).mean() >= 0.95
+    for w_, h_ in ((80, 45), (7, 5), (1, 9), (12, 1)):
+        cells = synth.gilbert2d(w_, h_)
+        assert len(set(cells)) == w_ * h_
+
+
+def test_random_tiny_case():
+    w = synth.random_tiny_case(3, heads=2, seq_len=300, block=64, empty_rows=(1,))
+    assert w.q.shape == (2, 320, 64)
+    assert int(w.mask[:, 1].sum()) == 0
+    assert torch.all(w.q[:, 300:] == 0)
