@@ -1,0 +1,161 @@
+// Block index of a block mask: per-query-block K/V lists (CSR) and the transposed
+// lists (CSC).  WaveAlign §II-B/§II-C: mask row i names the K/V blocks query block
+// i visits in the kernel's inner loop; the row sum is its workload.
+//
+// Integer work, bit-exact by construction: row and column lists are emitted in
+// ascending order with wavefront ballots, counts are exact and the prefix sums
+// are single-workgroup scans.
+#include "wa_internal.h"
+
+namespace wa {
+namespace {
+
+constexpr int kWave = 64;
+
+__device__ inline uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & (kWave - 1);
+  return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+}
+
+// One wavefront per mask row: row_nnz[r] = number of non-zero bytes.
+__global__ __launch_bounds__(256) void k_row_counts(const uint8_t* __restrict__ mask, int rows,
+                                                    int NB, int32_t* __restrict__ row_nnz) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const uint8_t* m = mask + (size_t)r * NB;
+  int cnt = 0;
+  for (int v0 = 0; v0 < NB; v0 += kWave) {
+    const int v = v0 + lane;
+    const bool bit = v < NB && m[v] != 0;
+    cnt += __popcll(__ballot(bit));
+  }
+  if (lane == 0) row_nnz[r] = cnt;
+}
+
+// One thread per (head, column): csc count of column v, written to cnt[h*NB + v].
+__global__ __launch_bounds__(256) void k_col_counts(const uint8_t* __restrict__ mask, int H,
+                                                    int MB, int NB, int32_t* __restrict__ cnt) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= H * NB) return;
+  const int h = t / NB, v = t % NB;
+  const uint8_t* m = mask + (size_t)h * MB * NB + v;
+  int c = 0;
+  for (int u = 0; u < MB; ++u) c += m[(size_t)u * NB] != 0;
+  cnt[t] = c;
+}
+
+// Exclusive prefix sum of n counts into ptr[0..n] (ptr may alias cnt).  One
+// workgroup of 1024 threads; each thread scans a contiguous chunk.
+__global__ __launch_bounds__(1024) void k_exclusive_scan(const int32_t* cnt, int32_t* ptr, int n) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  const int chunk = (n + 1023) / 1024;
+  const int lo = min(n, t * chunk), hi = min(n, lo + chunk);
+  int32_t s = 0;
+  for (int i = lo; i < hi; ++i) s += cnt[i];
+  part[t] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan of the 1024 partial sums.
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t add = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
+  }
+  int32_t run = part[t] - s;  // exclusive prefix of this chunk
+  for (int i = lo; i < hi; ++i) {
+    const int32_t c = cnt[i];
+    ptr[i] = run;
+    run += c;
+  }
+  if (t == 1023) ptr[n] = part[1023];
+}
+
+// One wavefront per row: ascending column ids of the non-zero bytes.
+__global__ __launch_bounds__(256) void k_fill_rows(const uint8_t* __restrict__ mask, int rows,
+                                                   int NB, const int32_t* __restrict__ row_ptr,
+                                                   int32_t* __restrict__ col_idx, int64_t cap) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const uint8_t* m = mask + (size_t)r * NB;
+  int64_t base = row_ptr[r];
+  const uint64_t lt = lanemask_lt();
+  for (int v0 = 0; v0 < NB; v0 += kWave) {
+    const int v = v0 + lane;
+    const bool bit = v < NB && m[v] != 0;
+    const uint64_t b = __ballot(bit);
+    if (bit) {
+      const int64_t idx = base + __popcll(b & lt);
+      if (idx < cap) col_idx[idx] = v;
+    }
+    base += __popcll(b);
+  }
+}
+
+// One workgroup per (head, 64-column tile): ascending row ids per column.  The
+// tile of 64 rows x 64 columns is staged in LDS so that global reads stay
+// row-contiguous; each wavefront then owns 16 columns and walks them with ballots
+// over the 64 rows of the tile.
+__global__ __launch_bounds__(256) void k_fill_cols(const uint8_t* __restrict__ mask, int H, int MB,
+                                                   int NB, const int32_t* __restrict__ csc_ptr,
+                                                   int32_t* __restrict__ csc_idx, int64_t cap) {
+  __shared__ uint8_t tile[64][65];
+  const int tiles_per_head = (NB + 63) / 64;
+  const int h = blockIdx.x / tiles_per_head;
+  const int v0 = (blockIdx.x % tiles_per_head) * 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t lt = lanemask_lt();
+  int64_t base[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int v = v0 + wave + 4 * j;
+    base[j] = v < NB ? csc_ptr[h * NB + v] : 0;
+  }
+  const uint8_t* mh = mask + (size_t)h * MB * NB;
+  for (int u0 = 0; u0 < MB; u0 += 64) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+      const int uu = e >> 6, vv = e & 63;
+      const int u = u0 + uu, v = v0 + vv;
+      tile[uu][vv] = (u < MB && v < NB) ? (mh[(size_t)u * NB + v] != 0) : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int vv = wave + 4 * j;
+      const bool bit = tile[lane][vv] != 0;
+      const uint64_t b = __ballot(bit);
+      if (bit) {
+        const int64_t idx = base[j] + __popcll(b & lt);
+        if (idx < cap) csc_idx[idx] = u0 + lane;
+      }
+      base[j] += __popcll(b);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_block_index(const uint8_t* mask, int H, int MB, int NB, int32_t* row_ptr,
+                              int32_t* col_idx, int64_t col_cap, int32_t* row_nnz,
+                              int32_t* csc_ptr, int32_t* csc_idx, int64_t csc_cap,
+                              hipStream_t s) {
+  const int rows = H * MB;
+  hipLaunchKernelGGL(k_row_counts, dim3((rows + 3) / 4), dim3(256), 0, s, mask, rows, NB, row_nnz);
+  hipLaunchKernelGGL(k_exclusive_scan, dim3(1), dim3(1024), 0, s, row_nnz, row_ptr, rows);
+  hipLaunchKernelGGL(k_fill_rows, dim3((rows + 3) / 4), dim3(256), 0, s, mask, rows, NB, row_ptr,
+                     col_idx, col_cap);
+  if (csc_ptr != nullptr) {
+    const int cols = H * NB;
+    hipLaunchKernelGGL(k_col_counts, dim3((cols + 255) / 256), dim3(256), 0, s, mask, H, MB, NB,
+                       csc_ptr);
+    hipLaunchKernelGGL(k_exclusive_scan, dim3(1), dim3(1024), 0, s, csc_ptr, csc_ptr, cols);
+    hipLaunchKernelGGL(k_fill_cols, dim3(H * ((NB + 63) / 64)), dim3(256), 0, s, mask, H, MB, NB,
+                       csc_ptr, csc_idx, csc_cap);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace wa

@@ -1,0 +1,435 @@
+// WaveAlign two-stage query-row reordering on the GPU (WaveAlign §IV-C, §IV-D,
+// §IV-E; Algorithms 1 and 2), one workgroup of 1024 threads per head.
+//
+//  1. statistics and the adaptive skip decision (§IV-E);
+//  2. rank-2 embedding of the column-centered mask by matrix-free centered subspace
+//     iteration (§IV-C-2, Algorithm 1): Y = M^T X - c (1^T X)/MB and
+//     Z = M Y - 1 (c^T Y)/MB with the CSC and CSR lists (gathers only, so every sum
+//     has a fixed order), modified Gram-Schmidt QR, then the Ritz rotation that
+//     orders the basis by singular value;
+//  3. polar angles (eq. (4)) and a stable ascending sort (Stage 1);
+//  4. buckets of at most W positions inside contiguous slices, and a stable
+//     NNZ-descending sort inside each bucket (§IV-D, Stage 2).
+//
+// Arithmetic is fp64 (MI355X runs fp64 vector code at half the fp32 rate; the
+// whole stage is a few MFLOP per head), so the angles agree with an fp64 reference
+// to rounding.  All reductions use a fixed shuffle tree, so results are bitwise
+// reproducible run to run.  The Stage-1 and Stage-2 orders are one bitonic sort
+// each of unique 64-bit keys in LDS.
+#include <math.h>
+
+#include "wa_internal.h"
+
+namespace wa {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr double kTwoPi = 6.283185307179586;
+
+struct DevParams {
+  int wave, n_slices, iters, stage1, stage2, skip_mode;
+  double ws_min, flops_min, jac_max;
+};
+
+// Block-wide sum of one or two doubles; every thread returns the same value.
+// `red` holds 2 * kWaves doubles.
+__device__ inline double2 block_sum2(double2 v, double* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    v.x += __shfl_xor(v.x, off);
+    v.y += __shfl_xor(v.y, off);
+  }
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) {
+    red[2 * w] = v.x;
+    red[2 * w + 1] = v.y;
+  }
+  __syncthreads();
+  double2 s = make_double2(0.0, 0.0);
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    s.x += red[2 * i];
+    s.y += red[2 * i + 1];
+  }
+  return s;
+}
+
+__device__ inline double block_sum(double v, double* red) {
+  return block_sum2(make_double2(v, 0.0), red).x;
+}
+
+__device__ inline long long block_sum_i64(long long v, long long* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  long long s = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) s += red[i];
+  return s;
+}
+
+__device__ inline int block_min_i32(int v, int* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  int s = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) s = min(s, red[i]);
+  return s;
+}
+
+// Q factor of the MB x 2 block in x (in place): modified Gram-Schmidt with a
+// positive diagonal; a second column whose orthogonalised norm is <= 1e-12 of the
+// first column's norm becomes zero; a zero first column zeroes both.
+__device__ void qr2_inplace(double2* x, int MB, double* red) {
+  const int t = threadIdx.x;
+  double s1 = 0.0;
+  for (int u = t; u < MB; u += kThreads) s1 += x[u].x * x[u].x;
+  const double n1 = sqrt(block_sum(s1, red));
+  if (n1 == 0.0) {
+    for (int u = t; u < MB; u += kThreads) x[u] = make_double2(0.0, 0.0);
+    __syncthreads();
+    return;
+  }
+  double s12 = 0.0;
+  for (int u = t; u < MB; u += kThreads) {
+    const double q1 = x[u].x / n1;
+    x[u].x = q1;
+    s12 += q1 * x[u].y;
+  }
+  const double r12 = block_sum(s12, red);
+  double s2 = 0.0;
+  for (int u = t; u < MB; u += kThreads) {
+    const double w = x[u].y - r12 * x[u].x;
+    x[u].y = w;
+    s2 += w * w;
+  }
+  const double n2 = sqrt(block_sum(s2, red));
+  const bool keep = n2 > 1e-12 * n1;
+  for (int u = t; u < MB; u += kThreads) x[u].y = keep ? x[u].y / n2 : 0.0;
+  __syncthreads();
+}
+
+// Y = M^T X - c (1^T X) / MB, reading X and writing Y (LDS).
+__device__ void apply_mt(const double2* x, double2* y, const int32_t* __restrict__ cp,
+                         const int32_t* __restrict__ ci, int cap, int MB, int NB, double* red) {
+  const int t = threadIdx.x;
+  double2 s = make_double2(0.0, 0.0);
+  for (int u = t; u < MB; u += kThreads) {
+    s.x += x[u].x;
+    s.y += x[u].y;
+  }
+  s = block_sum2(s, red);
+  const double inv = 1.0 / (double)MB;
+  for (int v = t; v < NB; v += kThreads) {
+    const int lo = min(cp[v], cap), hi = min(cp[v + 1], cap);
+    double ax = 0.0, ay = 0.0;
+    int k = lo;
+    for (; k + 4 <= hi; k += 4) {
+      const int u0 = ci[k], u1 = ci[k + 1], u2 = ci[k + 2], u3 = ci[k + 3];
+      ax += x[u0].x; ay += x[u0].y;
+      ax += x[u1].x; ay += x[u1].y;
+      ax += x[u2].x; ay += x[u2].y;
+      ax += x[u3].x; ay += x[u3].y;
+    }
+    for (; k < hi; ++k) {
+      const int u = ci[k];
+      ax += x[u].x;
+      ay += x[u].y;
+    }
+    const double c = (double)(hi - lo);
+    y[v] = make_double2(ax - c * s.x * inv, ay - c * s.y * inv);
+  }
+  __syncthreads();
+}
+
+// Z = M Y - 1 (c^T Y) / MB for the rows this thread owns.  Calls f(u, z).
+template <typename F>
+__device__ void apply_m(const double2* y, const int32_t* __restrict__ cp,
+                        const int32_t* __restrict__ rp, const int32_t* __restrict__ ci, int cap,
+                        int MB, int NB, double* red, F f) {
+  const int t = threadIdx.x;
+  double2 s = make_double2(0.0, 0.0);
+  for (int v = t; v < NB; v += kThreads) {
+    const double c = (double)(cp[v + 1] - cp[v]);
+    s.x += c * y[v].x;
+    s.y += c * y[v].y;
+  }
+  s = block_sum2(s, red);
+  const double inv = 1.0 / (double)MB;
+  for (int u = t; u < MB; u += kThreads) {
+    const int lo = min(rp[u], cap), hi = min(rp[u + 1], cap);
+    double ax = 0.0, ay = 0.0;
+    int k = lo;
+    for (; k + 4 <= hi; k += 4) {
+      const int v0 = ci[k], v1 = ci[k + 1], v2 = ci[k + 2], v3 = ci[k + 3];
+      ax += y[v0].x; ay += y[v0].y;
+      ax += y[v1].x; ay += y[v1].y;
+      ax += y[v2].x; ay += y[v2].y;
+      ax += y[v3].x; ay += y[v3].y;
+    }
+    for (; k < hi; ++k) {
+      const int v = ci[k];
+      ax += y[v].x;
+      ay += y[v].y;
+    }
+    f(u, make_double2(ax - s.x * inv, ay - s.y * inv));
+  }
+}
+
+// Ascending bitonic sort of n (power of two) (key, val) pairs in LDS, ordered by
+// key and then by val.
+__device__ void bitonic_sort_pairs(uint64_t* key, uint32_t* val, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int i = threadIdx.x; i < (n >> 1); i += kThreads) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t ka = key[lo], kb = key[hi];
+        const uint32_t va = val[lo], vb = val[hi];
+        const bool greater = ka > kb || (ka == kb && va > vb);
+        if (greater == up) {
+          key[lo] = kb;
+          key[hi] = ka;
+          val[lo] = vb;
+          val[hi] = va;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kThreads) void k_reorder(
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    const int32_t* __restrict__ csc_ptr, const int32_t* __restrict__ csc_idx, int cap,
+    const float* __restrict__ x0, int MB, int NB, int block, int head_dim, DevParams p,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm, uint8_t* __restrict__ skipped,
+    double* __restrict__ angles, double* __restrict__ stats) {
+  extern __shared__ double2 lds[];
+  __shared__ double red[2 * kWaves];
+  __shared__ long long redi[kWaves];
+  __shared__ int redm[kWaves];
+  const int h = blockIdx.x;
+  const int t = threadIdx.x;
+  const int32_t* rp = row_ptr + (size_t)h * MB;
+  const int32_t* cp = csc_ptr + (size_t)h * NB;
+  int32_t* perm_h = perm + (size_t)h * MB;
+  int32_t* inv_h = inv_perm + (size_t)h * MB;
+  double* ang_h = angles ? angles + (size_t)h * MB : nullptr;
+
+  // ---- statistics and the skip decision (§IV-E) ----
+  long long inter = 0, uni = 0;
+  for (int u = t; u + 1 < MB; u += kThreads) {
+    int a = min(rp[u], cap), ae = min(rp[u + 1], cap);
+    int b = ae, be = min(rp[u + 2], cap);
+    const int na = ae - a, nb = be - b;
+    int common = 0;
+    while (a < ae && b < be) {
+      const int va = col_idx[a], vb = col_idx[b];
+      common += va == vb;
+      a += va <= vb;
+      b += vb <= va;
+    }
+    inter += common;
+    uni += na + nb - common;
+  }
+  inter = block_sum_i64(inter, redi);
+  uni = block_sum_i64(uni, redi);
+  const long long nnz = (long long)rp[MB] - (long long)rp[0];
+  const double jac = uni == 0 ? 1.0 : (double)inter / (double)uni;
+  const double ws = (double)NB * (double)block * (double)head_dim * 4.0;
+  const double flops = 4.0 * (double)block * (double)block * (double)head_dim * (double)nnz;
+  if (stats != nullptr && t == 0) {
+    double* s = stats + (size_t)h * 5;
+    s[0] = (double)nnz;
+    s[1] = (double)nnz / ((double)MB * (double)NB);
+    s[2] = ws;
+    s[3] = flops;
+    s[4] = jac;
+  }
+  bool skip;
+  if (p.skip_mode == WA_SKIP_ALWAYS) {
+    skip = true;
+  } else if (p.skip_mode == WA_SKIP_NEVER) {
+    skip = false;
+  } else {
+    skip = !(ws > p.ws_min && flops >= p.flops_min && jac < p.jac_max);
+  }
+  if (t == 0) skipped[h] = skip ? 1 : 0;
+  if (skip) {
+    for (int u = t; u < MB; u += kThreads) {
+      perm_h[u] = u;
+      inv_h[u] = u;
+      if (ang_h) ang_h[u] = __longlong_as_double(0x7ff8000000000000ll);
+    }
+    return;
+  }
+
+  // ---- Stage 1: spectral polar order ----
+  double2* X = lds;        // [MB]
+  double2* Y = lds + MB;   // [NB]
+  bool varied = false;
+  for (int v = t; v < NB; v += kThreads) {
+    const int c = cp[v + 1] - cp[v];
+    varied |= (c != 0 && c != MB);
+  }
+  const bool embed = p.stage1 && __syncthreads_or(varied);
+  int n2 = 1;
+  while (n2 < MB) n2 <<= 1;
+  uint64_t* key = reinterpret_cast<uint64_t*>(lds);    // [n2], after the embedding
+  uint32_t* val = reinterpret_cast<uint32_t*>(key + n2);  // [n2]
+  if (embed) {
+    const float* xh = x0 + (size_t)h * MB * 2;
+    for (int u = t; u < MB; u += kThreads)
+      X[u] = make_double2((double)xh[2 * u], (double)xh[2 * u + 1]);
+    __syncthreads();
+    qr2_inplace(X, MB, red);
+    for (int it = 0; it < p.iters; ++it) {
+      apply_mt(X, Y, cp, csc_idx, cap, MB, NB, red);
+      apply_m(Y, cp, rp, col_idx, cap, MB, NB, red, [&](int u, double2 z) { X[u] = z; });
+      __syncthreads();
+      qr2_inplace(X, MB, red);
+    }
+    // Ritz rotation: B = X^T Z with Z = M~ M~^T X, symmetrised; rotate X onto the
+    // eigenvectors of B, larger eigenvalue first.
+    apply_mt(X, Y, cp, csc_idx, cap, MB, NB, red);
+    double b00 = 0.0, b01 = 0.0, b10 = 0.0, b11 = 0.0;
+    apply_m(Y, cp, rp, col_idx, cap, MB, NB, red, [&](int u, double2 z) {
+      const double2 xu = X[u];
+      b00 += xu.x * z.x;
+      b01 += xu.x * z.y;
+      b10 += xu.y * z.x;
+      b11 += xu.y * z.y;
+    });
+    const double2 bd = block_sum2(make_double2(b00, b11), red);
+    const double2 bo = block_sum2(make_double2(b01, b10), red);
+    const double boff = 0.5 * (bo.x + bo.y);
+    const double theta = 0.5 * atan2(2.0 * boff, bd.x - bd.y);
+    const double cs = cos(theta), sn = sin(theta);
+    double cube0 = 0.0, cube1 = 0.0;
+    for (int u = t; u < MB; u += kThreads) {
+      const double2 xu = X[u];
+      const double r0 = xu.x * cs + xu.y * sn;
+      const double r1 = -xu.x * sn + xu.y * cs;
+      X[u] = make_double2(r0, r1);
+      cube0 += r0 * r0 * r0;
+      cube1 += r1 * r1 * r1;
+    }
+    // Sign convention: positive sum of cubes; near zero, first entry > 1e-6 positive.
+    const double2 cube = block_sum2(make_double2(cube0, cube1), red);
+    int first0 = MB, first1 = MB;
+    for (int u = t; u < MB; u += kThreads) {
+      if (fabs(X[u].x) > 1e-6) first0 = min(first0, u);
+      if (fabs(X[u].y) > 1e-6) first1 = min(first1, u);
+    }
+    first0 = block_min_i32(first0, redm);
+    first1 = block_min_i32(first1, redm);
+    bool flip0, flip1;
+    if (fabs(cube.x) >= 1e-6) flip0 = cube.x < 0.0;
+    else flip0 = first0 < MB && X[first0].x < 0.0;
+    if (fabs(cube.y) >= 1e-6) flip1 = cube.y < 0.0;
+    else flip1 = first1 < MB && X[first1].y < 0.0;
+    __syncthreads();
+    // Angles (eq. (4)) in [0, 2pi].
+    double ang[WA_MAX_BLOCKS / kThreads];
+    int nmine = 0;
+    for (int u = t; u < MB; u += kThreads) {
+      const double a0 = flip0 ? -X[u].x : X[u].x;
+      const double a1 = flip1 ? -X[u].y : X[u].y;
+      double a = atan2(a1, a0);
+      if (a < 0.0) a += kTwoPi;
+      a += 0.0;
+      ang[nmine++] = a;
+      if (ang_h) ang_h[u] = a;
+    }
+    __syncthreads();  // X is dead from here on; its LDS holds the sort arrays
+    // A non-negative double's bit pattern sorts like its value, so sorting the pairs
+    // (angle bits, row) is the stable ascending sort by angle.
+    nmine = 0;
+    for (int u = t; u < MB; u += kThreads) {
+      key[u] = (uint64_t)__double_as_longlong(ang[nmine++]);
+      val[u] = (uint32_t)u;
+    }
+    for (int u = MB + t; u < n2; u += kThreads) {
+      key[u] = ~0ull;
+      val[u] = ~0u;
+    }
+    bitonic_sort_pairs(key, val, n2);
+  } else {
+    if (ang_h)
+      for (int u = t; u < MB; u += kThreads) ang_h[u] = __longlong_as_double(0x7ff8000000000000ll);
+    for (int u = t; u < MB; u += kThreads) val[u] = (uint32_t)u;
+    __syncthreads();
+  }
+  // val[pos] is the Stage-1 order.
+
+  // ---- Stage 2: NNZ-descending inside each wave bucket (§IV-D) ----
+  if (p.stage2) {
+    const int s = (MB + p.n_slices - 1) / p.n_slices;
+    const int per_slice = (s + p.wave - 1) / p.wave;
+    for (int pos = t; pos < n2; pos += kThreads) {
+      if (pos < MB) {
+        const int row = (int)val[pos];
+        const int nnz_row = min(rp[row + 1], cap) - min(rp[row], cap);
+        const int x = pos / s;
+        const int bucket = x * per_slice + (pos - x * s) / p.wave;
+        key[pos] = ((uint64_t)bucket << 40) | ((uint64_t)(NB - nnz_row) << 20) | (uint64_t)pos;
+      } else {
+        key[pos] = ~0ull;
+        val[pos] = ~0u;
+      }
+    }
+    bitonic_sort_pairs(key, val, n2);
+  }
+  for (int pos = t; pos < MB; pos += kThreads) {
+    const int row = (int)val[pos];
+    perm_h[pos] = row;
+    inv_h[row] = pos;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_reorder(const int32_t* row_ptr, const int32_t* col_idx, const int32_t* csc_ptr,
+                          const int32_t* csc_idx, int64_t cap64, const float* x0, int H, int MB, int NB,
+                          int block, int head_dim, const wa_reorder_params& p, int32_t* perm,
+                          int32_t* inv_perm, uint8_t* skipped, double* angles, double* stats,
+                          hipStream_t s) {
+  int n2 = 1;
+  while (n2 < MB) n2 <<= 1;
+  const size_t embed_bytes = (size_t)(MB + NB) * sizeof(double2);
+  const size_t sort_bytes = (size_t)n2 * (sizeof(uint64_t) + sizeof(uint32_t));
+  const size_t lds = embed_bytes > sort_bytes ? embed_bytes : sort_bytes;
+  // The dynamic LDS limit is a per-device function attribute; set it once per device.
+  static bool attr_set[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!attr_set[dev]) {
+    e = hipFuncSetAttribute((const void*)k_reorder, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024 - 4096);
+    if (e != hipSuccess) return e;
+    attr_set[dev] = true;
+  }
+  DevParams dp{p.wave, p.n_slices, p.iters, p.stage1, p.stage2, p.skip_mode,
+               p.ws_min_bytes, p.flops_min, p.jaccard_max};
+  const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
+  hipLaunchKernelGGL(k_reorder, dim3(H), dim3(kThreads), lds, s, row_ptr, col_idx, csc_ptr,
+                     csc_idx, cap, x0, MB, NB, block, head_dim, dp, perm, inv_perm, skipped, angles,
+                     stats);
+  return hipGetLastError();
+}
+
+}  // namespace wa

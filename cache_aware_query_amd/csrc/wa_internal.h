@@ -1,0 +1,45 @@
+// Internal declarations shared by the HIP translation units of libwavealign.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/wavealign.h"
+
+namespace wa {
+
+// Launchers (defined next to their kernels).  They assume validated arguments and
+// return the hipError_t of the launch.
+hipError_t launch_block_index(const uint8_t* mask, int H, int MB, int NB, int32_t* row_ptr,
+                              int32_t* col_idx, int64_t col_cap, int32_t* row_nnz,
+                              int32_t* csc_ptr, int32_t* csc_idx, int64_t csc_cap,
+                              hipStream_t s);
+
+hipError_t launch_reorder(const int32_t* row_ptr, const int32_t* col_idx, const int32_t* csc_ptr,
+                          const int32_t* csc_idx, int64_t cap, const float* x0, int H, int MB, int NB,
+                          int block, int head_dim, const wa_reorder_params& p, int32_t* perm,
+                          int32_t* inv_perm, uint8_t* skipped, double* angles, double* stats,
+                          hipStream_t s);
+
+size_t attn_workspace_bytes(int H, int L_pad, int head_dim);
+hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H,
+                              int L, int head_dim, int block, const int32_t* row_ptr,
+                              const int32_t* col_idx, int64_t cap, const int32_t* perm,
+                              int schedule,
+                              float scale, uint16_t* o, float* lse, float* g, void* workspace,
+                              hipStream_t s);
+int attn_resident_wgs_per_cu(int head_dim, int block);
+
+hipError_t launch_block_importance(const float* g, const float* lse, const int32_t* row_ptr,
+                                   int64_t cap, int H, int MB, int L, int block, float* w, hipStream_t s);
+hipError_t launch_topp(const float* w, const int32_t* row_ptr, const int32_t* col_idx,
+                       int64_t cap, int H,
+                       int MB, int NB, double p, uint8_t* mask_out, hipStream_t s);
+
+hipError_t launch_permute_blocks(const void* src, void* dst, const int32_t* perm, int H, int MB,
+                                 int64_t block_bytes, bool scatter, hipStream_t s);
+
+// Number of XCDs the attention schedule slices over.
+constexpr int kXcds = 8;
+
+}  // namespace wa

@@ -1,0 +1,112 @@
+"""One pass of the hot path with buffers allocated once.
+
+``HotPath.step`` enqueues, on the current stream and without allocating or
+synchronising:
+
+  1. wa_build_block_index   mask -> CSR + CSC                  (WaveAlign §II-B)
+  2. wa_reorder_rows        per-head permutation              (WaveAlign §IV)
+  3. wa_sparse_attn_fwd     attention in the permuted order   (WaveAlign §II-C, §V)
+                            + Phase-1 block LSE G             (GSRS §5.3)
+  4. wa_block_importance    block weights W                   (GSRS §5.3 Phase 2)
+  5. wa_topp_select         next block mask                   (GSRS Algorithm 3)
+
+Steps 4-5 run only when ``gsrs_p`` is set; step 2 is replaced by the identity
+order when ``reorder`` is None.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import (WA_SCHED_XCD_SLICED, BlockIndex, ReorderParams, _check, _ptr, _stream,
+               load_library, sparse_attn_workspace_size)
+
+
+class HotPath:
+    def __init__(self, heads: int, seq_len: int, head_dim: int, block: int, device,
+                 capacity: int | None = None, reorder: ReorderParams | None = None,
+                 schedule: int = WA_SCHED_XCD_SLICED, gsrs_p: float | None = 0.9):
+        self.lib = load_library()
+        self.H, self.L, self.d, self.b = heads, seq_len, head_dim, block
+        self.mb = -(-seq_len // block)
+        self.lp = self.mb * block
+        self.device = torch.device(device)
+        self.cap = heads * self.mb * self.mb if capacity is None else int(capacity)
+        self.reorder = reorder
+        self.schedule = schedule
+        self.gsrs_p = gsrs_p
+        dev = self.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        H, mb = heads, self.mb
+        self.row_ptr = torch.empty(H * mb + 1, **i32)
+        self.row_nnz = torch.empty(H * mb, **i32)
+        self.col_idx = torch.empty(max(self.cap, 1), **i32)
+        self.csc_ptr = torch.empty(H * mb + 1, **i32)
+        self.csc_idx = torch.empty(max(self.cap, 1), **i32)
+        self.perm = torch.empty(H, mb, **i32)
+        self.inv_perm = torch.empty(H, mb, **i32)
+        self.skipped = torch.empty(H, dtype=torch.uint8, device=dev)
+        self.angles = torch.empty(H, mb, dtype=torch.float64, device=dev)
+        self.stats = torch.empty(H, 5, dtype=torch.float64, device=dev)
+        self.o = torch.empty(H, self.lp, head_dim, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(H, self.lp, dtype=torch.float32, device=dev)
+        self.g = (torch.empty(max(self.cap, 1), block, dtype=torch.float32, device=dev)
+                  if gsrs_p is not None else None)
+        self.w = (torch.empty(max(self.cap, 1), dtype=torch.float32, device=dev)
+                  if gsrs_p is not None else None)
+        self.next_mask = (torch.empty(H, mb, mb, dtype=torch.uint8, device=dev)
+                          if gsrs_p is not None else None)
+        self.ws_bytes = sparse_attn_workspace_size(heads, seq_len, head_dim, block)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self._params = (reorder or ReorderParams())._c()
+
+    def index(self) -> BlockIndex:
+        return BlockIndex(self.row_ptr, self.col_idx, self.row_nnz, self.csc_ptr, self.csc_idx,
+                          self.H, self.mb, self.mb)
+
+    # Individual stages (each enqueues its launches on the current stream).
+    def build_index(self, mask: torch.Tensor) -> None:
+        lib, s = self.lib, _stream(self.device)
+        _check(lib.wa_build_block_index(_ptr(mask), self.H, self.mb, self.mb, _ptr(self.row_ptr),
+                                        _ptr(self.col_idx), self.cap, _ptr(self.row_nnz),
+                                        _ptr(self.csc_ptr), _ptr(self.csc_idx), self.cap, s),
+               "wa_build_block_index")
+
+    def reorder_rows(self, x0: torch.Tensor) -> None:
+        lib, s = self.lib, _stream(self.device)
+        _check(lib.wa_reorder_rows(_ptr(self.row_ptr), _ptr(self.col_idx), _ptr(self.csc_ptr),
+                                   _ptr(self.csc_idx), self.cap, _ptr(x0), self.H, self.mb, self.mb,
+                                   self.b, self.d, ctypes.byref(self._params), _ptr(self.perm),
+                                   _ptr(self.inv_perm), _ptr(self.skipped), _ptr(self.angles),
+                                   _ptr(self.stats), s), "wa_reorder_rows")
+
+    def attention(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
+        lib, s = self.lib, _stream(self.device)
+        perm = self.perm if self.reorder is not None else None
+        g = self.g if self.gsrs_p is not None else None
+        _check(lib.wa_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), self.H, self.L, self.d, self.b,
+                                      _ptr(self.row_ptr), _ptr(self.col_idx), self.cap, _ptr(perm),
+                                      self.schedule, self.d ** -0.5, _ptr(self.o), _ptr(self.lse),
+                                      _ptr(g), _ptr(self.workspace), self.ws_bytes, s),
+               "wa_sparse_attn_fwd")
+
+    def select(self) -> None:
+        lib, s = self.lib, _stream(self.device)
+        _check(lib.wa_block_importance(_ptr(self.g), _ptr(self.lse), _ptr(self.row_ptr), self.cap,
+                                       self.H,
+                                       self.mb, self.L, self.b, _ptr(self.w), s),
+               "wa_block_importance")
+        _check(lib.wa_topp_select(_ptr(self.w), _ptr(self.row_ptr), _ptr(self.col_idx), self.cap,
+                                  self.H,
+                                  self.mb, self.mb, float(self.gsrs_p), _ptr(self.next_mask), s),
+               "wa_topp_select")
+
+    def step(self, q, k, v, mask, x0) -> None:
+        self.build_index(mask)
+        if self.reorder is not None:
+            self.reorder_rows(x0)
+        self.attention(q, k, v)
+        if self.gsrs_p is not None:
+            self.select()

@@ -1,0 +1,233 @@
+/*
+ * wavealign.h - C ABI of the MI355X (gfx950) cache-aware block-sparse attention library.
+ *
+ * The library computes the hot path described by two pages:
+ *   [WA]   "WaveAlign: Cache-Aware Query-Row Scheduling for Sparse Attention in
+ *           Long-Video Generation"
+ *   [GSRS] "Sparse Attention for Video Generation Acceleration via Growing Sparsity
+ *           and Reduced Search"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array arguments are DEVICE pointers owned by the caller (allocated with
+ *    hipMalloc or by PyTorch) unless the comment says "host".  The library never
+ *    allocates or frees device memory and keeps no state between calls.
+ *  - Every call only validates its scalar arguments on the host and enqueues work
+ *    on `stream` (a hipStream_t, passed as void*; NULL means the null stream).  No
+ *    call synchronises.  Results are valid once the stream has reached the point
+ *    after the call.
+ *  - Return value: WA_OK (0) or a negative WA_ERR_* code.  On error nothing was
+ *    enqueued and wa_last_error() returns a message (thread-local, valid until the
+ *    next call from the same thread).
+ *  - Tensors are row-major.  bf16 values are stored as uint16_t bit patterns.
+ *  - Shapes: H heads, block size b, L valid tokens, L_pad = MB * b with
+ *    MB = NB = ceil(L / b) query and key/value blocks.  Token rows >= L are padding:
+ *    the caller zero-fills them in Q, K and V; their outputs are unspecified.
+ *  - Calls issued on different streams may run concurrently as long as they do not
+ *    write the same buffers.
+ */
+#ifndef WAVEALIGN_H
+#define WAVEALIGN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WA_OK 0
+#define WA_ERR_INVALID_ARG (-1) /* null pointer, negative size, bad flag */
+#define WA_ERR_UNSUPPORTED (-2) /* shape the kernels do not implement (head_dim, block, > limits) */
+#define WA_ERR_CAPACITY (-3)    /* a workspace or output buffer is too small */
+#define WA_ERR_HIP (-4)         /* the HIP runtime reported an error at launch */
+
+/* Largest number of query/key blocks per head the reorder kernel handles. */
+#define WA_MAX_BLOCKS 4096
+
+/* Attention schedules (how workgroups map to query blocks). */
+#define WA_SCHED_NATURAL 0     /* workgroup w runs position w of the head-major order      */
+#define WA_SCHED_XCD_SLICED 1  /* XCD x runs the x-th contiguous slice of each head's order */
+
+/* Skip modes of wa_reorder_rows. */
+#define WA_SKIP_ADAPTIVE 0
+#define WA_SKIP_NEVER 1
+#define WA_SKIP_ALWAYS 2
+
+typedef uint16_t wa_bf16;
+
+/* ABI version of this header; bumps on incompatible change. */
+int wa_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* wa_last_error(void);
+
+/*
+ * wa_schedule_info - hardware figures the reorder needs (host outputs).
+ *   n_xcd        number of XCDs (L2 domains) of `device`
+ *   cus_per_xcd  compute units per XCD
+ *   wave         [WA §II-C, §VI-A] the dispatch wave per XCD: compute units per XCD
+ *                times the attention workgroups resident per compute unit for
+ *                head_dim (the WaveAlign bucket size W on one L2 domain)
+ * Errors: WA_ERR_INVALID_ARG for null outputs, WA_ERR_UNSUPPORTED for head_dim not
+ * 64/128, WA_ERR_HIP if the device cannot be queried.
+ */
+int wa_schedule_info(int device, int32_t head_dim, int32_t* n_xcd, int32_t* cus_per_xcd,
+                     int32_t* wave);
+
+/*
+ * wa_build_block_index - [WA §II-B, §II-C] block mask -> per-query-block K/V lists.
+ * Mask row i of head h lists the K/V blocks query block i visits; its row sum is
+ * the query block's workload (NNZ).
+ *   mask      uint8 [H][MB][NB], non-zero = selected
+ *   row_ptr   int32 [H*MB + 1]  exclusive prefix sum of the row counts in head-major
+ *                               row order; row_ptr[H*MB] = total NNZ (always written)
+ *   col_idx   int32 [col_capacity]  ascending K/V block ids of each row, in row order
+ *   row_nnz   int32 [H*MB]      per-row counts
+ *   csc_ptr   int32 [H*NB + 1] or NULL  the same for the transposed mask (columns in
+ *                                       head-major order); NULL skips the CSC
+ *   csc_idx   int32 [csc_capacity] or NULL  ascending query block ids per column
+ * Entries that would land at an index >= capacity are not written; row_ptr[H*MB]
+ * and csc_ptr[H*NB] still hold the true totals, so a caller whose capacity is
+ * below H*MB*NB detects truncation by reading them.  Integer work, bit-exact.
+ * Errors: WA_ERR_INVALID_ARG (null required pointer, H/MB/NB < 1, negative capacity).
+ */
+int wa_build_block_index(const uint8_t* mask, int32_t H, int32_t MB, int32_t NB,
+                         int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                         int32_t* row_nnz, int32_t* csc_ptr, int32_t* csc_idx,
+                         int64_t csc_capacity, void* stream);
+
+/* Parameters of wa_reorder_rows (host struct). */
+typedef struct wa_reorder_params {
+  int32_t wave;        /* W, rows per wave bucket (>= 1)                                */
+  int32_t n_slices;    /* contiguous slices of the order, one per L2 domain (1..64);
+                          1 reproduces [WA Algorithm 2] exactly                          */
+  int32_t iters;       /* T of [WA Algorithm 1] (0..1000)                                */
+  int32_t stage1;      /* 1: spectral polar order, 0: keep the row order                 */
+  int32_t stage2;      /* 1: NNZ-descending order inside buckets, 0: off                  */
+  int32_t skip_mode;   /* WA_SKIP_ADAPTIVE / WA_SKIP_NEVER / WA_SKIP_ALWAYS              */
+  double ws_min_bytes; /* reorder only if the head's K/V bytes exceed this               */
+  double flops_min;    /* ... and its selected FLOP are at least this                    */
+  double jaccard_max;  /* ... and its adjacent-row Jaccard similarity is below this      */
+} wa_reorder_params;
+
+/*
+ * wa_reorder_rows - [WA §IV, Algorithms 1 and 2] per-head query-block permutation.
+ * Per head: statistics and the adaptive skip [WA §IV-E]; if not skipped, the rank-2
+ * embedding of the column-centered mask by matrix-free centered subspace iteration
+ * [WA §IV-C-2, Algorithm 1] from the start block x0, the optional Ritz rotation,
+ * polar angles a_i = atan2(u2, u1) in [0, 2pi] [WA eq. (4)], a stable ascending
+ * sort (Stage 1), buckets of at most `wave` positions inside `n_slices` contiguous
+ * slices, and a stable NNZ-descending sort inside each bucket (Stage 2) [WA §IV-D].
+ * Arithmetic is fp64.  Readings of open points: the start block is orthonormalised
+ * by modified Gram-Schmidt; a second basis vector whose norm falls to <= 1e-12 of
+ * the first is set to zero; each basis vector's sign makes its sum of cubes
+ * positive (first entry > 1e-6 positive if |sum| < 1e-6); a mask whose rows are
+ * all identical keeps the identity Stage-1 order; the skip rule reorders only if
+ * K/V bytes NB*b*d*4 > ws_min_bytes, 4*b*b*d*nnz >= flops_min and the pooled
+ * Jaccard similarity of adjacent rows < jaccard_max.
+ *   row_ptr, col_idx, csc_ptr, csc_idx  from wa_build_block_index (CSC required)
+ *   capacity  number of entries col_idx and csc_idx hold; list entries at or beyond it
+ *             are ignored (a truncated index never causes an out-of-bounds read)
+ *   x0        float [H][MB][2]  raw start values (the random block of Algorithm 1)
+ *   perm      int32 [H][MB] out  perm[h][pos] = query block executed at position pos
+ *   inv_perm  int32 [H][MB] out  inv_perm[h][perm[h][pos]] = pos
+ *   skipped   uint8 [H]     out  1 if the head kept the identity order
+ *   angles    double [H][MB] out or NULL  polar angle per query block (NaN where
+ *                                         Stage 1 did not run)
+ *   stats     double [H][5] out or NULL  nnz, density, K/V bytes, selected FLOP,
+ *                                        adjacent-row Jaccard
+ *   params    host pointer
+ * Errors: WA_ERR_INVALID_ARG (null pointer, bad params), WA_ERR_UNSUPPORTED
+ * (MB or NB > WA_MAX_BLOCKS, head_dim/block < 1), WA_ERR_HIP.
+ */
+int wa_reorder_rows(const int32_t* row_ptr, const int32_t* col_idx, const int32_t* csc_ptr,
+                    const int32_t* csc_idx, int64_t capacity, const float* x0, int32_t H,
+                    int32_t MB, int32_t NB,
+                    int32_t block, int32_t head_dim, const wa_reorder_params* params,
+                    int32_t* perm, int32_t* inv_perm, uint8_t* skipped, double* angles,
+                    double* stats, void* stream);
+
+/* Workspace bytes wa_sparse_attn_fwd needs for these sizes (host output). */
+int wa_sparse_attn_workspace_size(int32_t H, int32_t L, int32_t head_dim, int32_t block,
+                                  size_t* bytes);
+
+/*
+ * wa_sparse_attn_fwd - [WA §II-C; GSRS §3] block-sparse attention forward.
+ * Query block u of head h attends to the tokens j < L of the K/V blocks listed in
+ * col_idx[row_ptr[h*MB+u] .. row_ptr[h*MB+u+1]), in ascending order:
+ *   LSE_i = ln sum_j exp(scale * q_i.k_j),  O_i = sum_j exp(scale * q_i.k_j - LSE_i) v_j.
+ * A query block with no K/V block gets O = 0 and LSE = -inf [GSRS, fully masked rows].
+ * Inputs are bf16; products accumulate in fp32 (bf16 MFMA); the softmax is fp32 and
+ * the probabilities are rounded to bf16 before the P*V product.
+ *   q, k, v   bf16 [H][L_pad][head_dim]; head_dim 64 or 128; block 64 or 128
+ *   capacity  entries col_idx holds (and rows g holds); entries at or beyond it are
+ *             skipped, as are block ids outside [0, MB)
+ *   perm      int32 [H][MB] or NULL  execution order [WA §V]: position p of head h runs
+ *             query block perm[h][p]; O, LSE and G stay in the original order (the
+ *             permutation is applied by indexing, the inverse reorder is implicit)
+ *   schedule  WA_SCHED_NATURAL or WA_SCHED_XCD_SLICED
+ *   o         bf16 [H][L_pad][head_dim] out
+ *   lse       float [H][L_pad] out, natural log
+ *   g         float [row_ptr[H*MB]][block] out or NULL  [GSRS §5.3 Phase 1] for CSR
+ *             entry e = (u, v) and row r of u, the block log-sum-exp
+ *             G = m + ln sum_{j in v, j < L} exp(z_rj - m), m the block maximum
+ *   workspace device buffer of at least wa_sparse_attn_workspace_size bytes
+ * Errors: WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED (head_dim/block), WA_ERR_CAPACITY
+ * (workspace too small), WA_ERR_HIP.
+ */
+int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
+                       int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
+                       const int32_t* col_idx, int64_t capacity, const int32_t* perm,
+                       int32_t schedule,
+                       float scale, wa_bf16* o, float* lse, float* g, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * wa_block_importance - [GSRS §5.3 Phase 2, Appendix A.2] block weights.
+ * For CSR entry e = (h, u, v): W[e] = (1/B_u) sum over the valid rows i of query
+ * block u of exp(G[e][i] - LSE_i), B_u = number of rows of u below L; rows with
+ * LSE = -inf add nothing.  Each non-empty row of W sums to 1.
+ *   g    float [capacity][block], lse float [H][L_pad], w float [capacity] out; entries
+ *        at or beyond capacity are skipped
+ * Errors: WA_ERR_INVALID_ARG, WA_ERR_HIP.
+ */
+int wa_block_importance(const float* g, const float* lse, const int32_t* row_ptr,
+                        int64_t capacity, int32_t H, int32_t MB, int32_t L, int32_t block,
+                        float* w, void* stream);
+
+/*
+ * wa_topp_select - [GSRS Algorithm 3] Top-p block selection per query block.
+ * The candidates of a row (its CSR entries) are sorted by descending W, equal W by
+ * ascending block id; their W are summed in fp64 in that order and a block is kept
+ * while the sum before it is <= p (the block that takes the sum above p is the last
+ * one kept).  Restricting a second selection to the first selection's index gives
+ * the reduced search of GSRS.
+ *   w        float [capacity], col_idx int32 [capacity]; entries at or beyond capacity
+ *            are not candidates
+ *   mask_out uint8 [H][MB][NB] out (fully overwritten)
+ * Errors: WA_ERR_INVALID_ARG (p outside (0, 1], null pointers), WA_ERR_UNSUPPORTED
+ * (NB > WA_MAX_BLOCKS), WA_ERR_HIP.
+ */
+int wa_topp_select(const float* w, const int32_t* row_ptr, const int32_t* col_idx,
+                   int64_t capacity, int32_t H, int32_t MB, int32_t NB, double p,
+                   uint8_t* mask_out, void* stream);
+
+/*
+ * wa_gather_blocks / wa_scatter_blocks - [WA §V] explicit reorder operators.
+ * Row blocks of block_bytes bytes: gather dst[h][s] = src[h][perm[h][s]];
+ * scatter dst[h][perm[h][s]] = src[h][s].  Used for Q blocks, mask rows, O and
+ * LSE when the permutation is applied as copies instead of by indexing.
+ * src and dst must not overlap; perm entries outside [0, MB) are skipped.
+ * Errors: WA_ERR_INVALID_ARG, WA_ERR_HIP.
+ */
+int wa_gather_blocks(const void* src, void* dst, const int32_t* perm, int32_t H, int32_t MB,
+                     int64_t block_bytes, void* stream);
+int wa_scatter_blocks(const void* src, void* dst, const int32_t* perm, int32_t H, int32_t MB,
+                      int64_t block_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WAVEALIGN_H */

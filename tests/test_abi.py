@@ -1,0 +1,72 @@
+"""The C-ABI library loads on a CPU-only host, exports every declared entry point,
+and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import cache_aware_query_amd as caq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for f in os.listdir(inc):
+        if f.endswith(".h"):
+            text = open(os.path.join(inc, f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(wa_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(caq.LIB_PATH):
+        pytest.fail("libwavealign.so is not built; run __graft_entry__.build()")
+    return caq.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared()
+    assert declared, "no declarations found"
+    assert declared == set(caq.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version(lib):
+    assert lib.wa_abi_version() == 1
+
+
+def test_host_validation_rejects_bad_arguments(lib):
+    # Null pointers and bad sizes are refused on the host; nothing reaches HIP.
+    assert lib.wa_build_block_index(None, 1, 1, 1, None, None, 0, None, None, None, 0, None) == -1
+    assert b"null" in lib.wa_last_error()
+    n = ctypes.c_size_t()
+    assert lib.wa_sparse_attn_workspace_size(2, 1000, 96, 128, ctypes.byref(n)) == -2
+    assert lib.wa_sparse_attn_workspace_size(2, 1000, 128, 128, ctypes.byref(n)) == 0
+    assert n.value == 2 * 1024 * 128 * 2
+    assert lib.wa_last_error() == b""
+    fake = ctypes.c_void_p(16)
+    assert lib.wa_topp_select(fake, fake, fake, 4, 1, 1, 1, 1.5, fake, None) == -1
+    assert lib.wa_topp_select(fake, fake, fake, 4, 1, 1, 5000, 0.5, fake, None) == -2
+    assert lib.wa_topp_select(fake, fake, fake, -1, 1, 1, 1, 0.5, fake, None) == -1
+    p = caq.ReorderParams(wave=0)._c()
+    assert lib.wa_reorder_rows(fake, fake, fake, fake, 16, fake, 1, 4, 4, 128, 128,
+                               ctypes.byref(p), fake, fake, fake, None, None, None) == -1
+    p = caq.ReorderParams()._c()
+    assert lib.wa_reorder_rows(fake, fake, fake, fake, 16, fake, 1, 5000, 4, 128, 128,
+                               ctypes.byref(p), fake, fake, fake, None, None, None) == -2
+    # workspace too small
+    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 1,
+                                  0.1, fake, fake, None, fake, 10, None) == -3
+    # unaligned pointer
+    odd = ctypes.c_void_p(18)
+    assert lib.wa_sparse_attn_fwd(odd, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 1,
+                                  0.1, fake, fake, None, fake, 1 << 20, None) == -1
+    # overlapping gather
+    assert lib.wa_gather_blocks(fake, fake, fake, 1, 2, 64, None) == -1

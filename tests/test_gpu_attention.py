@@ -1,0 +1,106 @@
+"""wa_sparse_attn_fwd against the fp64 oracle (element by element), plus the
+invariants the pages fix: the output does not depend on the execution order of
+query blocks, an all-ones mask is dense attention, a fully masked query block
+gives O = 0 and LSE = -inf."""
+
+import numpy as np
+import pytest
+import torch
+
+import cache_aware_query_amd as caq
+import oracle
+import synth
+from helpers import assert_attention_close, banner, gpu, np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, perm=None, schedule=caq.WA_SCHED_XCD_SLICED, with_g=False):
+    dev = gpu()
+    q, k, v, mask = (t.to(dev) for t in (w.q, w.k, w.v, w.mask))
+    idx = caq.build_block_index(mask)
+    p = None if perm is None else perm.to(dev)
+    o, lse, g = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx,
+                                    perm=p, schedule=schedule, with_g=with_g)
+    torch.cuda.synchronize()
+    return o, lse, g, idx
+
+
+def _oracle(w):
+    return oracle.masked_attention(np64(w.q), np64(w.k), np64(w.v), w.mask.cpu().numpy(),
+                                   w.seq_len, w.block, w.scale)
+
+
+def _compare(w, o, lse, what):
+    o_ref, lse_ref = _oracle(w)
+    L = w.seq_len
+    assert_attention_close(np64(o)[:, :L], lse.cpu().numpy().astype(np.float64)[:, :L],
+                           o_ref[:, :L], lse_ref[:, :L], what)
+
+
+CASES = [
+    ("tiny", {}),
+    ("layer16k", {"heads": 3}),
+]
+
+
+@pytest.mark.parametrize("name,over", CASES)
+@pytest.mark.parametrize("schedule", [caq.WA_SCHED_NATURAL, caq.WA_SCHED_XCD_SLICED])
+def test_attention_matches_oracle_on_workloads(name, over, schedule):
+    w = synth.make_workload(name, **over)
+    banner(f"attention {name} {over} schedule={schedule}")
+    o, lse, _, _ = _run(w, schedule=schedule)
+    _compare(w, o, lse, f"{name} schedule={schedule}")
+
+
+@pytest.mark.parametrize("seq_len,head_dim,block,density", [
+    (1000, 128, 128, 0.5),    # ragged tail: 8 blocks, the last with 104 tokens
+    (1100, 64, 128, 0.4),     # d = 64
+    (700, 128, 64, 0.35),     # block 64, d 128, ragged
+    (257, 64, 64, 0.7),       # one valid token in the last block
+    (128, 128, 128, 1.0),     # a single block
+])
+def test_attention_ragged_and_shapes(seq_len, head_dim, block, density):
+    w = synth.random_tiny_case(seq_len + head_dim, heads=2, seq_len=seq_len, head_dim=head_dim,
+                               block=block, density=density, empty_rows=(1,))
+    banner(f"attention random L={seq_len} d={head_dim} b={block} rho={density}")
+    o, lse, _, _ = _run(w)
+    _compare(w, o, lse, f"L={seq_len} d={head_dim} b={block}")
+
+
+def test_all_ones_mask_is_dense_attention():
+    dev = gpu()
+    w = synth.random_tiny_case(7, heads=2, seq_len=640, head_dim=128, block=128, density=1.0)
+    banner("attention all-ones mask vs dense")
+    o, lse, _, _ = _run(w)
+    q, k, v = (np64(t)[:, :640] for t in (w.q, w.k, w.v))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)).numpy()
+    np.testing.assert_allclose(np64(o)[:, :640], ref, atol=2e-2, rtol=2e-2)
+    assert dev.type == "cuda"
+
+
+def test_output_is_independent_of_execution_order():
+    w = synth.random_tiny_case(11, heads=3, seq_len=2000, head_dim=128, block=128, density=0.4,
+                               empty_rows=(4,))
+    mb = w.mask.shape[1]
+    banner("attention permutation invariance")
+    o0, l0, g0, _ = _run(w, schedule=caq.WA_SCHED_NATURAL, with_g=True)
+    gen = torch.Generator().manual_seed(5)
+    perm = torch.stack([torch.randperm(mb, generator=gen) for _ in range(3)]).to(torch.int32)
+    for sched in (caq.WA_SCHED_NATURAL, caq.WA_SCHED_XCD_SLICED):
+        o1, l1, g1, _ = _run(w, perm=perm, schedule=sched, with_g=True)
+        assert torch.equal(o0, o1) and torch.equal(l0, l1) and torch.equal(g0, g1)
+    # repeated runs are bitwise identical
+    o2, l2, _, _ = _run(w, schedule=caq.WA_SCHED_NATURAL)
+    assert torch.equal(o0, o2) and torch.equal(l0, l2)
+
+
+def test_fully_masked_block_gives_zero_and_neg_inf():
+    w = synth.make_workload("tiny")
+    banner("attention fully masked block")
+    o, lse, _, _ = _run(w)
+    b = w.block
+    assert torch.all(o[0, 7 * b:8 * b] == 0)
+    assert torch.all(torch.isneginf(lse[0, 7 * b:8 * b]))
+    assert torch.all(torch.isfinite(lse[0, :7 * b]))

@@ -1,0 +1,94 @@
+"""Full-size workloads in the launch configuration the benchmark times (block index,
+reorder with XCD slicing, attention through the permutation, G, W, Top-p), with
+sampled outputs checked row by row against the fp64 oracle and whole-output
+properties checked everywhere."""
+
+import numpy as np
+import pytest
+import torch
+
+import cache_aware_query_amd as caq
+import oracle
+import synth
+from cache_aware_query_amd.pipeline import HotPath
+from helpers import assert_attention_close, banner, gpu, np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_full(name):
+    dev = gpu()
+    banner(f"full-size {name}: generating")
+    w = synth.make_workload(name, device=dev)
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    nnz = int(w.mask.sum())
+    _, _, wave = caq.schedule_info(0, w.head_dim)
+    params = caq.ReorderParams(wave=wave, n_slices=8, skip_mode=caq.WA_SKIP_NEVER)
+    hp = HotPath(H, w.seq_len, w.head_dim, w.block, dev, capacity=nnz, reorder=params, gsrs_p=0.9)
+    banner(f"full-size {name}: H={H} MB={mb} nnz={nnz} wave={wave}")
+    hp.step(w.q, w.k, w.v, w.mask, w.x0)
+    torch.cuda.synchronize()
+    return w, hp
+
+
+def _sample_rows(w, rng, n_heads=4, n_blocks=3):
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    L, b = w.seq_len, w.block
+    heads = sorted(set([0, H - 1] + rng.choice(H, size=n_heads, replace=False).tolist()))
+    out = []
+    for h in heads:
+        blocks = sorted(set([mb - 1] + rng.choice(mb, size=n_blocks, replace=False).tolist()))
+        for u in blocks:
+            r0, r1 = u * b, min((u + 1) * b, L)
+            rows = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, size=6)]))
+            out.append((h, u, rows))
+    return out
+
+
+@pytest.mark.parametrize("name", ["wan75k", "hunyuan119k"])
+def test_full_size_attention_sampled(name):
+    w, hp = _run_full(name)
+    rng = np.random.default_rng(7)
+    o = hp.o
+    lse = hp.lse
+    assert not torch.isnan(o[:, : w.seq_len]).any()
+    assert not torch.isnan(lse[:, : w.seq_len]).any()
+    perm = hp.perm.cpu().numpy()
+    for h in range(perm.shape[0]):
+        assert sorted(perm[h].tolist()) == list(range(perm.shape[1]))
+    for h, u, rows in _sample_rows(w, rng):
+        qh, kh, vh = (np64(t[h]) for t in (w.q, w.k, w.v))
+        o_ref, l_ref = oracle.masked_attention_rows(qh, kh, vh, w.mask[h].cpu().numpy(), rows,
+                                                    w.seq_len, w.block, w.scale)
+        assert_attention_close(np64(o[h])[rows], lse[h].cpu().numpy().astype(np.float64)[rows],
+                               o_ref, l_ref, f"{name} h={h} u={u}")
+    stats = hp.stats.cpu().numpy()
+    print(f"{name}: density per head {np.round(stats[:, 1], 4).tolist()}")
+
+
+def test_full_size_gsrs_dense_pass_sampled():
+    w, hp = _run_full("gsrs75k")
+    rng = np.random.default_rng(9)
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    L, b = w.seq_len, w.block
+    rp = hp.row_ptr.cpu().numpy()
+    wts = hp.w.cpu().numpy().astype(np.float64)
+    # every row of W sums to one over the dense candidate set
+    sums = wts[: rp[-1]].reshape(H * mb, mb).sum(1)
+    np.testing.assert_allclose(sums, 1.0, atol=1e-4)
+    sel = hp.next_mask.cpu().numpy()
+    assert 0 < sel.sum() < H * mb * mb
+    for h in sorted(set([0, H - 1, int(rng.integers(H))])):
+        for u in sorted(set([mb - 1, int(rng.integers(mb))])):
+            sub = np.zeros((1, mb, mb), dtype=np.uint8)
+            sub[0, u] = 1
+            srp, sci, _, _, _ = oracle.block_index(sub)
+            q, k = np64(w.q[h:h + 1]), np64(w.k[h:h + 1])
+            g_ref, lse_ref = oracle.block_lse(q, k, srp, sci, L, b, w.scale)
+            w_ref = oracle.block_importance(g_ref, lse_ref, srp, L, b)
+            nrows = min(b, L - u * b)
+            lo = rp[h * mb + u]
+            g_gpu = hp.g[lo:lo + mb, :nrows].cpu().numpy().astype(np.float64)
+            np.testing.assert_allclose(g_gpu, g_ref[:, :nrows], atol=5e-3, rtol=0)
+            np.testing.assert_allclose(wts[lo:lo + mb], w_ref, atol=2e-4, rtol=1e-3)
+            banner(f"gsrs75k h={h} u={u} kept {int(sel[h, u].sum())} of {mb}")

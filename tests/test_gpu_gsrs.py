@@ -1,0 +1,140 @@
+"""GSRS stage on the GPU against the oracle: Phase-1 G, Phase-2 W, Top-p.
+
+G and W are compared with tolerances (fp32 against fp64); the Top-p kept sets
+are compared bit for bit for the same W, which both sides get from the seeded
+generator."""
+
+import numpy as np
+import pytest
+import torch
+
+import cache_aware_query_amd as caq
+import oracle
+import synth
+from helpers import banner, gpu, np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _g_and_w(w):
+    dev = gpu()
+    q, k, v, mask = (t.to(dev) for t in (w.q, w.k, w.v, w.mask))
+    idx = caq.build_block_index(mask)
+    o, lse, g = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx,
+                                    with_g=True)
+    wts = caq.block_importance(g, lse, idx.row_ptr, w.seq_len, w.block)
+    torch.cuda.synchronize()
+    return idx, lse, g, wts
+
+
+@pytest.mark.parametrize("case", ["tiny", "ragged128", "ragged64"])
+def test_block_lse_and_importance_match_oracle(case):
+    if case == "tiny":
+        w = synth.make_workload("tiny")
+    elif case == "ragged128":
+        w = synth.random_tiny_case(21, heads=2, seq_len=1000, head_dim=128, block=128,
+                                   density=0.5, empty_rows=(2,))
+    else:
+        w = synth.random_tiny_case(22, heads=2, seq_len=700, head_dim=64, block=64, density=0.4,
+                                   empty_rows=(0,))
+    banner(f"gsrs G/W {case}")
+    idx, lse, g, wts = _g_and_w(w)
+    rp, ci, _, _, _ = oracle.block_index(w.mask.numpy())
+    nnz = int(rp[-1])
+    g_ref, lse_ref = oracle.block_lse(np64(w.q), np64(w.k), rp, ci, w.seq_len, w.block, w.scale)
+    w_ref = oracle.block_importance(g_ref, lse_ref, rp, w.seq_len, w.block)
+    g_gpu = g.cpu().numpy()[:nnz].astype(np.float64)
+    w_gpu = wts.cpu().numpy()[:nnz].astype(np.float64)
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    L, b = w.seq_len, w.block
+    for r in range(H * mb):
+        u = r % mb
+        nrows = min(b, L - u * b)
+        lo, hi = rp[r], rp[r + 1]
+        if hi == lo:
+            continue
+        gg, gr = g_gpu[lo:hi, :nrows], g_ref[lo:hi, :nrows]
+        assert not np.isnan(gg).any()
+        np.testing.assert_allclose(gg, gr, atol=5e-3, rtol=0)
+        np.testing.assert_allclose(w_gpu[lo:hi], w_ref[lo:hi], atol=2e-4, rtol=1e-3)
+        assert abs(w_gpu[lo:hi].sum() - 1.0) < 1e-4
+
+
+def _random_weights(rng, row_ptr):
+    """Per-row fp32 weights with ties, one-hot rows, uniform rows and zero rows."""
+    nnz = int(row_ptr[-1])
+    w = np.zeros(nnz, dtype=np.float32)
+    for r in range(len(row_ptr) - 1):
+        lo, hi = row_ptr[r], row_ptr[r + 1]
+        n = hi - lo
+        if n == 0:
+            continue
+        kind = r % 5
+        if kind == 0:
+            x = rng.random(n)
+        elif kind == 1:
+            x = rng.integers(1, 4, size=n).astype(float)       # many ties
+        elif kind == 2:
+            x = np.zeros(n)
+            x[rng.integers(0, n)] = 1.0                        # one-hot
+        elif kind == 3:
+            x = np.ones(n)                                     # uniform
+        else:
+            x = rng.random(n) ** 8                             # peaked
+        w[lo:hi] = (x / x.sum()).astype(np.float32)
+    return w
+
+
+@pytest.mark.parametrize("p", [0.5, 0.8, 0.9, 0.95, 1.0])
+def test_topp_is_bit_exact_for_a_given_w(p):
+    dev = gpu()
+    rng = np.random.default_rng(31)
+    H, mb, nb = 3, 120, 150
+    mask = (rng.random((H, mb, nb)) < 0.5).astype(np.uint8)
+    mask[:, 5] = 0
+    mask[:, 7] = 1          # full rows (150 candidates)
+    mask[0, 9] = 0
+    mask[0, 9, :100] = 1    # 100 uniform weights (the fp64 accumulation trap)
+    rp, ci, _, _, _ = oracle.block_index(mask)
+    w = _random_weights(rng, rp)
+    w[rp[9]:rp[10]] = np.float32(0.01)
+    banner(f"topp p={p}")
+    sel = caq.topp_select(torch.from_numpy(w).to(dev), torch.from_numpy(rp.astype(np.int32)).to(dev),
+                          torch.from_numpy(ci.astype(np.int32)).to(dev), H, mb, nb, p)
+    torch.cuda.synchronize()
+    ref = oracle.topp_select(w, rp, ci, H, mb, nb, p)
+    np.testing.assert_array_equal(sel.cpu().numpy(), ref)
+    if p == 0.9:
+        assert int(ref[0, 9].sum()) == 91
+
+
+def test_gsrs_search_pipeline_growing_sparsity():
+    """Dense pass -> W -> Top-p(0.9) = S1; pass over S1 -> W over S1 -> Top-p(0.8) = S2."""
+    dev = gpu()
+    w = synth.make_workload("gsrs75k", device="cuda", heads=2, grid=(3, 45, 80))
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    banner(f"gsrs pipeline H={H} MB={mb}")
+    idx, lse, g, wts = _g_and_w(w)
+    s1 = caq.topp_select(wts, idx.row_ptr, idx.col_idx, H, mb, mb, 0.9)
+    idx1 = caq.build_block_index(s1)
+    o1, lse1, g1 = caq.sparse_attn_fwd(w.q.to(dev), w.k.to(dev), w.v.to(dev), w.seq_len, w.block,
+                                       idx1.row_ptr, idx1.col_idx, with_g=True)
+    w1 = caq.block_importance(g1, lse1, idx1.row_ptr, w.seq_len, w.block)
+    s2 = caq.topp_select(w1, idx1.row_ptr, idx1.col_idx, H, mb, mb, 0.8)
+    torch.cuda.synchronize()
+    s1n, s2n = s1.cpu().numpy(), s2.cpu().numpy()
+    assert np.all(s2n <= s1n)
+    assert 0 < s2n.sum() < s1n.sum() < H * mb * mb
+    # every non-empty row of W over S1 sums to one
+    rp1 = idx1.row_ptr.cpu().numpy()
+    wn = w1.cpu().numpy().astype(np.float64)
+    sums = np.add.reduceat(wn[: rp1[-1]], rp1[:-1][np.diff(rp1) > 0])
+    np.testing.assert_allclose(sums, 1.0, atol=1e-4)
+    # the oracle's S1 from its own W agrees except at cumulative-sum near-ties
+    q, k = np64(w.q), np64(w.k)
+    rp, ci, _, _, _ = oracle.block_index(w.mask.cpu().numpy())
+    g_ref, lse_ref = oracle.block_lse(q, k, rp, ci, w.seq_len, w.block, w.scale)
+    w_ref = oracle.block_importance(g_ref, lse_ref, rp, w.seq_len, w.block).astype(np.float32)
+    s1_ref = oracle.topp_select(w_ref, rp, ci, H, mb, mb, 0.9)
+    diff = np.sum(s1_ref != s1n)
+    assert diff <= max(2, 0.002 * s1_ref.sum()), diff

@@ -1,0 +1,126 @@
+"""wa_reorder_rows against the oracle's reordering (same mask, same start block).
+
+Bit-exact: the statistics and skip flags, the identity order of skipped heads,
+permutation validity, and the Stage-2 structure (each bucket holds the positions
+of the GPU's own angle order and is sorted by descending NNZ, ties in angle
+order).  fp64 on both sides: angles agree with the oracle's to 1e-9, and the
+permutations are equal except where the oracle itself has a near-tie.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import cache_aware_query_amd as caq
+import oracle
+import synth
+from helpers import banner, gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_reorder(mask, x0, block, head_dim, params):
+    dev = gpu()
+    idx = caq.build_block_index(mask.to(dev))
+    ro = caq.reorder_rows(idx, x0.to(dev), block, head_dim, params)
+    torch.cuda.synchronize()
+    return ro
+
+
+def _oracle_params(p: caq.ReorderParams):
+    return oracle.ReorderParams(wave=p.wave, n_slices=p.n_slices, iters=p.iters,
+                                stage1=p.stage1, stage2=p.stage2, skip_mode=p.skip_mode,
+                                ws_min_bytes=p.ws_min_bytes, flops_min=p.flops_min,
+                                jaccard_max=p.jaccard_max)
+
+
+def _check_structure(perm, angles, nnz, skipped, p):
+    """Validity and Stage-2 structure of one head's GPU permutation."""
+    mb = perm.size
+    assert sorted(perm.tolist()) == list(range(mb))
+    if skipped:
+        assert perm.tolist() == list(range(mb))
+        return
+    if p.stage1 and np.all(np.isfinite(angles)):
+        order = np.argsort(angles, kind="stable")
+    else:
+        order = np.arange(mb)
+    buckets = oracle.wave_buckets(mb, p.n_slices, p.wave) if p.stage2 else [(0, mb)]
+    pos_in_order = np.empty(mb, dtype=np.int64)
+    pos_in_order[order] = np.arange(mb)
+    for lo, hi in buckets:
+        seg = perm[lo:hi]
+        assert sorted(seg.tolist()) == sorted(order[lo:hi].tolist())
+        if p.stage2:
+            key = list(zip((-nnz[seg]).tolist(), pos_in_order[seg].tolist()))
+            assert key == sorted(key)
+        else:
+            assert seg.tolist() == order[lo:hi].tolist()
+
+
+CASES = [
+    ("tiny", {}, caq.ReorderParams(wave=4, n_slices=2, skip_mode=caq.WA_SKIP_NEVER)),
+    ("layer16k", {}, caq.ReorderParams(wave=64, n_slices=8, skip_mode=caq.WA_SKIP_NEVER)),
+    ("layer16k", {}, caq.ReorderParams(wave=32, n_slices=1, skip_mode=caq.WA_SKIP_NEVER)),
+    ("layer16k", {}, caq.ReorderParams(wave=64, n_slices=8, skip_mode=caq.WA_SKIP_ADAPTIVE,
+                                       jaccard_max=0.35, flops_min=1e11)),
+    ("layer16k", {}, caq.ReorderParams(wave=16, n_slices=4, stage1=False,
+                                       skip_mode=caq.WA_SKIP_NEVER)),
+    ("layer16k", {}, caq.ReorderParams(wave=16, n_slices=4, stage2=False,
+                                       skip_mode=caq.WA_SKIP_NEVER)),
+    ("wan75k", {"heads": 4}, caq.ReorderParams(wave=64, n_slices=8, skip_mode=caq.WA_SKIP_NEVER)),
+    ("gsrs75k", {"heads": 2}, caq.ReorderParams(wave=64, n_slices=8, skip_mode=caq.WA_SKIP_NEVER)),
+]
+
+
+@pytest.mark.parametrize("name,over,params", CASES)
+def test_reorder_matches_oracle(name, over, params):
+    w = synth.make_workload(name, device="cuda" if name != "tiny" else "cpu", **over)
+    mask = w.mask.cpu()
+    x0 = w.x0.cpu()
+    banner(f"reorder {name} {over} {params}")
+    ro = _gpu_reorder(mask, x0, w.block, w.head_dim, params)
+    perm_g = ro.perm.cpu().numpy()
+    inv_g = ro.inv_perm.cpu().numpy()
+    skip_g = ro.skipped.cpu().numpy().astype(bool)
+    ang_g = ro.angles.cpu().numpy()
+    st_g = ro.stats.cpu().numpy()
+    m = mask.numpy()
+    perm_o, _, skip_o, ang_o, st_o = oracle.reorder_rows(m, x0.numpy().astype(np.float64),
+                                                         w.block, w.head_dim,
+                                                         _oracle_params(params))
+    np.testing.assert_array_equal(st_g, st_o)
+    np.testing.assert_array_equal(skip_g, skip_o)
+    H, mb = perm_g.shape
+    for h in range(H):
+        nnz = m[h].astype(np.int64).sum(1)
+        _check_structure(perm_g[h], ang_g[h], nnz, skip_g[h], params)
+        np.testing.assert_array_equal(inv_g[h][perm_g[h]], np.arange(mb))
+        both = np.isfinite(ang_o[h])
+        np.testing.assert_array_equal(np.isfinite(ang_g[h]), both)
+        np.testing.assert_allclose(ang_g[h][both], ang_o[h][both], atol=1e-9, rtol=0)
+        if not np.array_equal(perm_g[h], perm_o[h]):
+            # Only a near-tie of the oracle's own angles may reorder rows.
+            srt = np.sort(ang_o[h][both])
+            assert srt.size and np.min(np.diff(srt)) < 1e-9, f"head {h}: permutations differ"
+
+
+def test_reorder_is_deterministic():
+    w = synth.make_workload("layer16k", heads=4)
+    p = caq.ReorderParams(skip_mode=caq.WA_SKIP_NEVER)
+    banner("reorder determinism")
+    a = _gpu_reorder(w.mask, w.x0, w.block, w.head_dim, p)
+    b = _gpu_reorder(w.mask, w.x0, w.block, w.head_dim, p)
+    assert torch.equal(a.perm, b.perm) and torch.equal(a.angles.nan_to_num(), b.angles.nan_to_num())
+
+
+def test_dense_mask_keeps_identity_stage1():
+    m = torch.ones(2, 16, 16, dtype=torch.uint8)
+    x0 = torch.rand(2, 16, 2) * 2 - 1
+    banner("reorder dense mask")
+    ro = _gpu_reorder(m, x0, 128, 128, caq.ReorderParams(wave=4, n_slices=2,
+                                                         skip_mode=caq.WA_SKIP_NEVER))
+    assert ro.perm.cpu().tolist() == [list(range(16))] * 2
+    assert torch.isnan(ro.angles).all()
+    ro = _gpu_reorder(m, x0, 128, 128, caq.ReorderParams(jaccard_max=0.9))
+    assert ro.skipped.cpu().tolist() == [1, 1]
