@@ -304,7 +304,8 @@ def random_tiny_case(seed: int, heads: int = 2, seq_len: int = 300, head_dim: in
         idx = torch.arange(nb, device=device)
         mask[:, idx, idx] = 1
     for r in empty_rows:
-        mask[:, r, :] = 0
+        if r < nb:
+            mask[:, r, :] = 0
     x0 = torch.rand(heads, nb, 2, generator=g, device=device) * 2.0 - 1.0
     cfg = WorkloadConfig(f"random{seed}", 100 + seed, heads, head_dim, (1, 1, seq_len), block,
                          "gaussian", "bernoulli")
