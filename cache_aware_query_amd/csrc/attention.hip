@@ -63,44 +63,54 @@ __device__ inline int pi_row(int i) {
 template <int BLOCK, int D>
 struct Tile {
   static constexpr int kWaves = BLOCK / 32;
-  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kHalves = BLOCK / 64;   // 64-key halves of a K/V tile
   static constexpr int kKChunks = D / 8;       // 16-byte chunks per K row
   static constexpr int kVChunks = BLOCK / 8;   // 16-byte chunks per V^T row
-  static constexpr int kKBytes = BLOCK * D * 2;
-  static constexpr int kVBytes = D * BLOCK * 2;
-  static constexpr int kKInst = kKBytes / 1024;  // 1 KiB per wavefront instruction
-  static constexpr int kVInst = kVBytes / 1024;
-  static constexpr int kMT = BLOCK / 32;   // key tiles of S^T
-  static constexpr int kKS = D / 16;       // contraction steps of S^T
-  static constexpr int kDT = D / 32;       // d tiles of O^T
-  static constexpr int kPS = BLOCK / 16;   // contraction steps of O^T
+  static constexpr int kSubBytes = 64 * D * 2; // one half of the K or V^T tile
+  static constexpr int kSubInst = kSubBytes / 1024 / kWaves;  // DMA instructions per wave
+  static constexpr int kKS = D / 16;           // contraction steps of S^T
+  static constexpr int kDT = D / 32;           // d tiles of O^T
+  // Outstanding vector-memory operations allowed while waiting for one sub-tile:
+  // with two halves the three sub-tile loads issued after it (minus slack for one
+  // G store, which only makes the wait stricter) may stay in flight.
+  static constexpr int kWaitN = kHalves == 2 ? 2 * kSubInst : 0;
 };
 
-template <int BLOCK, int D>
-__device__ inline void load_tiles(char* sk, char* sv, const uint16_t* __restrict__ kh,
-                                  const uint16_t* __restrict__ vth, int key0, int Lp, int wave,
-                                  int lane) {
-  using T = Tile<BLOCK, D>;
-#pragma unroll
-  for (int i = wave; i < T::kKInst; i += T::kWaves) {
-    const int flat = i * 1024 + lane * 16;
-    const int r = flat / (D * 2);
-    const int slot = (flat % (D * 2)) / 16;
-    const int c = slot ^ swz_k<T::kKChunks>(r);
-    const uint16_t* src = kh + (size_t)(key0 + r) * D + c * 8;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(sk + i * 1024),
-                                     16, 0, 0);
-  }
-#pragma unroll
-  for (int i = wave; i < T::kVInst; i += T::kWaves) {
-    const int flat = i * 1024 + lane * 16;
-    const int d = flat / (BLOCK * 2);
-    const int slot = (flat % (BLOCK * 2)) / 16;
-    const int c = slot ^ swz_v<T::kVChunks>(d);
-    const uint16_t* src = vth + (size_t)d * Lp + key0 + c * 8;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(sv + i * 1024),
-                                     16, 0, 0);
-  }
+// Lazy softmax reference: the running maximum used as the exponent reference
+// only moves when a new block maximum exceeds it by more than kTau (log2
+// units), so most tiles need no rescale of the output accumulator; the
+// probabilities stay below 2^kTau, far inside bf16 and fp32 range.
+constexpr float kTau = 8.0f;
+// A half tile whose maximum lies more than kLow below the reference takes its
+// own maximum as reference, so that its block log-sum-exp keeps full precision.
+constexpr float kLow = 64.0f;
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4,
+// saddr form: wave-uniform base in SGPRs plus a per-lane 32-bit offset; the LDS
+// destination is the wave-uniform lds_addr plus 16 bytes per lane).  Issued
+// through inline assembly so that the compiler does not serialise the copy
+// against later LDS reads of other buffers; completion is awaited explicitly with
+// wait_vmcnt (vector-memory operations retire in issue order).  M0 is saved and
+// restored around the copy.
+__device__ inline void dma16(const char* base, uint32_t off, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(off), "s"(base)
+      : "memory");
+}
+
+__device__ inline uint32_t lds_address(const char* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)p;
 }
 
 template <int BLOCK, int D, bool WITH_G>
@@ -111,9 +121,12 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    int cap, const int32_t* __restrict__ perm, int schedule, float scale_log2,
                    uint16_t* __restrict__ O, float* __restrict__ lse, float* __restrict__ G) {
   using T = Tile<BLOCK, D>;
-  __shared__ __attribute__((aligned(1024))) char smem[T::kKBytes + T::kVBytes];
-  char* sk = smem;
-  char* sv = smem + T::kKBytes;
+  // Four separate LDS objects (K and V^T halves) so that the compiler can tell the
+  // asynchronous copies into one from the reads of another.
+  __shared__ __attribute__((aligned(1024))) char sk0[T::kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char sk1[T::kHalves == 2 ? T::kSubBytes : 16];
+  __shared__ __attribute__((aligned(1024))) char sv0[T::kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char sv1[T::kHalves == 2 ? T::kSubBytes : 16];
 
   const int Lp = MB * BLOCK;
   int h, pos;
@@ -131,7 +144,7 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int u = perm ? perm[h * MB + pos] : pos;
   if ((unsigned)u >= (unsigned)MB) return;  // malformed permutation entry: nothing to run
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
   const int i32 = lane & 31;
@@ -140,7 +153,7 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
   const int e0 = min(row_ptr[h * MB + u], cap);
   const int e1 = min(row_ptr[h * MB + u + 1], cap);
-  if (e0 == e1) {  // fully masked query block: O = 0, LSE = -inf
+  if (e0 >= e1) {  // fully masked query block: O = 0, LSE = -inf
 #pragma unroll
     for (int c = 0; c < D / 8; c += 2) {
       uint4* dst = reinterpret_cast<uint4*>(O + head_off + (size_t)qrow * D + (c + g) * 8);
@@ -149,6 +162,43 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     if (g == 0) lse[(size_t)h * Lp + qrow] = -INFINITY;
     return;
   }
+
+  // Per-lane byte offsets of this wave's DMA chunks inside a K half (rows = keys)
+  // and a V^T half (rows = d, 64 keys wide), relative to the half's global base.
+  uint32_t koff[T::kSubInst], voff[T::kSubInst];
+#pragma unroll
+  for (int j = 0; j < T::kSubInst; ++j) {
+    const int flat = (wave + j * T::kWaves) * 1024 + lane * 16;
+    const int r = flat / (D * 2);
+    const int ks = (flat % (D * 2)) / 16;
+    koff[j] = (uint32_t)(r * D * 2 + ((ks ^ swz_k<T::kKChunks>(r)) * 16));
+    const int d = flat / 128;  // a V^T half row is 64 keys = 128 bytes
+    const int vs = (flat % 128) / 16;
+    voff[j] = (uint32_t)((size_t)d * Lp * 2 + ((vs ^ swz_v<8>(d)) * 16));
+  }
+  const char* kbytes = reinterpret_cast<const char*>(K + head_off);
+  const char* vbytes = reinterpret_cast<const char*>(Vt + head_off);
+  const uint32_t lk[2] = {lds_address(sk0), lds_address(sk1)};
+  const uint32_t lv[2] = {lds_address(sv0), lds_address(sv1)};
+  auto issue_k = [&](int v, int half) {
+    const char* base = kbytes + ((size_t)v * BLOCK + 64 * half) * D * 2;
+#pragma unroll
+    for (int j = 0; j < T::kSubInst; ++j)
+      dma16(base, koff[j], lk[half] + (uint32_t)((wave + j * T::kWaves) * 1024));
+  };
+  auto issue_v = [&](int v, int half) {
+    const char* base = vbytes + ((size_t)v * BLOCK + 64 * half) * 2;
+#pragma unroll
+    for (int j = 0; j < T::kSubInst; ++j)
+      dma16(base, voff[j], lv[half] + (uint32_t)((wave + j * T::kWaves) * 1024));
+  };
+  // Block id of CSR entry e, or 0 for an entry outside [0, MB) (then copied but
+  // not used, so that every iteration issues the same copies).  Read as a
+  // wave-uniform value so that the copy bases stay in scalar registers.
+  auto block_of = [&](int e) {
+    const int v = __builtin_amdgcn_readfirstlane(col_idx[e]);
+    return ((unsigned)v < (unsigned)MB) ? v : 0;
+  };
 
   // Q fragment (B operand of S^T): lane holds q[qrow][16*ks + 8*g .. +7].
   bf16x8 qf[T::kKS];
@@ -164,106 +214,152 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   for (int dt = 0; dt < T::kDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.0f;
-  float m_run = -INFINITY;  // running max (log2 units)
-  float l_run = 0.0f;       // this lane's half of the running sum
+  float m_run = -INFINITY;  // exponent reference (log2 units)
+  float l_run = 0.0f;       // this lane's part of the running sum
 
-  const uint16_t* kh = K + head_off;
-  const uint16_t* vth = Vt + head_off;
+  // Prologue: the first tile's K halves and first V half.
+  int v_cur = block_of(e0);
+  issue_k(v_cur, 0);
+  if constexpr (T::kHalves == 2) {
+    issue_v(v_cur, 0);
+    issue_k(v_cur, 1);
+  }
 
   for (int e = e0; e < e1; ++e) {
-    const int v = col_idx[e];
-    if ((unsigned)v >= (unsigned)MB) continue;  // malformed block id: skipped (uniform)
-    const int key0 = v * BLOCK;
-    __syncthreads();  // every wave is done reading the previous tiles
-    load_tiles<BLOCK, D>(sk, sv, kh, vth, key0, Lp, wave, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    const bool last = e + 1 == e1;
+    const bool ok = (unsigned)col_idx[e] < (unsigned)MB;
+    const int v_next = last ? 0 : block_of(e + 1);
+    const int key0 = v_cur * BLOCK;
+    const int valid = L - key0;  // valid keys in this tile (>= 1 for a valid block)
+    float c_half[2] = {-INFINITY, -INFINITY};
+    float r_half[2] = {0.0f, 0.0f};
 
-    // S^T = K Q^T, one 32-key tile at a time.
-    f32x16 acc_s[T::kMT];
 #pragma unroll
-    for (int mt = 0; mt < T::kMT; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_s[mt][r] = 0.0f;
-      const int krow = mt * 32 + pi_row(i32);
-      const char* base = sk + krow * (D * 2);
-      const int sw = swz_k<T::kKChunks>(krow);
-#pragma unroll
-      for (int ks = 0; ks < T::kKS; ++ks) {
-        const int c = 2 * ks + g;
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(base + 16 * (c ^ sw)));
-        acc_s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], acc_s[mt], 0, 0, 0);
+    for (int hh = 0; hh < T::kHalves; ++hh) {
+      // ---- wait for K half hh, then S^T for its 64 keys ----
+      if (last) wait_vmcnt<0>(); else wait_vmcnt<T::kWaitN>();
+      __syncthreads();
+      // Copies issued once every wave has passed this barrier, i.e. finished
+      // the previous P.V product: with two halves, V half 1 of this tile (hh = 0)
+      // and V half 0 of the next tile (hh = 1); with one half, this tile's V.
+      if constexpr (T::kHalves == 2) {
+        if (hh == 0) issue_v(v_cur, 1);
+        else if (!last) issue_v(v_next, 0);
+      } else {
+        issue_v(v_cur, 0);
       }
-    }
-
-    // Keys past L in the last block never enter the softmax.
-    const int valid = L - key0;
-    if (valid < BLOCK) {
+      const bool live = ok && valid > 64 * hh;  // uniform: the half holds valid keys
+      f32x16 acc_s[2];
+      const char* sk = hh ? sk1 : sk0;
+      if (live) {
 #pragma unroll
-      for (int mt = 0; mt < T::kMT; ++mt)
+        for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = mt * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-          if (key >= valid) acc_s[mt][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) acc_s[mt][r] = 0.0f;
+          const int krow = mt * 32 + pi_row(i32);
+          const char* base = sk + krow * (D * 2);
+          const int sw = swz_k<T::kKChunks>(krow);
+#pragma unroll
+          for (int ks = 0; ks < T::kKS; ++ks) {
+            const int c = 2 * ks + g;
+            const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(base + 16 * (c ^ sw)));
+            acc_s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], acc_s[mt], 0, 0, 0);
+          }
         }
-    }
-
-    // Online softmax (log2 domain, scale folded into the exponent).
-    float mx = -INFINITY;
+        // Keys past L in the last tile never enter the softmax.
+        const int vh = valid - 64 * hh;
+        if (vh < 64) {
 #pragma unroll
-    for (int mt = 0; mt < T::kMT; ++mt)
+          for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[mt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_blk = mx * scale_log2;
-    const float m_new = fmaxf(m_run, m_blk);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    // Reference of the exponentials: the block max when G is wanted (so that the
-    // block sum is exact), the running max otherwise.
-    const float ref = WITH_G ? m_blk : m_new;
-    float psum = 0.0f;
+            for (int r = 0; r < 16; ++r) {
+              const int key = mt * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+              if (key >= vh) acc_s[mt][r] = -INFINITY;
+            }
+        }
+        // ---- online softmax over the half ----
+        float mx = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < T::kMT; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(acc_s[mt][r], scale_log2, -ref));
-        acc_s[mt][r] = p;
-        psum += p;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[mt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_h = mx * scale_log2;
+        const bool grow = m_h > m_run + kTau;
+        const float m_ref = grow ? m_h : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+        bool low = false;
+        float c = m_ref;
+        if constexpr (WITH_G) {
+          low = m_h < m_ref - kLow;
+          c = low ? m_h : m_ref;
+        }
+        float psum = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(acc_s[mt][r], scale_log2, -c));
+            acc_s[mt][r] = pv;
+            psum += pv;
+          }
+        float beta = 1.0f;
+        if constexpr (WITH_G) {
+          c_half[hh] = c;
+          r_half[hh] = psum;
+          if (__builtin_amdgcn_ballot_w64(low) != 0) {
+            beta = low ? __builtin_amdgcn_exp2f(m_h - m_ref) : 1.0f;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc_s[mt][r] *= beta;
+          }
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+          for (int dt = 0; dt < T::kDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+        }
+        l_run = l_run * alpha + psum * beta;
+        m_run = m_ref;
       }
-    float beta = 1.0f;
-    if constexpr (WITH_G) {
-      const float rsum = psum + __shfl_xor(psum, 32);
-      if (g == 0) G[(size_t)e * BLOCK + wave * 32 + i32] = (m_blk + __log2f(rsum)) * kLn2;
-      beta = __builtin_amdgcn_exp2f(m_blk - m_new);
-#pragma unroll
-      for (int mt = 0; mt < T::kMT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_s[mt][r] *= beta;
-    }
-    l_run = l_run * alpha + psum * beta;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < T::kDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+      if constexpr (WITH_G) {
+        if (hh == T::kHalves - 1 && ok) {
+          // Block log-sum-exp of the tile from the halves' (reference, sum) pairs.
+          const float R0 = r_half[0] + __shfl_xor(r_half[0], 32);
+          const float R1 = r_half[1] + __shfl_xor(r_half[1], 32);
+          const float M = fmaxf(c_half[0], c_half[1]);
+          const float sum = R0 * __builtin_amdgcn_exp2f(c_half[0] - M) +
+                            R1 * __builtin_amdgcn_exp2f(c_half[1] - M);
+          if (g == 0) G[(size_t)e * BLOCK + wave * 32 + i32] = (M + __log2f(sum)) * kLn2;
+        }
+      }
 
-    // O^T += V^T P^T.  P for contraction step ps is registers 8*(ps%2)..+7 of key
-    // tile ps/2, rounded to bf16.
+      // ---- wait for V^T half hh, then O^T += V^T P^T over its 64 keys ----
+      if (last) wait_vmcnt<0>(); else wait_vmcnt<T::kWaitN>();
+      __syncthreads();
+      if (!last) issue_k(v_next, hh);
+      if (live) {
+        const char* sv = hh ? sv1 : sv0;
 #pragma unroll
-    for (int ps = 0; ps < T::kPS; ++ps) {
-      bf16x8 pb;
+        for (int ps = 0; ps < 4; ++ps) {
+          bf16x8 pb;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[j] = (__bf16)acc_s[ps >> 1][8 * (ps & 1) + j];
-      const int c = 2 * ps + g;
+          for (int j = 0; j < 8; ++j) pb[j] = (__bf16)acc_s[ps >> 1][8 * (ps & 1) + j];
+          const int c = 2 * ps + g;
 #pragma unroll
-      for (int dt = 0; dt < T::kDT; ++dt) {
-        const int drow = dt * 32 + i32;
-        const char* base = sv + drow * (BLOCK * 2);
-        const bf16x8 a = as_bf16x8(
-            *reinterpret_cast<const uint4*>(base + 16 * (c ^ swz_v<T::kVChunks>(drow))));
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc_o[dt], 0, 0, 0);
+          for (int dt = 0; dt < T::kDT; ++dt) {
+            const int drow = dt * 32 + i32;
+            const char* base = sv + drow * 128;
+            const bf16x8 a = as_bf16x8(
+                *reinterpret_cast<const uint4*>(base + 16 * (c ^ swz_v<8>(drow))));
+            acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc_o[dt], 0, 0, 0);
+          }
+        }
       }
     }
+    v_cur = v_next;
   }
 
   // Normalise and store.  Register r of d tile dt holds d = 32*dt + 8*(r/4) + 4*g + r%4.
