@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--workload", default="wan75k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="before the steps, run three plain device copies of this many MiB "
+                         "(a known-size reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -137,6 +140,16 @@ def main():
                  schedule=caq.WA_SCHED_XCD_SLICED, gsrs_p=0.9)
     _log(f"H={H} L={L} d={d} b={b} MB={mb} nnz={nnz} density={nnz / (H * mb * mb):.4f} "
          f"xcd={n_xcd} cus/xcd={cus} wave={wave}")
+
+    if args.copy_calib_mb > 0:
+        n = args.copy_calib_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        _log(f"copy calibration: 3 copies of {n} bytes")
+        del src, dst
 
     def step(ev=None):
         hp.build_index(w.mask)
