@@ -11,25 +11,34 @@
 //
 // Mapping onto the hardware
 // -------------------------
-//  * One workgroup per query block: BLOCK/32 wavefronts, each owning 32 query rows.
+//  * One workgroup per query block: BLOCK/32 wavefronts, each owning 32 query rows;
+//    two workgroups share a compute unit (two wavefronts per SIMD).
 //  * Both products are computed transposed with v_mfma_f32_32x32x16_bf16:
 //      S^T = K Q^T   (A = K rows from LDS, B = this wave's Q rows in registers)
 //      O^T = V^T P^T (A = V^T rows from LDS, B = P taken straight from S^T)
 //    In both outputs a lane owns one query row (column of the 32x32 tile), so the
 //    row max needs one cross-lane exchange (lanes l and l^32 hold the two halves of
-//    a row) and the row sum needs none until the end.  The K rows feeding the A
-//    operand of S^T are permuted (pi below) so that the accumulator registers of
-//    S^T are, register for register, the B operand of the P.V product: no data
-//    moves between the two products.
-//  * K and V^T tiles are copied HBM/L2 -> LDS with global_load_lds_dwordx4 (no
-//    VGPR staging), in 16-byte chunks whose position inside a row is XOR-swizzled
-//    so that the 16 lanes of an LDS read phase hit distinct banks.  V is
-//    transposed once per call by a separate pass into the workspace.
+//    a row, swapped with v_permlane32_swap) and the row sum none until the end.
+//    The K rows feeding the A operand of S^T are permuted (pi below) so that the
+//    accumulator registers of S^T are, register for register, the B operand of the
+//    P.V product: no data moves between the two products.  Row sums are taken from
+//    the bf16 probabilities with dot products against 1.
+//  * The list is walked in 32-key quarters, software-pipelined: the S^T product of
+//    quarter q+1 is issued while the softmax of quarter q runs, and the P.V product
+//    of quarter q while the row maximum of quarter q+1 is taken.
+//  * K and V^T are copied HBM/L2 -> LDS with global_load_lds_dwordx4 (no VGPR
+//    staging) in 64-key halves, double-buffered, in 16-byte chunks whose position
+//    inside a row is XOR-swizzled so that the 16 lanes of an LDS read phase hit
+//    distinct banks.  V is transposed once per call by a separate pass into the
+//    workspace.  The query block's K/V list is staged in LDS so that block ids
+//    never wait on scalar memory inside the loop.
 //  * Workgroup -> query block: natural head-major order, or XCD-sliced: workgroup
 //    w runs on XCD w % 8 (round-robin dispatch), and XCD x takes the x-th
 //    contiguous slice of each head's execution order, so each XCD's L2 sees one
 //    contiguous run of the (reordered) schedule and all XCDs stay on one head.
 #include <math.h>
+
+#include <type_traits>
 
 #include "wa_internal.h"
 
@@ -51,7 +60,7 @@ __device__ inline int swz_k(int r) {
 }
 template <int CHUNKS>
 __device__ inline int swz_v(int r) {
-  return r & (CHUNKS - 1);
+  return (r >> 1) & (CHUNKS - 1);
 }
 
 // Key row of a 32-key tile that feeds A-operand row i of S^T, chosen so that
@@ -70,18 +79,17 @@ struct Tile {
   static constexpr int kSubInst = kSubBytes / 1024 / kWaves;  // DMA instructions per wave
   static constexpr int kKS = D / 16;           // contraction steps of S^T
   static constexpr int kDT = D / 32;           // d tiles of O^T
-  // Outstanding vector-memory operations allowed while waiting for one sub-tile:
-  // with two halves the three sub-tile loads issued after it (minus slack for one
-  // G store, which only makes the wait stricter) may stay in flight.
-  static constexpr int kWaitN = kHalves == 2 ? 2 * kSubInst : 0;
 };
+
+// Entries of a query block's K/V list staged in LDS.
+constexpr int kListCap = 1024;
 
 // Lazy softmax reference: the running maximum used as the exponent reference
 // only moves when a new block maximum exceeds it by more than kTau (log2
 // units), so most tiles need no rescale of the output accumulator; the
 // probabilities stay below 2^kTau, far inside bf16 and fp32 range.
 constexpr float kTau = 8.0f;
-// A half tile whose maximum lies more than kLow below the reference takes its
+// A quarter whose maximum lies more than kLow below the reference takes its
 // own maximum as reference, so that its block log-sum-exp keeps full precision.
 constexpr float kLow = 64.0f;
 
@@ -95,23 +103,55 @@ __device__ inline void wait_vmcnt() {
 // destination is the wave-uniform lds_addr plus 16 bytes per lane).  Issued
 // through inline assembly so that the compiler does not serialise the copy
 // against later LDS reads of other buffers; completion is awaited explicitly with
-// wait_vmcnt (vector-memory operations retire in issue order).  M0 is saved and
-// restored around the copy.
+// wait_vmcnt (vector-memory loads retire in issue order).  M0 (the LDS
+// destination register) is declared clobbered.
 __device__ inline void dma16(const char* base, uint32_t off, uint32_t lds_addr) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
       : "s"(lds_addr), "v"(off), "s"(base)
-      : "memory");
+      : "memory", "m0");
 }
 
 __device__ inline uint32_t lds_address(const char* p) {
   return (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)p;
 }
+
+// Sum (or maximum) of lane l and lane l ^ 32, returned to both lanes.  Lanes l and
+// l ^ 32 hold the two key halves of the same query row in every product below.
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Sum of the eight bf16 values of v added to acc (two fp32 dot products with 1).
+__device__ inline float sum8(bf16x8 v, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+}
+
+// Softmax bookkeeping for one 32-key quarter, fixed before its exponentials.
+struct QuarterDecision {
+  float m_h;    // maximum of the scaled scores (log2 units), -inf if none is valid
+  float m_ref;  // exponent reference after this quarter
+  float c;      // exponent offset used for the probabilities (finite)
+  float c_g;    // the same offset as a block statistic (-inf if nothing is valid)
+  float alpha;  // rescale of the previous output and sum
+  bool grow;    // the reference moved
+  bool low;     // the quarter keeps its own maximum as offset (block LSE precision)
+};
 
 template <int BLOCK, int D, bool WITH_G>
 __global__ __launch_bounds__(BLOCK * 2) __attribute__((amdgpu_waves_per_eu(2)))
@@ -121,12 +161,13 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    int cap, const int32_t* __restrict__ perm, int schedule, float scale_log2,
                    uint16_t* __restrict__ O, float* __restrict__ lse, float* __restrict__ G) {
   using T = Tile<BLOCK, D>;
-  // Four separate LDS objects (K and V^T halves) so that the compiler can tell the
-  // asynchronous copies into one from the reads of another.
+  // Two K and two V^T half-tile buffers, separate LDS objects so that the compiler
+  // can tell the asynchronous copies into one from the reads of another.
   __shared__ __attribute__((aligned(1024))) char sk0[T::kSubBytes];
-  __shared__ __attribute__((aligned(1024))) char sk1[T::kHalves == 2 ? T::kSubBytes : 16];
+  __shared__ __attribute__((aligned(1024))) char sk1[T::kSubBytes];
   __shared__ __attribute__((aligned(1024))) char sv0[T::kSubBytes];
-  __shared__ __attribute__((aligned(1024))) char sv1[T::kHalves == 2 ? T::kSubBytes : 16];
+  __shared__ __attribute__((aligned(1024))) char sv1[T::kSubBytes];
+  __shared__ int32_t blist[kListCap + 4];
 
   const int Lp = MB * BLOCK;
   int h, pos;
@@ -163,11 +204,27 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     return;
   }
 
-  // Per-lane byte offsets of this wave's DMA chunks inside a K half (rows = keys)
+  // The query block's K/V list, staged in LDS so that the loop reads block ids
+  // without scalar-memory waits (longer lists fall back to global reads).
+  const int ntiles = e1 - e0;
+  const bool staged = ntiles <= kListCap;
+  for (int i = threadIdx.x; i < min(ntiles, kListCap); i += BLOCK * 2) blist[i] = col_idx[e0 + i];
+  __syncthreads();
+  // List entry of tile t (wave-uniform; t is clamped into the list).
+  auto list_entry = [&](int t) {
+    t = min(t, ntiles - 1);
+    return __builtin_amdgcn_readfirstlane(staged ? blist[t] : col_idx[e0 + t]);
+  };
+
+  // Per-lane byte offsets of this wave's copy chunks inside a K half (rows = keys)
   // and a V^T half (rows = d, 64 keys wide), relative to the half's global base.
-  uint32_t koff[T::kSubInst], voff[T::kSubInst];
+  // Where the swizzle does not depend on the chunk round j (every shape but
+  // block 64 with d 128) round j adds a uniform stride, kept in the scalar base.
+  constexpr bool kAffine = !(BLOCK == 64 && D == 128);
+  constexpr int kOffRegs = kAffine ? 1 : T::kSubInst;
+  uint32_t koff[kOffRegs], voff[kOffRegs];
 #pragma unroll
-  for (int j = 0; j < T::kSubInst; ++j) {
+  for (int j = 0; j < kOffRegs; ++j) {
     const int flat = (wave + j * T::kWaves) * 1024 + lane * 16;
     const int r = flat / (D * 2);
     const int ks = (flat % (D * 2)) / 16;
@@ -180,24 +237,30 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const char* vbytes = reinterpret_cast<const char*>(Vt + head_off);
   const uint32_t lk[2] = {lds_address(sk0), lds_address(sk1)};
   const uint32_t lv[2] = {lds_address(sv0), lds_address(sv1)};
-  auto issue_k = [&](int v, int half) {
-    const char* base = kbytes + ((size_t)v * BLOCK + 64 * half) * D * 2;
+
+  // The list is walked in 32-key quarters q = 0 .. NQ-1: quarter q is key tile q % 2
+  // of half q / 2; half hh is part hh % kHalves of list tile hh / kHalves and
+  // lives in K/V buffer hh % 2.
+  const int NH = (e1 - e0) * T::kHalves;
+  const int NQ = 2 * NH;
+  // K/V block to copy for list entry v: an entry outside [0, MB) copies block 0,
+  // which is then masked out, so that every half issues the same copies.  The
+  // entry is wave-uniform, so the copy bases stay in scalar registers.
+  auto copy_block = [&](int v) { return ((unsigned)v < (unsigned)MB) ? v : 0; };
+  auto issue_k = [&](int v, int hh, int buf) {
+    const char* base =
+        kbytes + ((size_t)copy_block(v) * BLOCK + 64 * (hh % T::kHalves)) * D * 2;
 #pragma unroll
     for (int j = 0; j < T::kSubInst; ++j)
-      dma16(base, koff[j], lk[half] + (uint32_t)((wave + j * T::kWaves) * 1024));
+      dma16(kAffine ? base + (size_t)j * T::kWaves * 1024 : base, koff[kAffine ? 0 : j],
+            lk[buf] + (uint32_t)((wave + j * T::kWaves) * 1024));
   };
-  auto issue_v = [&](int v, int half) {
-    const char* base = vbytes + ((size_t)v * BLOCK + 64 * half) * 2;
+  auto issue_v = [&](int v, int hh, int buf) {
+    const char* base = vbytes + ((size_t)copy_block(v) * BLOCK + 64 * (hh % T::kHalves)) * 2;
 #pragma unroll
     for (int j = 0; j < T::kSubInst; ++j)
-      dma16(base, voff[j], lv[half] + (uint32_t)((wave + j * T::kWaves) * 1024));
-  };
-  // Block id of CSR entry e, or 0 for an entry outside [0, MB) (then copied but
-  // not used, so that every iteration issues the same copies).  Read as a
-  // wave-uniform value so that the copy bases stay in scalar registers.
-  auto block_of = [&](int e) {
-    const int v = __builtin_amdgcn_readfirstlane(col_idx[e]);
-    return ((unsigned)v < (unsigned)MB) ? v : 0;
+      dma16(kAffine ? base + (size_t)j * T::kWaves * 8 * Lp * 2 : base, voff[kAffine ? 0 : j],
+            lv[buf] + (uint32_t)((wave + j * T::kWaves) * 1024));
   };
 
   // Q fragment (B operand of S^T): lane holds q[qrow][16*ks + 8*g .. +7].
@@ -209,6 +272,35 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * ks));
   }
 
+  // S^T of one 32-key tile (key tile mt of the half in a K buffer).
+  auto compute_s = [&](f32x16& acc, const char* sk, int mt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    const int krow = mt * 32 + pi_row(i32);
+    const char* base = sk + krow * (D * 2);
+    const int sw = swz_k<T::kKChunks>(krow);
+#pragma unroll
+    for (int ks = 0; ks < T::kKS; ++ks) {
+      const int c = 2 * ks + g;
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(base + 16 * (c ^ sw)));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], acc, 0, 0, 0);
+    }
+  };
+  // Keys past L (last tile) and every key of an invalid list entry leave the softmax.
+  auto mask_s = [&](f32x16& acc, int v, int q) {
+    const int hh = q >> 1;
+    const int vq = (unsigned)v < (unsigned)MB
+                       ? L - v * BLOCK - 64 * (hh % T::kHalves) - 32 * (q & 1)
+                       : 0;
+    if (vq < 32) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 16 * (r >> 3) + 8 * g + (r & 7);
+        if (key >= vq) acc[r] = -INFINITY;
+      }
+    }
+  };
+
   f32x16 acc_o[T::kDT];
 #pragma unroll
   for (int dt = 0; dt < T::kDT; ++dt)
@@ -216,154 +308,177 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.0f;
   float m_run = -INFINITY;  // exponent reference (log2 units)
   float l_run = 0.0f;       // this lane's part of the running sum
-
-  // Prologue: the first tile's K halves and first V half.
-  int v_cur = block_of(e0);
-  issue_k(v_cur, 0);
-  if constexpr (T::kHalves == 2) {
-    issue_v(v_cur, 0);
-    issue_k(v_cur, 1);
+  constexpr int kQ = BLOCK / 32;  // quarters per list tile
+  float c_q[kQ], r_q[kQ];         // per-quarter block statistics of the current tile
+#pragma unroll
+  for (int i = 0; i < kQ; ++i) {
+    c_q[i] = -INFINITY;
+    r_q[i] = 0.0f;
   }
+  float g_pending = 0.0f;  // G of the last finished tile, stored at the next half start
+  int e_pending = -1;
 
-  for (int e = e0; e < e1; ++e) {
-    const bool last = e + 1 == e1;
-    const bool ok = (unsigned)col_idx[e] < (unsigned)MB;
-    const int v_next = last ? 0 : block_of(e + 1);
-    const int key0 = v_cur * BLOCK;
-    const int valid = L - key0;  // valid keys in this tile (>= 1 for a valid block)
-    float c_half[2] = {-INFINITY, -INFINITY};
-    float r_half[2] = {0.0f, 0.0f};
+  // Row maximum of a masked quarter and the reference decisions that follow from it.
+  auto decide = [&](const f32x16& acc) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+    QuarterDecision d;
+    d.m_h = pair_max(mx) * scale_log2;
+    d.grow = d.m_h > m_run + kTau;
+    d.m_ref = d.grow ? d.m_h : m_run;
+    d.alpha = d.grow ? __builtin_amdgcn_exp2f(m_run - d.m_h) : 1.0f;
+    d.low = WITH_G && d.m_h < d.m_ref - kLow;
+    d.c_g = d.low ? d.m_h : d.m_ref;
+    d.c = d.c_g == -INFINITY ? 0.0f : d.c_g;
+    return d;
+  };
 
+  // Probabilities of quarter q (in acc, decided by d), packed to bf16 for P.V;
+  // updates the running reference and sum and, at the tile's last quarter, the
+  // pending block LSE of the tile.
+  auto softmax = [&](const f32x16& acc, const QuarterDecision& d, int v, int q, bf16x8(&pb)[2]) {
 #pragma unroll
-    for (int hh = 0; hh < T::kHalves; ++hh) {
-      // ---- wait for K half hh, then S^T for its 64 keys ----
-      if (last) wait_vmcnt<0>(); else wait_vmcnt<T::kWaitN>();
-      __syncthreads();
-      // Copies issued once every wave has passed this barrier, i.e. finished
-      // the previous P.V product: with two halves, V half 1 of this tile (hh = 0)
-      // and V half 0 of the next tile (hh = 1); with one half, this tile's V.
-      if constexpr (T::kHalves == 2) {
-        if (hh == 0) issue_v(v_cur, 1);
-        else if (!last) issue_v(v_next, 0);
-      } else {
-        issue_v(v_cur, 0);
-      }
-      const bool live = ok && valid > 64 * hh;  // uniform: the half holds valid keys
-      f32x16 acc_s[2];
-      const char* sk = hh ? sk1 : sk0;
-      if (live) {
+    for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+      for (int j = 0; j < 8; ++j)
+        pb[ps][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc[8 * ps + j], scale_log2, -d.c));
+    const float psum = sum8(pb[1], sum8(pb[0], 0.0f));
+    float lsum = psum;
+    if constexpr (WITH_G) {
+      const int qi = q % kQ;
+      c_q[qi] = d.c_g;
+      r_q[qi] = psum;
+      if (__builtin_amdgcn_ballot_w64(d.low) != 0) {
+        // Lanes whose quarter sits far below the reference: their output share uses
+        // the common reference (a value 2^-64 below it or smaller).
+        if (d.low) {
+          const float cr = d.m_ref == -INFINITY ? 0.0f : d.m_ref;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc_s[mt][r] = 0.0f;
-          const int krow = mt * 32 + pi_row(i32);
-          const char* base = sk + krow * (D * 2);
-          const int sw = swz_k<T::kKChunks>(krow);
+          for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
-          for (int ks = 0; ks < T::kKS; ++ks) {
-            const int c = 2 * ks + g;
-            const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(base + 16 * (c ^ sw)));
-            acc_s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], acc_s[mt], 0, 0, 0);
-          }
-        }
-        // Keys past L in the last tile never enter the softmax.
-        const int vh = valid - 64 * hh;
-        if (vh < 64) {
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = mt * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-              if (key >= vh) acc_s[mt][r] = -INFINITY;
-            }
-        }
-        // ---- online softmax over the half ----
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[mt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_h = mx * scale_log2;
-        const bool grow = m_h > m_run + kTau;
-        const float m_ref = grow ? m_h : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-        bool low = false;
-        float c = m_ref;
-        if constexpr (WITH_G) {
-          low = m_h < m_ref - kLow;
-          c = low ? m_h : m_ref;
-        }
-        float psum = 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(acc_s[mt][r], scale_log2, -c));
-            acc_s[mt][r] = pv;
-            psum += pv;
-          }
-        float beta = 1.0f;
-        if constexpr (WITH_G) {
-          c_half[hh] = c;
-          r_half[hh] = psum;
-          if (__builtin_amdgcn_ballot_w64(low) != 0) {
-            beta = low ? __builtin_amdgcn_exp2f(m_h - m_ref) : 1.0f;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc_s[mt][r] *= beta;
-          }
-        }
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-          for (int dt = 0; dt < T::kDT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
-        }
-        l_run = l_run * alpha + psum * beta;
-        m_run = m_ref;
-      }
-      if constexpr (WITH_G) {
-        if (hh == T::kHalves - 1 && ok) {
-          // Block log-sum-exp of the tile from the halves' (reference, sum) pairs.
-          const float R0 = r_half[0] + __shfl_xor(r_half[0], 32);
-          const float R1 = r_half[1] + __shfl_xor(r_half[1], 32);
-          const float M = fmaxf(c_half[0], c_half[1]);
-          const float sum = R0 * __builtin_amdgcn_exp2f(c_half[0] - M) +
-                            R1 * __builtin_amdgcn_exp2f(c_half[1] - M);
-          if (g == 0) G[(size_t)e * BLOCK + wave * 32 + i32] = (M + __log2f(sum)) * kLn2;
+            for (int j = 0; j < 8; ++j)
+              pb[ps][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc[8 * ps + j], scale_log2, -cr));
+          lsum = sum8(pb[1], sum8(pb[0], 0.0f));
         }
       }
-
-      // ---- wait for V^T half hh, then O^T += V^T P^T over its 64 keys ----
-      if (last) wait_vmcnt<0>(); else wait_vmcnt<T::kWaitN>();
-      __syncthreads();
-      if (!last) issue_k(v_next, hh);
-      if (live) {
-        const char* sv = hh ? sv1 : sv0;
+      if (qi == kQ - 1) {
+        const int e = e0 + q / kQ;
+        if ((unsigned)v < (unsigned)MB) {
+          float M = -INFINITY;
 #pragma unroll
-        for (int ps = 0; ps < 4; ++ps) {
-          bf16x8 pb;
+          for (int i = 0; i < kQ; ++i) M = fmaxf(M, c_q[i]);
+          float sum = 0.0f;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) pb[j] = (__bf16)acc_s[ps >> 1][8 * (ps & 1) + j];
-          const int c = 2 * ps + g;
-#pragma unroll
-          for (int dt = 0; dt < T::kDT; ++dt) {
-            const int drow = dt * 32 + i32;
-            const char* base = sv + drow * 128;
-            const bf16x8 a = as_bf16x8(
-                *reinterpret_cast<const uint4*>(base + 16 * (c ^ swz_v<8>(drow))));
-            acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc_o[dt], 0, 0, 0);
-          }
+          for (int i = 0; i < kQ; ++i) sum += pair_sum(r_q[i]) * __builtin_amdgcn_exp2f(c_q[i] - M);
+          g_pending = M == -INFINITY ? -INFINITY : (M + __log2f(sum)) * kLn2;
+          e_pending = e;
         }
       }
     }
-    v_cur = v_next;
+    l_run = l_run * d.alpha + lsum;
+    m_run = d.m_ref;
+  };
+
+  // O^T += V^T P^T over one quarter (key tile mt of the half in a V^T buffer).
+  auto pv = [&](const bf16x8(&pb)[2], const char* sv, int mt) {
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2) {
+      const int c = 2 * (2 * mt + p2) + g;
+#pragma unroll
+      for (int dt = 0; dt < T::kDT; ++dt) {
+        const int drow = dt * 32 + i32;
+        const char* base = sv + drow * 128;
+        const bf16x8 a =
+            as_bf16x8(*reinterpret_cast<const uint4*>(base + 16 * (c ^ swz_v<8>(drow))));
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[p2], acc_o[dt], 0, 0, 0);
+      }
+    }
+  };
+  auto store_pending_g = [&]() {
+    if constexpr (WITH_G) {
+      if (e_pending >= 0 && g == 0) G[(size_t)e_pending * BLOCK + wave * 32 + i32] = g_pending;
+      e_pending = -1;
+    }
+  };
+
+  // One quarter step.  On entry S of quarter q is in acc[MT] with its decision dec.
+  // Copies: K of half hh+2 is issued at the middle of half hh (once K of half hh is
+  // consumed) and V of half hh+1 at its start; each is awaited one half later, with
+  // only the younger copies (loads retire in order) left in flight.
+  f32x16 acc[2];
+  QuarterDecision dec;
+  bf16x8 pb[2];
+  // ids[i] is the list entry of tile t0 + i, t0 the tile of the step's first half.
+  auto step = [&](auto mt_c, auto buf_c, int q, int t0, const int (&ids)[4]) {
+    constexpr int MT = decltype(mt_c)::value;   // key tile of quarter q inside its half
+    constexpr int P = decltype(buf_c)::value;   // buffer of quarter q's half
+    const int hh = q >> 1;
+    const bool younger = hh + 1 < NH;
+    if (younger) wait_vmcnt<T::kSubInst>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    auto id_of_half = [&](int x) { return ids[x / T::kHalves - t0]; };
+    if constexpr (MT == 0) {
+      store_pending_g();
+      if (hh + 1 < NH) issue_v(id_of_half(hh + 1), hh + 1, 1 - P);
+    } else {
+      if (hh + 2 < NH) issue_k(id_of_half(hh + 2), hh + 2, P);
+    }
+    // S of quarter q+1 (after the last quarter the product reads a stale buffer and
+    // is unused) while this quarter's softmax runs.
+    if constexpr (MT == 0) compute_s(acc[1], P ? sk1 : sk0, 1);
+    else compute_s(acc[0], P ? sk0 : sk1, 0);
+    softmax(acc[MT], dec, id_of_half(hh), q, pb);
+    if (__builtin_amdgcn_ballot_w64(dec.grow) != 0) {
+#pragma unroll
+      for (int dt = 0; dt < T::kDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[dt][r] *= dec.alpha;
+    }
+    if (q + 1 < NQ) mask_s(acc[1 - MT], id_of_half((q + 1) >> 1), q + 1);
+    pv(pb, P ? sv1 : sv0, MT);
+    dec = decide(acc[1 - MT]);
+  };
+
+  // Prologue: K of halves 0 and 1 and V of half 0; S of quarter 0.
+  int ids[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ids[i] = list_entry(i);
+  issue_k(ids[0], 0, 0);
+  issue_v(ids[0], 0, 0);
+  if (NH > 1) {
+    issue_k(ids[1 / T::kHalves], 1, 1);
+    wait_vmcnt<2 * T::kSubInst>();
+  } else {
+    wait_vmcnt<T::kSubInst>();
   }
+  __syncthreads();
+  compute_s(acc[0], sk0, 0);
+  mask_s(acc[0], ids[0], 0);
+  dec = decide(acc[0]);
+
+  // Each iteration runs two halves (four quarters); the list entries it needs
+  // (tiles t0 .. t0+3 at most) are read one iteration ahead.
+  constexpr int kTilesPerIter = 2 / T::kHalves;
+  for (int q = 0; q < NQ; q += 4) {
+    const int t0 = (q >> 1) / T::kHalves;
+    int next[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) next[i] = list_entry(t0 + kTilesPerIter + i);
+    step(std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), q, t0, ids);
+    step(std::integral_constant<int, 1>(), std::integral_constant<int, 0>(), q + 1, t0, ids);
+    if (q + 2 < NQ) {
+      step(std::integral_constant<int, 0>(), std::integral_constant<int, 1>(), q + 2, t0, ids);
+      step(std::integral_constant<int, 1>(), std::integral_constant<int, 1>(), q + 3, t0, ids);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ids[i] = next[i];
+  }
+  store_pending_g();
 
   // Normalise and store.  Register r of d tile dt holds d = 32*dt + 8*(r/4) + 4*g + r%4.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   const float inv_l = 1.0f / l_tot;
   uint16_t* op = O + head_off + (size_t)qrow * D;
 #pragma unroll
