@@ -45,11 +45,11 @@ def _kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic_bytes_per_launch():
-    """HBM bytes per attention launch from the committed counter summary, if it
-    was taken on the current kernel source; otherwise None."""
+def _counter_profile():
+    """Figures of the committed counter summary (HBM bytes, L2 hits) if it was taken
+    on the current attention kernel source; otherwise an empty dict."""
     if not os.path.exists(TRAFFIC_FILE):
-        return None
+        return {}
     kv = {}
     with open(TRAFFIC_FILE) as f:
         for line in f:
@@ -57,24 +57,27 @@ def _traffic_bytes_per_launch():
                 a, b = line.split("=", 1)
                 kv[a.strip()] = b.strip()
     if kv.get("kernel_sha256_16") != _kernel_hash():
-        return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        return {}
+    out = {}
+    for key in ("hbm_bytes_per_launch", "hbm_read_bytes_per_launch", "l2_hit_pct"):
+        try:
+            out[key] = float(kv[key])
+        except (KeyError, ValueError):
+            pass
+    return out
 
 
-def _time_attention(hp, q, k, v, reps):
+def _time_calls(fn, reps):
+    """Average ms of fn() over reps calls, timed with events on the current stream."""
     import torch
 
-    start = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    stop = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    for i in range(reps):
-        start[i].record()
-        hp.attention(q, k, v)
-        stop[i].record()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        fn()
+    ev1.record()
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in zip(start, stop)) / reps
+    return ev0.elapsed_time(ev1) / reps
 
 
 def cpu_baseline(w, budget_s: float = 12.0):
@@ -108,6 +111,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan75k")
+    ap.add_argument("--iters", type=int, default=5,
+                    help="subspace iterations T of the reorder (the pages use 5..15)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -134,12 +139,12 @@ def main():
     nnz = int(w.mask.sum())
     flops = 4.0 * b * b * d * nnz
     n_xcd, cus, wave = caq.schedule_info(0, d)
-    params = caq.ReorderParams(wave=wave, n_slices=n_xcd, iters=10,
+    params = caq.ReorderParams(wave=wave, n_slices=n_xcd, iters=args.iters,
                                skip_mode=caq.WA_SKIP_NEVER)
     hp = HotPath(H, L, d, b, dev, capacity=nnz, reorder=params,
                  schedule=caq.WA_SCHED_XCD_SLICED, gsrs_p=0.9)
     _log(f"H={H} L={L} d={d} b={b} MB={mb} nnz={nnz} density={nnz / (H * mb * mb):.4f} "
-         f"xcd={n_xcd} cus/xcd={cus} wave={wave}")
+         f"xcd={n_xcd} cus/xcd={cus} wave={wave} T={args.iters} csc={hp.with_csc}")
 
     if args.copy_calib_mb > 0:
         n = args.copy_calib_mb << 20
@@ -176,36 +181,43 @@ def main():
     attn_ms = sum(a.elapsed_time(b_) for a, b_ in evs) / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    traffic = _traffic_bytes_per_launch()
+    prof = _counter_profile()
 
     detail = {"attn_ms": round(attn_ms, 4), "nnz_pairs": nnz,
               "selected_tflop": round(flops / 1e12, 4),
-              "skipped_heads": int(hp.skipped.sum().item())}
+              "skipped_heads": int(hp.skipped.sum().item()),
+              "reorder_iters": args.iters,
+              "hbm_read_gb_per_launch": (round(prof["hbm_read_bytes_per_launch"] / 1e9, 3)
+                                         if "hbm_read_bytes_per_launch" in prof else None),
+              "l2_hit_pct": prof.get("l2_hit_pct")}
     if not args.no_variants:
-        # Kernel time with and without reordering (same kernel, same inputs).
         reps = max(3, args.steps // 2)
-        t_reord = _time_attention(hp, w.q, w.k, w.v, reps)
-        hp_nat = HotPath(H, L, d, b, dev, capacity=nnz, reorder=None,
-                         schedule=caq.WA_SCHED_NATURAL, gsrs_p=0.9)
-        hp_nat.build_index(w.mask)
-        t_nat = _time_attention(hp_nat, w.q, w.k, w.v, reps)
-        hp_nat.schedule = caq.WA_SCHED_XCD_SLICED
-        t_xcd = _time_attention(hp_nat, w.q, w.k, w.v, reps)
-        del hp_nat
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record()
-        for _ in range(reps):
-            hp.build_index(w.mask)
-            hp.reorder_rows(w.x0)
-        s1.record()
-        torch.cuda.synchronize()
-        t_over = s0.elapsed_time(s1) / reps
-        detail.update({"attn_ms_reordered_xcd": round(t_reord, 4),
-                       "attn_ms_natural_order": round(t_nat, 4),
+        # Stage times of the reordered step.
+        t_index = _time_calls(lambda: hp.build_index(w.mask), reps)
+        t_reorder = _time_calls(lambda: hp.reorder_rows(w.x0), reps)
+        t_reord = _time_calls(lambda: hp.attention(w.q, w.k, w.v), reps)
+        t_select = _time_calls(hp.select, reps)
+        # The same kernel without reordering: identity order, natural and XCD-sliced
+        # schedules (the index it needs has no transposed lists).
+        hp_id = HotPath(H, L, d, b, dev, capacity=nnz, reorder=None,
+                        schedule=caq.WA_SCHED_XCD_SLICED, gsrs_p=0.9)
+        t_index_id = _time_calls(lambda: hp_id.build_index(w.mask), reps)
+        t_xcd = _time_calls(lambda: hp_id.attention(w.q, w.k, w.v), reps)
+        hp_id.schedule = caq.WA_SCHED_NATURAL
+        t_nat = _time_calls(lambda: hp_id.attention(w.q, w.k, w.v), reps)
+        del hp_id
+        e2e_reord = t_index + t_reorder + t_reord
+        e2e_plain = t_index_id + min(t_xcd, t_nat)
+        detail.update({"index_ms": round(t_index, 4),
+                       "reorder_ms": round(t_reorder, 4),
+                       "attn_ms_reordered_xcd": round(t_reord, 4),
+                       "gsrs_select_ms": round(t_select, 4),
+                       "index_ms_without_reorder": round(t_index_id, 4),
                        "attn_ms_identity_xcd": round(t_xcd, 4),
-                       "index_plus_reorder_ms": round(t_over, 4),
-                       "reorder_speedup_incl_overhead":
-                           round(min(t_nat, t_xcd) / (t_reord + t_over), 4)})
+                       "attn_ms_natural_order": round(t_nat, 4),
+                       "e2e_ms_reordered": round(e2e_reord, 4),
+                       "e2e_ms_unreordered_best": round(e2e_plain, 4),
+                       "reorder_speedup_incl_overhead": round(e2e_plain / e2e_reord, 4)})
 
     line = {
         "metric": "selected-block attention TFLOP/s + HBM read GB + L2 hit %, "
@@ -225,7 +237,7 @@ def main():
                    "block": b, "density": round(nnz / (H * mb * mb), 5)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic},
+                     "traffic": prof.get("hbm_bytes_per_launch")},
         "detail": detail,
     }
     if not args.no_cpu_baseline:

@@ -29,7 +29,8 @@ WA_SKIP_ALWAYS = 2
 
 EXPORTED = (
     "wa_abi_version", "wa_last_error", "wa_schedule_info", "wa_build_block_index",
-    "wa_reorder_rows", "wa_sparse_attn_workspace_size", "wa_sparse_attn_fwd",
+    "wa_reorder_rows", "wa_reorder_needs_csc", "wa_sparse_attn_workspace_size",
+    "wa_sparse_attn_fwd",
     "wa_block_importance", "wa_topp_select", "wa_gather_blocks", "wa_scatter_blocks",
 )
 
@@ -92,6 +93,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "wa_reorder_rows": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P, _I32, _I32, _I32, _I32, _I32,
                                            ctypes.POINTER(_ReorderParams), _P, _P, _P, _P, _P,
                                            _P]),
+        "wa_reorder_needs_csc": (ctypes.c_int, [_I32, _I32]),
         "wa_sparse_attn_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32,
                                                          ctypes.POINTER(ctypes.c_size_t)]),
         "wa_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _I64, _P,
@@ -203,8 +205,8 @@ def reorder_rows(index: BlockIndex, x0: torch.Tensor, block: int, head_dim: int,
     H, MB, NB = index.heads, index.mb, index.nb
     if tuple(x0.shape) != (H, MB, 2):
         raise ValueError(f"x0 must be [{H}, {MB}, 2]")
-    if index.csc_ptr is None:
-        raise ValueError("reorder_rows needs the CSC of the block index")
+    if index.csc_ptr is None and reorder_needs_csc(MB, NB):
+        raise ValueError(f"reorder_rows needs the CSC of the block index for MB={MB}, NB={NB}")
     dev = x0.device
     perm = torch.empty(H, MB, dtype=torch.int32, device=dev)
     inv = torch.empty(H, MB, dtype=torch.int32, device=dev)
@@ -212,12 +214,21 @@ def reorder_rows(index: BlockIndex, x0: torch.Tensor, block: int, head_dim: int,
     angles = torch.empty(H, MB, dtype=torch.float64, device=dev)
     stats = torch.empty(H, 5, dtype=torch.float64, device=dev)
     cp = params._c()
-    cap = min(index.col_idx.numel(), index.csc_idx.numel())
+    cap = index.col_idx.numel()
+    if index.csc_idx is not None:
+        cap = min(cap, index.csc_idx.numel())
     _check(lib.wa_reorder_rows(_ptr(index.row_ptr), _ptr(index.col_idx), _ptr(index.csc_ptr),
                                _ptr(index.csc_idx), cap, _ptr(x0), H, MB, NB, block, head_dim,
                                ctypes.byref(cp), _ptr(perm), _ptr(inv), _ptr(skipped),
                                _ptr(angles), _ptr(stats), _stream(dev)), "wa_reorder_rows")
     return Reorder(perm, inv, skipped, angles, stats)
+
+
+def reorder_needs_csc(mb: int, nb: int) -> bool:
+    """Whether reorder_rows must be given the CSC for an MB x NB mask."""
+    r = load_library().wa_reorder_needs_csc(mb, nb)
+    _check(0 if r >= 0 else r, "wa_reorder_needs_csc")
+    return r == 1
 
 
 def sparse_attn_workspace_size(heads: int, seq_len: int, head_dim: int, block: int) -> int:

@@ -81,12 +81,13 @@ int wa_reorder_rows(const int32_t* row_ptr, const int32_t* col_idx, const int32_
                     int32_t block, int32_t head_dim, const wa_reorder_params* params,
                     int32_t* perm, int32_t* inv_perm, uint8_t* skipped, double* angles,
                     double* stats, void* stream) {
-  if (!row_ptr || !col_idx || !csc_ptr || !csc_idx || !x0 || !params || !perm || !inv_perm ||
-      !skipped)
+  if (!row_ptr || !col_idx || !x0 || !params || !perm || !inv_perm || !skipped)
     return fail(WA_ERR_INVALID_ARG, "null pointer argument");
   if (H < 1 || MB < 1 || NB < 1) return fail(WA_ERR_INVALID_ARG, "H, MB, NB must be >= 1");
   if (MB > WA_MAX_BLOCKS || NB > WA_MAX_BLOCKS)
     return fail(WA_ERR_UNSUPPORTED, "MB and NB must be <= %d", WA_MAX_BLOCKS);
+  if ((!csc_ptr || !csc_idx) && wa::reorder_needs_csc(MB, NB))
+    return fail(WA_ERR_INVALID_ARG, "csc_ptr and csc_idx are required for MB=%d, NB=%d", MB, NB);
   if (block < 1 || head_dim < 1) return fail(WA_ERR_UNSUPPORTED, "block and head_dim must be >= 1");
   if (capacity < 0) return fail(WA_ERR_INVALID_ARG, "negative capacity");
   const wa_reorder_params& p = *params;
@@ -101,6 +102,14 @@ int wa_reorder_rows(const int32_t* row_ptr, const int32_t* col_idx, const int32_
                                        head_dim, p, perm, inv_perm, skipped, angles, stats,
                                        static_cast<hipStream_t>(stream)),
                     "wa_reorder_rows");
+}
+
+int wa_reorder_needs_csc(int32_t MB, int32_t NB) {
+  if (MB < 1 || NB < 1) return fail(WA_ERR_INVALID_ARG, "MB and NB must be >= 1");
+  if (MB > WA_MAX_BLOCKS || NB > WA_MAX_BLOCKS)
+    return fail(WA_ERR_UNSUPPORTED, "MB and NB must be <= %d", WA_MAX_BLOCKS);
+  ok();
+  return wa::reorder_needs_csc(MB, NB) ? 1 : 0;
 }
 
 int wa_sparse_attn_workspace_size(int32_t H, int32_t L, int32_t head_dim, int32_t block,

@@ -46,30 +46,58 @@ __global__ __launch_bounds__(256) void k_col_counts(const uint8_t* __restrict__ 
 }
 
 // Exclusive prefix sum of n counts into ptr[0..n] (ptr may alias cnt).  One
-// workgroup of 1024 threads; each thread scans a contiguous chunk.
+// workgroup of 1024 threads walks the array in tiles of 4096 counts: each thread
+// holds four consecutive counts, wavefront shuffles and one LDS pass scan the
+// tile, and the running total carries into the next tile, whose counts are
+// loaded before the current tile is scanned.
 __global__ __launch_bounds__(1024) void k_exclusive_scan(const int32_t* cnt, int32_t* ptr, int n) {
-  __shared__ int32_t part[1024];
-  const int t = threadIdx.x;
-  const int chunk = (n + 1023) / 1024;
-  const int lo = min(n, t * chunk), hi = min(n, lo + chunk);
-  int32_t s = 0;
-  for (int i = lo; i < hi; ++i) s += cnt[i];
-  part[t] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan of the 1024 partial sums.
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t add = t >= off ? part[t - off] : 0;
+  __shared__ int32_t wsum[16];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  auto load4 = [&](int base) {
+    int4 v = make_int4(0, 0, 0, 0);
+    const int i = base + 4 * t;
+    if (i < n) v.x = cnt[i];
+    if (i + 1 < n) v.y = cnt[i + 1];
+    if (i + 2 < n) v.z = cnt[i + 2];
+    if (i + 3 < n) v.w = cnt[i + 3];
+    return v;
+  };
+  int32_t carry = 0;
+  int4 cur = load4(0);
+  for (int base = 0; base < n; base += 4096) {
+    const int4 nxt = base + 4096 < n ? load4(base + 4096) : make_int4(0, 0, 0, 0);
+    const int32_t s4 = cur.x + cur.y + cur.z + cur.w;
+    // Inclusive scan of the per-thread sums across the wavefront.
+    int32_t incl = s4;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wsum[w] = incl;
     __syncthreads();
-    part[t] += add;
-    __syncthreads();
+    int32_t before = carry;
+    int32_t total = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int32_t x = wsum[j];
+      before += j < w ? x : 0;
+      total += x;
+    }
+    __syncthreads();  // wsum is rewritten by the next tile
+    int32_t run = before + incl - s4;  // exclusive prefix of this thread's first count
+    const int i = base + 4 * t;
+    if (i < n) ptr[i] = run;
+    run += cur.x;
+    if (i + 1 < n) ptr[i + 1] = run;
+    run += cur.y;
+    if (i + 2 < n) ptr[i + 2] = run;
+    run += cur.z;
+    if (i + 3 < n) ptr[i + 3] = run;
+    carry += total;
+    cur = nxt;
   }
-  int32_t run = part[t] - s;  // exclusive prefix of this chunk
-  for (int i = lo; i < hi; ++i) {
-    const int32_t c = cnt[i];
-    ptr[i] = run;
-    run += c;
-  }
-  if (t == 1023) ptr[n] = part[1023];
+  if (t == 0) ptr[n] = carry;
 }
 
 // One wavefront per row: ascending column ids of the non-zero bytes.

@@ -24,6 +24,9 @@ namespace wa {
 namespace {
 
 constexpr int kThreads = 1024;
+// Dynamic LDS the bitmask form of the reorder may use (the rest of the 160 KiB is
+// left to the kernel's static arrays).
+constexpr size_t kBitsLdsLimit = 144 * 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr double kTwoPi = 6.283185307179586;
 
@@ -185,6 +188,86 @@ __device__ void apply_m(const double2* y, const int32_t* __restrict__ cp,
   }
 }
 
+// The head's mask as bitmasks in LDS: row u is rm[u*NW .. +NW) (bit v%32 of word
+// v/32), column v is cm[v*MW .. +MW); cc[v] is the column count.  Four lanes share
+// a row or column, each summing every fourth word in ascending bit order, and the
+// four partial sums are combined with a fixed shuffle tree (so every sum has a
+// fixed order and the result is reproducible).
+struct MaskBits {
+  const uint32_t* rm;
+  const uint32_t* cm;
+  const int32_t* cc;
+  int NW, MW;
+};
+
+// Y = M^T X - c (1^T X) / MB from the column bitmasks.
+__device__ void apply_mt_bits(const double2* x, double2* y, const MaskBits& mb, int MB, int NB,
+                              double* red) {
+  const int t = threadIdx.x;
+  double2 s = make_double2(0.0, 0.0);
+  for (int u = t; u < MB; u += kThreads) {
+    s.x += x[u].x;
+    s.y += x[u].y;
+  }
+  s = block_sum2(s, red);
+  const double inv = 1.0 / (double)MB;
+  const int sub = t & 3;
+  for (int v = t >> 2; v < NB; v += kThreads / 4) {
+    double ax = 0.0, ay = 0.0;
+    const uint32_t* col = mb.cm + (size_t)v * mb.MW;
+    for (int i = sub; i < mb.MW; i += 4) {
+      uint32_t bits = col[i];
+      while (bits != 0u) {
+        const int u = 32 * i + __builtin_ctz(bits);
+        bits &= bits - 1u;
+        ax += x[u].x;
+        ay += x[u].y;
+      }
+    }
+    ax += __shfl_xor(ax, 1);
+    ay += __shfl_xor(ay, 1);
+    ax += __shfl_xor(ax, 2);
+    ay += __shfl_xor(ay, 2);
+    const double c = (double)mb.cc[v];
+    if (sub == 0) y[v] = make_double2(ax - c * s.x * inv, ay - c * s.y * inv);
+  }
+  __syncthreads();
+}
+
+// Z = M Y - 1 (c^T Y) / MB from the row bitmasks; calls f(u, z) on one lane per row.
+template <typename F>
+__device__ void apply_m_bits(const double2* y, const MaskBits& mb, int MB, int NB, double* red,
+                             F f) {
+  const int t = threadIdx.x;
+  double2 s = make_double2(0.0, 0.0);
+  for (int v = t; v < NB; v += kThreads) {
+    const double c = (double)mb.cc[v];
+    s.x += c * y[v].x;
+    s.y += c * y[v].y;
+  }
+  s = block_sum2(s, red);
+  const double inv = 1.0 / (double)MB;
+  const int sub = t & 3;
+  for (int u = t >> 2; u < MB; u += kThreads / 4) {
+    double ax = 0.0, ay = 0.0;
+    const uint32_t* row = mb.rm + (size_t)u * mb.NW;
+    for (int i = sub; i < mb.NW; i += 4) {
+      uint32_t bits = row[i];
+      while (bits != 0u) {
+        const int v = 32 * i + __builtin_ctz(bits);
+        bits &= bits - 1u;
+        ax += y[v].x;
+        ay += y[v].y;
+      }
+    }
+    ax += __shfl_xor(ax, 1);
+    ay += __shfl_xor(ay, 1);
+    ax += __shfl_xor(ax, 2);
+    ay += __shfl_xor(ay, 2);
+    if (sub == 0) f(u, make_double2(ax - s.x * inv, ay - s.y * inv));
+  }
+}
+
 // Ascending bitonic sort of n (power of two) (key, val) pairs in LDS, ordered by
 // key and then by val.
 __device__ void bitonic_sort_pairs(uint64_t* key, uint32_t* val, int n) {
@@ -210,6 +293,10 @@ __device__ void bitonic_sort_pairs(uint64_t* key, uint32_t* val, int n) {
   __syncthreads();
 }
 
+// BITS: the head's mask is first expanded into row and column bitmasks in LDS and
+// every product with M or M^T reads those (the CSC is not used); otherwise the
+// products gather through the CSR and CSC lists in global memory.
+template <bool BITS>
 __global__ __launch_bounds__(kThreads) void k_reorder(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ csc_ptr, const int32_t* __restrict__ csc_idx, int cap,
@@ -223,23 +310,58 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
   const int h = blockIdx.x;
   const int t = threadIdx.x;
   const int32_t* rp = row_ptr + (size_t)h * MB;
-  const int32_t* cp = csc_ptr + (size_t)h * NB;
+  const int32_t* cp = BITS ? nullptr : csc_ptr + (size_t)h * NB;
   int32_t* perm_h = perm + (size_t)h * MB;
   int32_t* inv_h = inv_perm + (size_t)h * MB;
   double* ang_h = angles ? angles + (size_t)h * MB : nullptr;
 
+  MaskBits bits{};
+  if constexpr (BITS) {
+    const int NW = (NB + 31) / 32, MW = (MB + 31) / 32;
+    uint32_t* rm = reinterpret_cast<uint32_t*>(lds + MB + NB);
+    uint32_t* cm = rm + (size_t)MB * NW;
+    int32_t* cc = reinterpret_cast<int32_t*>(cm + (size_t)NB * MW);
+    for (int i = t; i < MB * NW + NB * MW; i += kThreads) rm[i] = 0u;
+    __syncthreads();
+    const int w = t >> 6, lane = t & 63;
+    for (int u = w; u < MB; u += kWaves) {
+      const int lo = min(rp[u], cap), hi = min(rp[u + 1], cap);
+      for (int k = lo + lane; k < hi; k += 64) {
+        const int v = col_idx[k];
+        if ((unsigned)v < (unsigned)NB) {
+          atomicOr(&rm[(size_t)u * NW + (v >> 5)], 1u << (v & 31));
+          atomicOr(&cm[(size_t)v * MW + (u >> 5)], 1u << (u & 31));
+        }
+      }
+    }
+    __syncthreads();
+    for (int v = t; v < NB; v += kThreads) {
+      int c = 0;
+      for (int i = 0; i < MW; ++i) c += __popc(cm[(size_t)v * MW + i]);
+      cc[v] = c;
+    }
+    __syncthreads();
+    bits = MaskBits{rm, cm, cc, NW, MW};
+  }
+
   // ---- statistics and the skip decision (§IV-E) ----
   long long inter = 0, uni = 0;
   for (int u = t; u + 1 < MB; u += kThreads) {
-    int a = min(rp[u], cap), ae = min(rp[u + 1], cap);
-    int b = ae, be = min(rp[u + 2], cap);
-    const int na = ae - a, nb = be - b;
+    const int na = min(rp[u + 1], cap) - min(rp[u], cap);
+    const int nb = min(rp[u + 2], cap) - min(rp[u + 1], cap);
     int common = 0;
-    while (a < ae && b < be) {
-      const int va = col_idx[a], vb = col_idx[b];
-      common += va == vb;
-      a += va <= vb;
-      b += vb <= va;
+    if constexpr (BITS) {
+      for (int i = 0; i < bits.NW; ++i)
+        common += __popc(bits.rm[(size_t)u * bits.NW + i] & bits.rm[(size_t)(u + 1) * bits.NW + i]);
+    } else {
+      int a = min(rp[u], cap), ae = min(rp[u + 1], cap);
+      int b = ae, be = min(rp[u + 2], cap);
+      while (a < ae && b < be) {
+        const int va = col_idx[a], vb = col_idx[b];
+        common += va == vb;
+        a += va <= vb;
+        b += vb <= va;
+      }
     }
     inter += common;
     uni += na + nb - common;
@@ -281,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
   double2* Y = lds + MB;   // [NB]
   bool varied = false;
   for (int v = t; v < NB; v += kThreads) {
-    const int c = cp[v + 1] - cp[v];
+    const int c = BITS ? bits.cc[v] : cp[v + 1] - cp[v];
     varied |= (c != 0 && c != MB);
   }
   const bool embed = p.stage1 && __syncthreads_or(varied);
@@ -296,22 +418,33 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
     __syncthreads();
     qr2_inplace(X, MB, red);
     for (int it = 0; it < p.iters; ++it) {
-      apply_mt(X, Y, cp, csc_idx, cap, MB, NB, red);
-      apply_m(Y, cp, rp, col_idx, cap, MB, NB, red, [&](int u, double2 z) { X[u] = z; });
+      if constexpr (BITS) {
+        apply_mt_bits(X, Y, bits, MB, NB, red);
+        apply_m_bits(Y, bits, MB, NB, red, [&](int u, double2 z) { X[u] = z; });
+      } else {
+        apply_mt(X, Y, cp, csc_idx, cap, MB, NB, red);
+        apply_m(Y, cp, rp, col_idx, cap, MB, NB, red, [&](int u, double2 z) { X[u] = z; });
+      }
       __syncthreads();
       qr2_inplace(X, MB, red);
     }
     // Ritz rotation: B = X^T Z with Z = M~ M~^T X, symmetrised; rotate X onto the
     // eigenvectors of B, larger eigenvalue first.
-    apply_mt(X, Y, cp, csc_idx, cap, MB, NB, red);
     double b00 = 0.0, b01 = 0.0, b10 = 0.0, b11 = 0.0;
-    apply_m(Y, cp, rp, col_idx, cap, MB, NB, red, [&](int u, double2 z) {
+    auto ritz_acc = [&](int u, double2 z) {
       const double2 xu = X[u];
       b00 += xu.x * z.x;
       b01 += xu.x * z.y;
       b10 += xu.y * z.x;
       b11 += xu.y * z.y;
-    });
+    };
+    if constexpr (BITS) {
+      apply_mt_bits(X, Y, bits, MB, NB, red);
+      apply_m_bits(Y, bits, MB, NB, red, ritz_acc);
+    } else {
+      apply_mt(X, Y, cp, csc_idx, cap, MB, NB, red);
+      apply_m(Y, cp, rp, col_idx, cap, MB, NB, red, ritz_acc);
+    }
     const double2 bd = block_sum2(make_double2(b00, b11), red);
     const double2 bo = block_sum2(make_double2(b01, b10), red);
     const double boff = 0.5 * (bo.x + bo.y);
@@ -401,6 +534,13 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
 
 }  // namespace
 
+size_t reorder_bits_lds_bytes(int MB, int NB) {
+  const size_t NW = (NB + 31) / 32, MW = (MB + 31) / 32;
+  return (size_t)(MB + NB) * sizeof(double2) + ((size_t)MB * NW + (size_t)NB * MW + NB) * 4;
+}
+
+bool reorder_needs_csc(int MB, int NB) { return reorder_bits_lds_bytes(MB, NB) > kBitsLdsLimit; }
+
 hipError_t launch_reorder(const int32_t* row_ptr, const int32_t* col_idx, const int32_t* csc_ptr,
                           const int32_t* csc_idx, int64_t cap64, const float* x0, int H, int MB, int NB,
                           int block, int head_dim, const wa_reorder_params& p, int32_t* perm,
@@ -408,7 +548,9 @@ hipError_t launch_reorder(const int32_t* row_ptr, const int32_t* col_idx, const 
                           hipStream_t s) {
   int n2 = 1;
   while (n2 < MB) n2 <<= 1;
-  const size_t embed_bytes = (size_t)(MB + NB) * sizeof(double2);
+  const bool use_bits = !reorder_needs_csc(MB, NB);
+  const size_t embed_bytes = use_bits ? reorder_bits_lds_bytes(MB, NB)
+                                      : (size_t)(MB + NB) * sizeof(double2);
   const size_t sort_bytes = (size_t)n2 * (sizeof(uint64_t) + sizeof(uint32_t));
   const size_t lds = embed_bytes > sort_bytes ? embed_bytes : sort_bytes;
   // The dynamic LDS limit is a per-device function attribute; set it once per device.
@@ -418,17 +560,26 @@ hipError_t launch_reorder(const int32_t* row_ptr, const int32_t* col_idx, const 
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (!attr_set[dev]) {
-    e = hipFuncSetAttribute((const void*)k_reorder, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024 - 4096);
+    e = hipFuncSetAttribute((const void*)k_reorder<false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 4096);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)k_reorder<true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 4096);
     if (e != hipSuccess) return e;
     attr_set[dev] = true;
   }
   DevParams dp{p.wave, p.n_slices, p.iters, p.stage1, p.stage2, p.skip_mode,
                p.ws_min_bytes, p.flops_min, p.jaccard_max};
   const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
-  hipLaunchKernelGGL(k_reorder, dim3(H), dim3(kThreads), lds, s, row_ptr, col_idx, csc_ptr,
-                     csc_idx, cap, x0, MB, NB, block, head_dim, dp, perm, inv_perm, skipped, angles,
-                     stats);
+  if (use_bits) {
+    hipLaunchKernelGGL(k_reorder<true>, dim3(H), dim3(kThreads), lds, s, row_ptr, col_idx, csc_ptr,
+                       csc_idx, cap, x0, MB, NB, block, head_dim, dp, perm, inv_perm, skipped,
+                       angles, stats);
+  } else {
+    hipLaunchKernelGGL(k_reorder<false>, dim3(H), dim3(kThreads), lds, s, row_ptr, col_idx,
+                       csc_ptr, csc_idx, cap, x0, MB, NB, block, head_dim, dp, perm, inv_perm,
+                       skipped, angles, stats);
+  }
   return hipGetLastError();
 }
 

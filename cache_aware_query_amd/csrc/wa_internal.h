@@ -21,6 +21,10 @@ hipError_t launch_reorder(const int32_t* row_ptr, const int32_t* col_idx, const 
                           int32_t* inv_perm, uint8_t* skipped, double* angles, double* stats,
                           hipStream_t s);
 
+// True if the reorder of an MB x NB mask cannot hold the mask as bitmasks in LDS
+// and must read the transposed lists (CSC) instead.
+bool reorder_needs_csc(int MB, int NB);
+
 size_t attn_workspace_bytes(int H, int L_pad, int head_dim);
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H,
                               int L, int head_dim, int block, const int32_t* row_ptr,

@@ -21,7 +21,7 @@ import ctypes
 import torch
 
 from . import (WA_SCHED_XCD_SLICED, BlockIndex, ReorderParams, _check, _ptr, _stream,
-               load_library, sparse_attn_workspace_size)
+               load_library, reorder_needs_csc, sparse_attn_workspace_size)
 
 
 class HotPath:
@@ -43,8 +43,11 @@ class HotPath:
         self.row_ptr = torch.empty(H * mb + 1, **i32)
         self.row_nnz = torch.empty(H * mb, **i32)
         self.col_idx = torch.empty(max(self.cap, 1), **i32)
-        self.csc_ptr = torch.empty(H * mb + 1, **i32)
-        self.csc_idx = torch.empty(max(self.cap, 1), **i32)
+        # The transposed lists are built only when the reorder cannot hold the mask
+        # as bitmasks in LDS.
+        self.with_csc = reorder is not None and reorder_needs_csc(mb, mb)
+        self.csc_ptr = torch.empty(H * mb + 1, **i32) if self.with_csc else None
+        self.csc_idx = torch.empty(max(self.cap, 1), **i32) if self.with_csc else None
         self.perm = torch.empty(H, mb, **i32)
         self.inv_perm = torch.empty(H, mb, **i32)
         self.skipped = torch.empty(H, dtype=torch.uint8, device=dev)
@@ -71,7 +74,8 @@ class HotPath:
         lib, s = self.lib, _stream(self.device)
         _check(lib.wa_build_block_index(_ptr(mask), self.H, self.mb, self.mb, _ptr(self.row_ptr),
                                         _ptr(self.col_idx), self.cap, _ptr(self.row_nnz),
-                                        _ptr(self.csc_ptr), _ptr(self.csc_idx), self.cap, s),
+                                        _ptr(self.csc_ptr), _ptr(self.csc_idx),
+                                        self.cap if self.with_csc else 0, s),
                "wa_build_block_index")
 
     def reorder_rows(self, x0: torch.Tensor) -> None:

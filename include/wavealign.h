@@ -126,7 +126,10 @@ typedef struct wa_reorder_params {
  * all identical keeps the identity Stage-1 order; the skip rule reorders only if
  * K/V bytes NB*b*d*4 > ws_min_bytes, 4*b*b*d*nnz >= flops_min and the pooled
  * Jaccard similarity of adjacent rows < jaccard_max.
- *   row_ptr, col_idx, csc_ptr, csc_idx  from wa_build_block_index (CSC required)
+ *   row_ptr, col_idx, csc_ptr, csc_idx  from wa_build_block_index.  The CSC may be
+ *             NULL when the head's mask fits in LDS as row and column bitmasks:
+ *             (MB+NB)*16 + (MB*ceil(NB/32) + NB*ceil(MB/32) + NB)*4 <= 147456 bytes
+ *             (about MB = NB <= 700); the reorder then reads only the CSR
  *   capacity  number of entries col_idx and csc_idx hold; list entries at or beyond it
  *             are ignored (a truncated index never causes an out-of-bounds read)
  *   x0        float [H][MB][2]  raw start values (the random block of Algorithm 1)
@@ -138,8 +141,9 @@ typedef struct wa_reorder_params {
  *   stats     double [H][5] out or NULL  nnz, density, K/V bytes, selected FLOP,
  *                                        adjacent-row Jaccard
  *   params    host pointer
- * Errors: WA_ERR_INVALID_ARG (null pointer, bad params), WA_ERR_UNSUPPORTED
- * (MB or NB > WA_MAX_BLOCKS, head_dim/block < 1), WA_ERR_HIP.
+ * Errors: WA_ERR_INVALID_ARG (null pointer, bad params, CSC missing where it is
+ * required), WA_ERR_UNSUPPORTED (MB or NB > WA_MAX_BLOCKS, head_dim/block < 1),
+ * WA_ERR_HIP.
  */
 int wa_reorder_rows(const int32_t* row_ptr, const int32_t* col_idx, const int32_t* csc_ptr,
                     const int32_t* csc_idx, int64_t capacity, const float* x0, int32_t H,
@@ -147,6 +151,10 @@ int wa_reorder_rows(const int32_t* row_ptr, const int32_t* col_idx, const int32_
                     int32_t block, int32_t head_dim, const wa_reorder_params* params,
                     int32_t* perm, int32_t* inv_perm, uint8_t* skipped, double* angles,
                     double* stats, void* stream);
+
+/* 1 if wa_reorder_rows needs the CSC (csc_ptr, csc_idx) for an MB x NB mask,
+ * 0 if it reads only the CSR (see wa_reorder_rows), negative on bad sizes. */
+int wa_reorder_needs_csc(int32_t MB, int32_t NB);
 
 /* Workspace bytes wa_sparse_attn_fwd needs for these sizes (host output). */
 int wa_sparse_attn_workspace_size(int32_t H, int32_t L, int32_t head_dim, int32_t block,

@@ -61,6 +61,10 @@ def test_host_validation_rejects_bad_arguments(lib):
     p = caq.ReorderParams()._c()
     assert lib.wa_reorder_rows(fake, fake, fake, fake, 16, fake, 1, 5000, 4, 128, 128,
                                ctypes.byref(p), fake, fake, fake, None, None, None) == -2
+    # the transposed lists are required once the mask no longer fits LDS as bitmasks
+    assert lib.wa_reorder_rows(fake, fake, None, None, 16, fake, 1, 760, 760, 128, 128,
+                               ctypes.byref(p), fake, fake, fake, None, None, None) == -1
+    assert b"csc" in lib.wa_last_error()
     # workspace too small
     assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 1,
                                   0.1, fake, fake, None, fake, 10, None) == -3
@@ -70,3 +74,11 @@ def test_host_validation_rejects_bad_arguments(lib):
                                   0.1, fake, fake, None, fake, 1 << 20, None) == -1
     # overlapping gather
     assert lib.wa_gather_blocks(fake, fake, fake, 1, 2, 64, None) == -1
+
+
+def test_reorder_needs_csc_threshold(lib):
+    assert lib.wa_reorder_needs_csc(591, 591) == 0
+    assert lib.wa_reorder_needs_csc(16, 16) == 0
+    assert lib.wa_reorder_needs_csc(760, 760) == 1
+    assert lib.wa_reorder_needs_csc(929, 929) == 1
+    assert lib.wa_reorder_needs_csc(0, 5) < 0

@@ -76,9 +76,23 @@ CASES = [
 @pytest.mark.parametrize("name,over,params", CASES)
 def test_reorder_matches_oracle(name, over, params):
     w = synth.make_workload(name, device="cuda" if name != "tiny" else "cpu", **over)
+    banner(f"reorder {name} {over} {params}")
+    _compare_with_oracle(w, params)
+
+
+def test_reorder_from_transposed_lists_matches_oracle():
+    """A mask too large for the LDS bitmasks takes the CSR + CSC gather form."""
+    w = synth.random_tiny_case(5, heads=2, seq_len=760 * 64, head_dim=64, block=64,
+                               density=0.05)
+    assert caq.reorder_needs_csc(760, 760)
+    banner("reorder 760 x 760 (CSC form)")
+    _compare_with_oracle(w, caq.ReorderParams(wave=64, n_slices=8,
+                                              skip_mode=caq.WA_SKIP_NEVER))
+
+
+def _compare_with_oracle(w, params):
     mask = w.mask.cpu()
     x0 = w.x0.cpu()
-    banner(f"reorder {name} {over} {params}")
     ro = _gpu_reorder(mask, x0, w.block, w.head_dim, params)
     perm_g = ro.perm.cpu().numpy()
     inv_g = ro.inv_perm.cpu().numpy()
