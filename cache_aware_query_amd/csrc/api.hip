@@ -128,7 +128,7 @@ int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int
                        const int32_t* col_idx, int64_t capacity, const int32_t* perm,
                        int32_t schedule, float scale, wa_bf16* o, float* lse, float* g,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !row_ptr || !col_idx || !o || !lse || !workspace)
+  if (!q || !k || !v || !row_ptr || !col_idx || !o || !lse)
     return fail(WA_ERR_INVALID_ARG, "null pointer argument");
   if (H < 1 || L < 1) return fail(WA_ERR_INVALID_ARG, "H and L must be >= 1");
   if (!supported_shape(head_dim, block))
@@ -143,11 +143,10 @@ int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int
   if ((int64_t)H * MB * 8 >= ((int64_t)1 << 31))
     return fail(WA_ERR_UNSUPPORTED, "too many query blocks");
   const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
-                       reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
-                       reinterpret_cast<uintptr_t>(workspace);
-  if (al % 16 != 0) return fail(WA_ERR_INVALID_ARG, "q, k, v, o and workspace must be 16-byte aligned");
+                       reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o);
+  if (al % 16 != 0) return fail(WA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
   const size_t need = wa::attn_workspace_bytes(H, (int)(MB * block), head_dim);
-  if (workspace_bytes < need)
+  if (workspace_bytes < need || (need > 0 && !workspace))
     return fail(WA_ERR_CAPACITY, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
   return hip_status(wa::launch_sparse_attn(q, k, v, H, L, head_dim, block, row_ptr, col_idx,
                                            capacity, perm,

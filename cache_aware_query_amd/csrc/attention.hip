@@ -15,7 +15,8 @@
 //    two workgroups share a compute unit (two wavefronts per SIMD).
 //  * Both products are computed transposed with v_mfma_f32_32x32x16_bf16:
 //      S^T = K Q^T   (A = K rows from LDS, B = this wave's Q rows in registers)
-//      O^T = V^T P^T (A = V^T rows from LDS, B = P taken straight from S^T)
+//      O^T = V^T P^T (A = V^T rows read transposed from LDS, B = P taken straight
+//                     from S^T)
 //    In both outputs a lane owns one query row (column of the 32x32 tile), so the
 //    row max needs one cross-lane exchange (lanes l and l^32 hold the two halves of
 //    a row, swapped with v_permlane32_swap) and the row sum none until the end.
@@ -26,12 +27,13 @@
 //  * The list is walked in 32-key quarters, software-pipelined: the S^T product of
 //    quarter q+1 is issued while the softmax of quarter q runs, and the P.V product
 //    of quarter q while the row maximum of quarter q+1 is taken.
-//  * K and V^T are copied HBM/L2 -> LDS with global_load_lds_dwordx4 (no VGPR
+//  * K and V are copied HBM/L2 -> LDS with global_load_lds_dwordx4 (no VGPR
 //    staging) in 64-key halves, double-buffered, in 16-byte chunks whose position
-//    inside a row is XOR-swizzled so that the 16 lanes of an LDS read phase hit
-//    distinct banks.  V is transposed once per call by a separate pass into the
-//    workspace.  The query block's K/V list is staged in LDS so that block ids
-//    never wait on scalar memory inside the loop.
+//    inside a row is XOR-swizzled so that the lanes of an LDS read phase hit
+//    distinct banks.  V keeps its key-row layout: the V^T operand of the P.V
+//    product is gathered with ds_read_b64_tr_b16 transposing reads, so no
+//    transposed copy of V is ever written.  The query block's K/V list is staged
+//    in LDS so that block ids never wait on scalar memory inside the loop.
 //  * Workgroup -> query block: natural head-major order, or XCD-sliced: workgroup
 //    w runs on XCD w % 8 (round-robin dispatch), and XCD x takes the x-th
 //    contiguous slice of each head's execution order, so each XCD's L2 sees one
@@ -58,9 +60,21 @@ template <int CHUNKS>
 __device__ inline int swz_k(int r) {
   return ((r & 3) | ((r >> 1) & 4) | ((r << 1) & 8)) & (CHUNKS - 1);
 }
+// V rows (keys) are read with transposing LDS reads that take four consecutive
+// rows per 16-lane group; the swizzle spreads those four rows over distinct banks.
 template <int CHUNKS>
 __device__ inline int swz_v(int r) {
-  return (r >> 1) & (CHUNKS - 1);
+  return CHUNKS == 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane s names 4 consecutive 16-bit
+// elements (a row segment); lane j receives element j % 4 of lanes j / 4, j / 4 + 4,
+// j / 4 + 8 and j / 4 + 12, i.e. one column of the 4 x 16 block the group names.
+__device__ inline i16x4 lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(__attribute__((address_space(3))) const char*)p);
 }
 
 // Key row of a 32-key tile that feeds A-operand row i of S^T, chosen so that
@@ -156,7 +170,7 @@ struct QuarterDecision {
 template <int BLOCK, int D, bool WITH_G>
 __global__ __launch_bounds__(BLOCK * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                   const uint16_t* __restrict__ Vt, int H, int L, int MB,
+                   const uint16_t* __restrict__ V, int H, int L, int MB,
                    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                    int cap, const int32_t* __restrict__ perm, int schedule, float scale_log2,
                    uint16_t* __restrict__ O, float* __restrict__ lse, float* __restrict__ G) {
@@ -229,12 +243,10 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int r = flat / (D * 2);
     const int ks = (flat % (D * 2)) / 16;
     koff[j] = (uint32_t)(r * D * 2 + ((ks ^ swz_k<T::kKChunks>(r)) * 16));
-    const int d = flat / 128;  // a V^T half row is 64 keys = 128 bytes
-    const int vs = (flat % 128) / 16;
-    voff[j] = (uint32_t)((size_t)d * Lp * 2 + ((vs ^ swz_v<8>(d)) * 16));
+    voff[j] = (uint32_t)(r * D * 2 + ((ks ^ swz_v<T::kKChunks>(r)) * 16));
   }
   const char* kbytes = reinterpret_cast<const char*>(K + head_off);
-  const char* vbytes = reinterpret_cast<const char*>(Vt + head_off);
+  const char* vbytes = reinterpret_cast<const char*>(V + head_off);
   const uint32_t lk[2] = {lds_address(sk0), lds_address(sk1)};
   const uint32_t lv[2] = {lds_address(sv0), lds_address(sv1)};
 
@@ -256,10 +268,11 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             lk[buf] + (uint32_t)((wave + j * T::kWaves) * 1024));
   };
   auto issue_v = [&](int v, int hh, int buf) {
-    const char* base = vbytes + ((size_t)copy_block(v) * BLOCK + 64 * (hh % T::kHalves)) * 2;
+    const char* base =
+        vbytes + ((size_t)copy_block(v) * BLOCK + 64 * (hh % T::kHalves)) * D * 2;
 #pragma unroll
     for (int j = 0; j < T::kSubInst; ++j)
-      dma16(kAffine ? base + (size_t)j * T::kWaves * 8 * Lp * 2 : base, voff[kAffine ? 0 : j],
+      dma16(kAffine ? base + (size_t)j * T::kWaves * 1024 : base, voff[kAffine ? 0 : j],
             lv[buf] + (uint32_t)((wave + j * T::kWaves) * 1024));
   };
 
@@ -380,17 +393,28 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     m_run = d.m_ref;
   };
 
-  // O^T += V^T P^T over one quarter (key tile mt of the half in a V^T buffer).
+  // O^T += V^T P^T over one quarter (key tile mt of the half in a V buffer).  The V
+  // buffer holds key rows; the A operand (8 consecutive keys of one d row per lane)
+  // is gathered by two transposing LDS reads of four keys each.
+  const int tr_s = lane & 15, tr_grp = lane >> 4;
+  const int tr_key = tr_s >> 2;  // key of the row segment this lane names (mod 4)
+  int tr_off[T::kDT];
+#pragma unroll
+  for (int dt = 0; dt < T::kDT; ++dt) {
+    const int chunk = dt * 4 + 2 * (tr_grp & 1) + ((tr_s & 3) >> 1);
+    tr_off[dt] = (8 * g + tr_key) * (D * 2) + ((chunk ^ swz_v<T::kKChunks>(tr_key)) * 16) +
+                 8 * (tr_s & 1);
+  }
   auto pv = [&](const bf16x8(&pb)[2], const char* sv, int mt) {
 #pragma unroll
     for (int p2 = 0; p2 < 2; ++p2) {
-      const int c = 2 * (2 * mt + p2) + g;
+      const int ps = 2 * mt + p2;
 #pragma unroll
       for (int dt = 0; dt < T::kDT; ++dt) {
-        const int drow = dt * 32 + i32;
-        const char* base = sv + drow * 128;
-        const bf16x8 a =
-            as_bf16x8(*reinterpret_cast<const uint4*>(base + 16 * (c ^ swz_v<8>(drow))));
+        const char* base = sv + tr_off[dt] + 16 * ps * (D * 2);
+        const i16x4 lo = lds_read_tr16(base);
+        const i16x4 hi = lds_read_tr16(base + 4 * (D * 2));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[p2], acc_o[dt], 0, 0, 0);
       }
     }
@@ -499,54 +523,21 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   if (g == 0) lse[(size_t)h * Lp + qrow] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
-// V [H][Lp][D] -> V^T [H][D][Lp], 64 x 64 tiles through LDS.
-template <int D>
-__global__ __launch_bounds__(256) void k_transpose_v(const uint16_t* __restrict__ V,
-                                                     uint16_t* __restrict__ Vt, int Lp) {
-  __shared__ uint16_t tile[64][64 + 2];
-  const int tiles_t = Lp / 64;
-  const int h = blockIdx.x / (tiles_t * (D / 64));
-  const int rem = blockIdx.x % (tiles_t * (D / 64));
-  const int t0 = (rem / (D / 64)) * 64;
-  const int d0 = (rem % (D / 64)) * 64;
-  const uint16_t* src = V + (size_t)h * Lp * D;
-  uint16_t* dst = Vt + (size_t)h * D * Lp;
-  for (int c = threadIdx.x; c < 64 * 8; c += 256) {
-    const int tt = c >> 3, dc = (c & 7) * 8;
-    const uint4 val = *reinterpret_cast<const uint4*>(src + (size_t)(t0 + tt) * D + d0 + dc);
-    const uint16_t* pv = reinterpret_cast<const uint16_t*>(&val);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tile[tt][dc + j] = pv[j];
-  }
-  __syncthreads();
-  for (int c = threadIdx.x; c < 64 * 8; c += 256) {
-    const int dd = c >> 3, tc = (c & 7) * 8;
-    uint16_t w[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) w[j] = tile[tc + j][dd];
-    *reinterpret_cast<uint4*>(dst + (size_t)(d0 + dd) * Lp + t0 + tc) =
-        *reinterpret_cast<const uint4*>(w);
-  }
-}
-
 template <int BLOCK, int D>
 hipError_t launch_typed(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H, int L,
                         const int32_t* row_ptr, const int32_t* col_idx, int cap,
-                        const int32_t* perm,
-                        int schedule, float scale, uint16_t* o, float* lse, float* g,
-                        uint16_t* vt, hipStream_t s) {
+                        const int32_t* perm, int schedule, float scale, uint16_t* o, float* lse,
+                        float* g, hipStream_t s) {
   const int MB = (L + BLOCK - 1) / BLOCK;
-  const int Lp = MB * BLOCK;
-  hipLaunchKernelGGL(k_transpose_v<D>, dim3(H * (Lp / 64) * (D / 64)), dim3(256), 0, s, v, vt, Lp);
   int grid = H * MB;
   if (schedule == WA_SCHED_XCD_SLICED) grid = H * kXcds * ((MB + kXcds - 1) / kXcds);
   const float sl2 = scale * kLog2e;
   if (g != nullptr) {
     hipLaunchKernelGGL((k_sparse_attn<BLOCK, D, true>), dim3(grid), dim3(BLOCK * 2), 0, s, q, k,
-                       vt, H, L, MB, row_ptr, col_idx, cap, perm, schedule, sl2, o, lse, g);
+                       v, H, L, MB, row_ptr, col_idx, cap, perm, schedule, sl2, o, lse, g);
   } else {
     hipLaunchKernelGGL((k_sparse_attn<BLOCK, D, false>), dim3(grid), dim3(BLOCK * 2), 0, s, q, k,
-                       vt, H, L, MB, row_ptr, col_idx, cap, perm, schedule, sl2, o, lse, g);
+                       v, H, L, MB, row_ptr, col_idx, cap, perm, schedule, sl2, o, lse, g);
   }
   return hipGetLastError();
 }
@@ -554,13 +545,16 @@ hipError_t launch_typed(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 }  // namespace
 
 size_t attn_workspace_bytes(int H, int L_pad, int head_dim) {
-  return (size_t)H * (size_t)L_pad * (size_t)head_dim * sizeof(uint16_t);
+  (void)H;
+  (void)L_pad;
+  (void)head_dim;
+  return 0;  // V is read in its own layout; no staging buffer
 }
 
 int attn_resident_wgs_per_cu(int head_dim, int block) {
   (void)head_dim;
   (void)block;
-  return 2;  // 64 KiB of LDS per workgroup, two waves per SIMD
+  return 2;  // 64 KiB of K/V buffers per workgroup, two waves per SIMD
 }
 
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H,
@@ -568,19 +562,19 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
                               const int32_t* col_idx, int64_t cap64, const int32_t* perm,
                               int schedule, float scale, uint16_t* o, float* lse, float* g,
                               void* workspace, hipStream_t s) {
-  uint16_t* vt = static_cast<uint16_t*>(workspace);
+  (void)workspace;
   const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
   if (block == 128 && head_dim == 128)
-    return launch_typed<128, 128>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o, lse,
-                                  g, vt, s);
+    return launch_typed<128, 128>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o,
+                                  lse, g, s);
   if (block == 128 && head_dim == 64)
-    return launch_typed<128, 64>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o, lse,
-                                 g, vt, s);
+    return launch_typed<128, 64>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o,
+                                 lse, g, s);
   if (block == 64 && head_dim == 128)
-    return launch_typed<64, 128>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o, lse,
-                                 g, vt, s);
-  return launch_typed<64, 64>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o, lse, g,
-                              vt, s);
+    return launch_typed<64, 128>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o,
+                                 lse, g, s);
+  return launch_typed<64, 64>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o, lse,
+                              g, s);
 }
 
 }  // namespace wa

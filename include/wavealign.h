@@ -156,7 +156,8 @@ int wa_reorder_rows(const int32_t* row_ptr, const int32_t* col_idx, const int32_
  * 0 if it reads only the CSR (see wa_reorder_rows), negative on bad sizes. */
 int wa_reorder_needs_csc(int32_t MB, int32_t NB);
 
-/* Workspace bytes wa_sparse_attn_fwd needs for these sizes (host output). */
+/* Workspace bytes wa_sparse_attn_fwd needs for these sizes (host output).  The
+ * current kernels read K and V in place and need none (0 bytes). */
 int wa_sparse_attn_workspace_size(int32_t H, int32_t L, int32_t head_dim, int32_t block,
                                   size_t* bytes);
 
@@ -180,7 +181,8 @@ int wa_sparse_attn_workspace_size(int32_t H, int32_t L, int32_t head_dim, int32_
  *   g         float [row_ptr[H*MB]][block] out or NULL  [GSRS §5.3 Phase 1] for CSR
  *             entry e = (u, v) and row r of u, the block log-sum-exp
  *             G = m + ln sum_{j in v, j < L} exp(z_rj - m), m the block maximum
- *   workspace device buffer of at least wa_sparse_attn_workspace_size bytes
+ *   workspace device buffer of at least wa_sparse_attn_workspace_size bytes (may be
+ *             NULL when that size is 0)
  * Errors: WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED (head_dim/block), WA_ERR_CAPACITY
  * (workspace too small), WA_ERR_HIP.
  */

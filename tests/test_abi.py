@@ -49,7 +49,7 @@ def test_host_validation_rejects_bad_arguments(lib):
     n = ctypes.c_size_t()
     assert lib.wa_sparse_attn_workspace_size(2, 1000, 96, 128, ctypes.byref(n)) == -2
     assert lib.wa_sparse_attn_workspace_size(2, 1000, 128, 128, ctypes.byref(n)) == 0
-    assert n.value == 2 * 1024 * 128 * 2
+    assert n.value == 0  # K and V are read in place
     assert lib.wa_last_error() == b""
     fake = ctypes.c_void_p(16)
     assert lib.wa_topp_select(fake, fake, fake, 4, 1, 1, 1, 1.5, fake, None) == -1
@@ -65,13 +65,17 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert lib.wa_reorder_rows(fake, fake, None, None, 16, fake, 1, 760, 760, 128, 128,
                                ctypes.byref(p), fake, fake, fake, None, None, None) == -1
     assert b"csc" in lib.wa_last_error()
-    # workspace too small
+    # negative capacity, bad schedule and non-positive scale are refused on the host
+    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, -1, None, 1,
+                                  0.1, fake, fake, None, None, 0, None) == -1
+    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 7,
+                                  0.1, fake, fake, None, None, 0, None) == -1
     assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 1,
-                                  0.1, fake, fake, None, fake, 10, None) == -3
+                                  -0.1, fake, fake, None, None, 0, None) == -1
     # unaligned pointer
     odd = ctypes.c_void_p(18)
     assert lib.wa_sparse_attn_fwd(odd, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 1,
-                                  0.1, fake, fake, None, fake, 1 << 20, None) == -1
+                                  0.1, fake, fake, None, None, 0, None) == -1
     # overlapping gather
     assert lib.wa_gather_blocks(fake, fake, fake, 1, 2, 64, None) == -1
 
