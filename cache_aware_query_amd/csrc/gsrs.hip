@@ -12,63 +12,80 @@
 namespace wa {
 namespace {
 
-// One workgroup (4 wavefronts) per query-block row; each wavefront takes CSR
-// entries in turn, each lane two rows of the block, and reduces with a fixed
-// shuffle tree, so W is bitwise reproducible.
+// One workgroup per query-block row u.  Eight consecutive threads share one CSR
+// entry and each sums a fixed slice of BLOCK/8 rows of it, so a wavefront reads
+// eight whole G rows (8 x BLOCK floats, contiguous in memory) with 16-byte loads;
+// the eight partial sums are combined by a fixed shuffle tree, so W is bitwise
+// reproducible.  exp(G - L) is evaluated as exp2((G - L) log2 e).
 template <int BLOCK>
 __global__ __launch_bounds__(256) void k_block_importance(const float* __restrict__ G,
                                                           const float* __restrict__ lse,
                                                           const int32_t* __restrict__ row_ptr,
                                                           int cap, int MB, int L,
                                                           float* __restrict__ W) {
-  constexpr int kPer = BLOCK / 64;
+  constexpr int kParts = 8;                // threads per CSR entry
+  constexpr int kRows = BLOCK / kParts;    // rows per thread
+  constexpr int kPerPass = 256 / kParts;   // entries per pass of the workgroup
+  constexpr float kLog2e = 1.4426950408889634f;
   const int row = blockIdx.x;  // h * MB + u
   const int h = row / MB, u = row % MB;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int part = threadIdx.x % kParts, slot = threadIdx.x / kParts;
   const int e0 = min(row_ptr[row], cap), e1 = min(row_ptr[row + 1], cap);
   const int nvalid = min(BLOCK, L - u * BLOCK);
   const size_t lp = (size_t)MB * BLOCK;
-  float l[kPer];
-  bool live[kPer];
+  float lsc[kRows];
+  bool live[kRows];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int r = lane + 64 * j;
+  for (int k = 0; k < kRows; ++k) {
+    const int r = part * kRows + k;
     const float x = r < nvalid ? lse[(size_t)h * lp + (size_t)u * BLOCK + r] : -INFINITY;
-    live[j] = r < nvalid && x != -INFINITY;
-    l[j] = x;
+    live[k] = r < nvalid && x != -INFINITY;
+    lsc[k] = live[k] ? x * kLog2e : 0.0f;
   }
   const float inv_b = 1.0f / (float)nvalid;
-  for (int e = e0 + wave; e < e1; e += 4) {
+  for (int e = e0 + slot; e < e1; e += kPerPass) {
+    const float4* gp = reinterpret_cast<const float4*>(G + (size_t)e * BLOCK + part * kRows);
     float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int r = lane + 64 * j;
-      if (live[j]) s += expf(G[(size_t)e * BLOCK + r] - l[j]);
-    }
+    for (int k4 = 0; k4 < kRows / 4; ++k4) {
+      const float4 v = gp[k4];
+      const float gv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) W[e] = s * inv_b;
+      for (int j = 0; j < 4; ++j) {
+        const int k = 4 * k4 + j;
+        if (live[k]) s += __builtin_amdgcn_exp2f(fmaf(gv[j], kLog2e, -lsc[k]));
+      }
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if (part == 0) W[e] = s * inv_b;
   }
 }
 
-// One workgroup per query-block row: sort the candidates by (W descending, block
-// id ascending) with a bitonic sort of 64-bit keys in LDS, then accumulate in fp64
-// in that order on one lane (the order of the additions fixes the rounding of the
-// running total, and the kept set depends on it).
-__global__ __launch_bounds__(256) void k_topp(const float* __restrict__ W,
-                                              const int32_t* __restrict__ row_ptr,
-                                              const int32_t* __restrict__ col_idx, int cap,
-                                              int NB, double p, uint8_t* __restrict__ mask_out) {
-  __shared__ uint64_t key[WA_MAX_BLOCKS];
+// One wavefront per query-block row: sort the candidates by (W descending, block
+// id ascending) with a bitonic sort of 64-bit keys in LDS (n2 = the candidate count
+// rounded up to a power of two), then walk them in that order with a wave-uniform
+// fp64 running total (the order of the additions fixes the rounding of the total,
+// and the kept set depends on it) and keep blocks while the total before them is
+// at most p.
+__global__ __launch_bounds__(64) void k_topp(const float* __restrict__ W,
+                                             const int32_t* __restrict__ row_ptr,
+                                             const int32_t* __restrict__ col_idx, int cap,
+                                             int NB, double p, uint8_t* __restrict__ mask_out) {
+  extern __shared__ uint64_t key[];
   const int row = blockIdx.x;
+  const int lane = threadIdx.x;
   const int e0 = min(row_ptr[row], cap), e1 = min(row_ptr[row + 1], cap);
-  const int n = min(e1 - e0, WA_MAX_BLOCKS);
+  int n2max = 1;  // LDS keys allocated by the launcher
+  while (n2max < NB) n2max <<= 1;
+  const int n = max(0, min(e1 - e0, n2max));  // a well-formed row has at most NB entries
   uint8_t* out = mask_out + (size_t)row * NB;
-  for (int v = threadIdx.x; v < NB; v += 256) out[v] = 0;
+  for (int v = lane; v < NB; v += 64) out[v] = 0;
   if (n <= 0) return;
   int n2 = 1;
   while (n2 < n) n2 <<= 1;
-  for (int i = threadIdx.x; i < n2; i += 256) {
+  for (int i = lane; i < n2; i += 64) {
     if (i < n) {
       float w = W[e0 + i];
       if (!(w >= 0.0f)) w = 0.0f;  // NaN or negative weights rank last
@@ -81,7 +98,7 @@ __global__ __launch_bounds__(256) void k_topp(const float* __restrict__ W,
   for (int size = 2; size <= n2; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       __syncthreads();
-      for (int i = threadIdx.x; i < (n2 >> 1); i += 256) {
+      for (int i = lane; i < (n2 >> 1); i += 64) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
         const bool up = (lo & size) == 0;
@@ -94,15 +111,17 @@ __global__ __launch_bounds__(256) void k_topp(const float* __restrict__ W,
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double acc = 0.0;
-    for (int i = 0; i < n; ++i) {
+  double acc = 0.0;
+  for (int c = 0; c < n && !(acc > p); c += 64) {
+    const uint64_t mine = c + lane < n ? key[c + lane] : ~0ull;
+    const uint32_t klo = (uint32_t)mine, khi = (uint32_t)(mine >> 32);
+    const int m = min(64, n - c);
+    for (int j = 0; j < m; ++j) {
       if (acc > p) break;
-      const uint64_t k = key[i];
-      const int v = (int)(uint32_t)(k & 0xFFFFFFFFu);
-      const float w = __uint_as_float(0x7FFFFFFFu - (uint32_t)(k >> 32));
-      if (v >= 0 && v < NB) out[v] = 1;
-      acc += (double)w;
+      const uint32_t wv = 0x7FFFFFFFu - __builtin_amdgcn_readlane(khi, j);
+      const int v = (int)__builtin_amdgcn_readlane(klo, j);
+      if (lane == 0 && v >= 0 && v < NB) out[v] = 1;
+      acc += (double)__uint_as_float(wv);
     }
   }
 }
@@ -126,8 +145,10 @@ hipError_t launch_topp(const float* w, const int32_t* row_ptr, const int32_t* co
                        int64_t cap64, int H, int MB, int NB, double p, uint8_t* mask_out,
                        hipStream_t s) {
   const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
-  hipLaunchKernelGGL(k_topp, dim3(H * MB), dim3(256), 0, s, w, row_ptr, col_idx, cap, NB, p,
-                     mask_out);
+  int n2 = 1;
+  while (n2 < NB) n2 <<= 1;  // a row has at most NB candidates
+  hipLaunchKernelGGL(k_topp, dim3(H * MB), dim3(64), (size_t)n2 * sizeof(uint64_t), s, w,
+                     row_ptr, col_idx, cap, NB, p, mask_out);
   return hipGetLastError();
 }
 
