@@ -61,6 +61,20 @@ class ReorderParams:
     flops_min: float = 0.0
     jaccard_max: float = 1.0
 
+    @classmethod
+    def calibrated(cls, path: str | None = None, **over) -> "ReorderParams":
+        """Adaptive skip with the thresholds that ``python -m cache_aware_query_amd.calibrate``
+        measured on this GPU model (raises FileNotFoundError if no calibration exists)."""
+        import json
+
+        with open(path or os.path.join(_HERE, "calib_mi355x.json")) as f:
+            c = json.load(f)
+        kw = dict(skip_mode=WA_SKIP_ADAPTIVE, iters=int(c["iters"]),
+                  ws_min_bytes=float(c["ws_min_bytes"]), flops_min=float(c["flops_min"]),
+                  jaccard_max=float(c["jaccard_max"]))
+        kw.update(over)
+        return cls(**kw)
+
     def _c(self) -> _ReorderParams:
         return _ReorderParams(int(self.wave), int(self.n_slices), int(self.iters),
                               int(bool(self.stage1)), int(bool(self.stage2)), int(self.skip_mode),

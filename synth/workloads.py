@@ -27,6 +27,10 @@ Five workloads are defined (``CONFIGS``):
 ``gsrs75k``      The ``wan75k`` tensors with an all-ones mask (the first, dense
                  search pass of the GSRS pipeline).
 
+Any field can be overridden (``make_workload("wan75k", grid=(9, 45, 80),
+heads=16, density=0.1)``): ``density`` fixes the Top-k budget of every head,
+which the skip-calibration sweep uses.
+
 Smooth field: per head, 8 sinusoids sin(2*pi*f.p + phase) over normalised grid
 coordinates p = (t/(T-1), y/(Y-1), x/(X-1)), f ~ U(-3, 3)^3, phase ~ U[0, 2*pi),
 shared by Q, K and V of that head; each tensor projects the 8 channels to d
@@ -62,6 +66,7 @@ class WorkloadConfig:
     qkv: str     # "gaussian" | "smooth"
     mask: str    # "bernoulli" | "neighbour" | "topk" | "topp" | "dense"
     hilbert: bool = False
+    density: float | None = None  # "topk": a fixed k = round(density * NB) for every head
 
     @property
     def seq_len(self) -> int:
@@ -239,6 +244,8 @@ def _mask_topk(cfg: WorkloadConfig, q, k, device, seed: int) -> torch.Tensor:
     for h in range(H):
         g = _gen(device, cfg.index, "topk", h, seed)
         kk = int(torch.randint(lo, hi + 1, (1,), generator=g, device=device).item())
+        if cfg.density is not None:
+            kk = max(1, min(nb, round(cfg.density * nb)))
         idx = _order_desc(scores[h])[:, :kk]
         m[h].scatter_(1, idx, 1)
         m[h, ar, ar] = 1
