@@ -33,16 +33,36 @@ __global__ __launch_bounds__(256) void k_row_counts(const uint8_t* __restrict__ 
   if (lane == 0) row_nnz[r] = cnt;
 }
 
-// One thread per (head, column): csc count of column v, written to cnt[h*NB + v].
-__global__ __launch_bounds__(256) void k_col_counts(const uint8_t* __restrict__ mask, int H,
-                                                    int MB, int NB, int32_t* __restrict__ cnt) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= H * NB) return;
-  const int h = t / NB, v = t % NB;
+// One workgroup of 16 wavefronts per (head, 64-column tile): lane l of every
+// wavefront counts column v0 + l over the rows u = wave, wave + 16, ... (each row
+// read is 64 contiguous bytes), and the 16 partial counts are added in LDS.
+__global__ __launch_bounds__(1024) void k_col_counts(const uint8_t* __restrict__ mask, int H,
+                                                     int MB, int NB, int32_t* __restrict__ cnt) {
+  __shared__ int32_t part[16][64];
+  const int tiles_per_head = (NB + 63) / 64;
+  const int h = blockIdx.x / tiles_per_head;
+  const int v0 = (blockIdx.x % tiles_per_head) * 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int v = v0 + lane;
   const uint8_t* m = mask + (size_t)h * MB * NB + v;
   int c = 0;
-  for (int u = 0; u < MB; ++u) c += m[(size_t)u * NB] != 0;
-  cnt[t] = c;
+  if (v < NB) {
+    int u = wave;
+    for (; u + 48 < MB; u += 64) {
+      const uint8_t a = m[(size_t)u * NB], b = m[(size_t)(u + 16) * NB];
+      const uint8_t d = m[(size_t)(u + 32) * NB], e = m[(size_t)(u + 48) * NB];
+      c += (a != 0) + (b != 0) + (d != 0) + (e != 0);
+    }
+    for (; u < MB; u += 16) c += m[(size_t)u * NB] != 0;
+  }
+  part[wave][lane] = c;
+  __syncthreads();
+  if (wave == 0 && v < NB) {
+    int s = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) s += part[w][lane];
+    cnt[h * NB + v] = s;
+  }
 }
 
 // Exclusive prefix sum of n counts into ptr[0..n] (ptr may alias cnt).  One
@@ -122,38 +142,49 @@ __global__ __launch_bounds__(256) void k_fill_rows(const uint8_t* __restrict__ m
   }
 }
 
-// One workgroup per (head, 64-column tile): ascending row ids per column.  The
-// tile of 64 rows x 64 columns is staged in LDS so that global reads stay
-// row-contiguous; each wavefront then owns 16 columns and walks them with ballots
-// over the 64 rows of the tile.
-__global__ __launch_bounds__(256) void k_fill_cols(const uint8_t* __restrict__ mask, int H, int MB,
-                                                   int NB, const int32_t* __restrict__ csc_ptr,
-                                                   int32_t* __restrict__ csc_idx, int64_t cap) {
-  __shared__ uint8_t tile[64][65];
+// One workgroup of 16 wavefronts per (head, 64-column tile): ascending row ids
+// per column.  The mask is walked in tiles of 64 rows x 64 columns, staged in LDS
+// so that global reads stay row-contiguous; the next tile is loaded into
+// registers while the current one is scanned, and the two LDS buffers alternate
+// so that one barrier per tile suffices.  Each wavefront owns 4 columns and walks
+// them with ballots over the 64 rows of the tile.
+__global__ __launch_bounds__(1024) void k_fill_cols(const uint8_t* __restrict__ mask, int H, int MB,
+                                                    int NB, const int32_t* __restrict__ csc_ptr,
+                                                    int32_t* __restrict__ csc_idx, int64_t cap) {
+  __shared__ uint8_t tile[2][64][65];
   const int tiles_per_head = (NB + 63) / 64;
   const int h = blockIdx.x / tiles_per_head;
   const int v0 = (blockIdx.x % tiles_per_head) * 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint64_t lt = lanemask_lt();
-  int64_t base[16];
+  int64_t base[4];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int v = v0 + wave + 4 * j;
+  for (int j = 0; j < 4; ++j) {
+    const int v = v0 + wave + 16 * j;
     base[j] = v < NB ? csc_ptr[h * NB + v] : 0;
   }
   const uint8_t* mh = mask + (size_t)h * MB * NB;
-  for (int u0 = 0; u0 < MB; u0 += 64) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-      const int uu = e >> 6, vv = e & 63;
-      const int u = u0 + uu, v = v0 + vv;
-      tile[uu][vv] = (u < MB && v < NB) ? (mh[(size_t)u * NB + v] != 0) : 0;
+  // Thread (wave, lane) stages rows wave + 16 k (k < 4) of column v0 + lane.
+  const int sv = v0 + lane;
+  uint8_t r[4];
+  auto load = [&](int u0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int u = u0 + wave + 16 * k;
+      r[k] = (u < MB && sv < NB) ? (mh[(size_t)u * NB + sv] != 0) : 0;
     }
+  };
+  load(0);
+  int buf = 0;
+  for (int u0 = 0; u0 < MB; u0 += 64) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tile[buf][wave + 16 * k][lane] = r[k];
+    if (u0 + 64 < MB) load(u0 + 64);
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int vv = wave + 4 * j;
-      const bool bit = tile[lane][vv] != 0;
+    for (int j = 0; j < 4; ++j) {
+      const int vv = wave + 16 * j;
+      const bool bit = tile[buf][lane][vv] != 0;
       const uint64_t b = __ballot(bit);
       if (bit) {
         const int64_t idx = base[j] + __popcll(b & lt);
@@ -161,6 +192,7 @@ __global__ __launch_bounds__(256) void k_fill_cols(const uint8_t* __restrict__ m
       }
       base[j] += __popcll(b);
     }
+    buf ^= 1;
   }
 }
 
@@ -177,10 +209,10 @@ hipError_t launch_block_index(const uint8_t* mask, int H, int MB, int NB, int32_
                      col_idx, col_cap);
   if (csc_ptr != nullptr) {
     const int cols = H * NB;
-    hipLaunchKernelGGL(k_col_counts, dim3((cols + 255) / 256), dim3(256), 0, s, mask, H, MB, NB,
+    hipLaunchKernelGGL(k_col_counts, dim3(H * ((NB + 63) / 64)), dim3(1024), 0, s, mask, H, MB, NB,
                        csc_ptr);
     hipLaunchKernelGGL(k_exclusive_scan, dim3(1), dim3(1024), 0, s, csc_ptr, csc_ptr, cols);
-    hipLaunchKernelGGL(k_fill_cols, dim3(H * ((NB + 63) / 64)), dim3(256), 0, s, mask, H, MB, NB,
+    hipLaunchKernelGGL(k_fill_cols, dim3(H * ((NB + 63) / 64)), dim3(1024), 0, s, mask, H, MB, NB,
                        csc_ptr, csc_idx, csc_cap);
   }
   return hipGetLastError();

@@ -13,9 +13,11 @@
 //
 // Arithmetic is fp64 (MI355X runs fp64 vector code at half the fp32 rate; the
 // whole stage is a few MFLOP per head), so the angles agree with an fp64 reference
-// to rounding.  All reductions use a fixed shuffle tree, so results are bitwise
-// reproducible run to run.  The Stage-1 and Stage-2 orders are one bitonic sort
-// each of unique 64-bit keys in LDS.
+// to rounding.  All reductions use a fixed tree (DPP and lane-swap steps inside a
+// wavefront, then the wavefront sums in index order), so results are bitwise
+// reproducible run to run.  The Stage-1 and Stage-2 orders are one sort each of
+// distinct (key, index) pairs in LDS: wavefront rank sorts of 64, then pairwise
+// merges by binary search.
 #include <math.h>
 
 #include "wa_internal.h"
@@ -35,32 +37,88 @@ struct DevParams {
   double ws_min, flops_min, jac_max;
 };
 
-// Block-wide sum of one or two doubles; every thread returns the same value.
-// `red` holds 2 * kWaves doubles.
-__device__ inline double2 block_sum2(double2 v, double* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    v.x += __shfl_xor(v.x, off);
-    v.y += __shfl_xor(v.y, off);
-  }
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) {
-    red[2 * w] = v.x;
-    red[2 * w + 1] = v.y;
-  }
-  __syncthreads();
-  double2 s = make_double2(0.0, 0.0);
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    s.x += red[2 * i];
-    s.y += red[2 * i + 1];
-  }
-  return s;
+// One 32-bit lane move across the wavefront by a DPP pattern (all source lanes
+// exist for the patterns used here).
+template <int CTRL>
+__device__ inline double dpp_move(double x) {
+  const long long b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
-__device__ inline double block_sum(double v, double* red) {
-  return block_sum2(make_double2(v, 0.0), red).x;
+// x of this lane plus x of the lane 16 (or 32) rows away, with the two operands in
+// the same order on both lanes of the pair.
+__device__ inline double pair16_sum(double x) {
+  const long long b = __double_as_longlong(x);
+  const auto lo = __builtin_amdgcn_permlane16_swap((unsigned)b, (unsigned)b, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap((unsigned)(b >> 32), (unsigned)(b >> 32), false,
+                                                   false);
+  return __longlong_as_double(((long long)hi[0] << 32) | lo[0]) +
+         __longlong_as_double(((long long)hi[1] << 32) | lo[1]);
+}
+__device__ inline double pair32_sum(double x) {
+  const long long b = __double_as_longlong(x);
+  const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)b, (unsigned)b, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((unsigned)(b >> 32), (unsigned)(b >> 32), false,
+                                                   false);
+  return __longlong_as_double(((long long)hi[0] << 32) | lo[0]) +
+         __longlong_as_double(((long long)hi[1] << 32) | lo[1]);
+}
+
+// Wavefront sum, bitwise equal on every lane: each step adds a lane to its partner
+// under a pairing that is its own inverse (xor 1, xor 2 inside quads, mirror inside
+// rows and half rows, then across rows), and a + b == b + a exactly, so both
+// partners always hold the same value.
+__device__ inline double wave_sum(double x) {
+  x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_move<0x140>(x);  // row_mirror
+  x += dpp_move<0x141>(x);  // row_half_mirror
+  x = pair16_sum(x);
+  return pair32_sum(x);
+}
+
+// Block-wide sums through two alternating LDS slots: a slot is written again only
+// two reductions later, after every thread has passed the barrier of the reduction
+// in between, so one barrier per reduction suffices.  All threads call every
+// reduction in the same order.
+struct Reducer {
+  double* buf;  // 2 slots of 4 * kWaves doubles
+  int phase;
+};
+
+template <int N>
+__device__ inline void block_sum_n(double (&v)[N], Reducer& r) {
+  static_assert(N <= 4, "at most four sums per reduction");
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  double* slot = r.buf + r.phase * 4 * kWaves;
+  r.phase ^= 1;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = wave_sum(v[i]);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) slot[N * w + i] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = 0.0;
+#pragma unroll
+  for (int j = 0; j < kWaves; ++j)
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += slot[N * j + i];
+}
+
+__device__ inline double2 block_sum2(double2 v, Reducer& r) {
+  double a[2] = {v.x, v.y};
+  block_sum_n(a, r);
+  return make_double2(a[0], a[1]);
+}
+
+__device__ inline double block_sum(double v, Reducer& r) {
+  double a[1] = {v};
+  block_sum_n(a, r);
+  return a[0];
 }
 
 __device__ inline long long block_sum_i64(long long v, long long* red) {
@@ -89,30 +147,32 @@ __device__ inline int block_min_i32(int v, int* red) {
   return s;
 }
 
-// Q factor of the MB x 2 block in x (in place): modified Gram-Schmidt with a
-// positive diagonal; a second column whose orthogonalised norm is <= 1e-12 of the
-// first column's norm becomes zero; a zero first column zeroes both.
-__device__ void qr2_inplace(double2* x, int MB, double* red) {
+// Q factor of the MB x 2 block in x (in place): Gram-Schmidt with a positive
+// diagonal; a second column whose orthogonalised norm is <= 1e-12 of the first
+// column's norm becomes zero; a zero first column zeroes both.  The projection
+// coefficient is taken as (x1 . x2) / |x1| from the same reduction as |x1|; the
+// orthogonalised column's norm is summed from the new column itself.
+__device__ void qr2_inplace(double2* x, int MB, Reducer& red) {
   const int t = threadIdx.x;
-  double s1 = 0.0;
-  for (int u = t; u < MB; u += kThreads) s1 += x[u].x * x[u].x;
-  const double n1 = sqrt(block_sum(s1, red));
+  double g[2] = {0.0, 0.0};
+  for (int u = t; u < MB; u += kThreads) {
+    const double2 xu = x[u];
+    g[0] += xu.x * xu.x;
+    g[1] += xu.x * xu.y;
+  }
+  block_sum_n(g, red);
+  const double n1 = sqrt(g[0]);
   if (n1 == 0.0) {
     for (int u = t; u < MB; u += kThreads) x[u] = make_double2(0.0, 0.0);
     __syncthreads();
     return;
   }
-  double s12 = 0.0;
-  for (int u = t; u < MB; u += kThreads) {
-    const double q1 = x[u].x / n1;
-    x[u].x = q1;
-    s12 += q1 * x[u].y;
-  }
-  const double r12 = block_sum(s12, red);
+  const double r12 = g[1] / n1;
   double s2 = 0.0;
   for (int u = t; u < MB; u += kThreads) {
-    const double w = x[u].y - r12 * x[u].x;
-    x[u].y = w;
+    const double q1 = x[u].x / n1;
+    const double w = x[u].y - r12 * q1;
+    x[u] = make_double2(q1, w);
     s2 += w * w;
   }
   const double n2 = sqrt(block_sum(s2, red));
@@ -123,7 +183,7 @@ __device__ void qr2_inplace(double2* x, int MB, double* red) {
 
 // Y = M^T X - c (1^T X) / MB, reading X and writing Y (LDS).
 __device__ void apply_mt(const double2* x, double2* y, const int32_t* __restrict__ cp,
-                         const int32_t* __restrict__ ci, int cap, int MB, int NB, double* red) {
+                         const int32_t* __restrict__ ci, int cap, int MB, int NB, Reducer& red) {
   const int t = threadIdx.x;
   double2 s = make_double2(0.0, 0.0);
   for (int u = t; u < MB; u += kThreads) {
@@ -158,7 +218,7 @@ __device__ void apply_mt(const double2* x, double2* y, const int32_t* __restrict
 template <typename F>
 __device__ void apply_m(const double2* y, const int32_t* __restrict__ cp,
                         const int32_t* __restrict__ rp, const int32_t* __restrict__ ci, int cap,
-                        int MB, int NB, double* red, F f) {
+                        int MB, int NB, Reducer& red, F f) {
   const int t = threadIdx.x;
   double2 s = make_double2(0.0, 0.0);
   for (int v = t; v < NB; v += kThreads) {
@@ -202,7 +262,7 @@ struct MaskBits {
 
 // Y = M^T X - c (1^T X) / MB from the column bitmasks.
 __device__ void apply_mt_bits(const double2* x, double2* y, const MaskBits& mb, int MB, int NB,
-                              double* red) {
+                              Reducer& red) {
   const int t = threadIdx.x;
   double2 s = make_double2(0.0, 0.0);
   for (int u = t; u < MB; u += kThreads) {
@@ -236,7 +296,7 @@ __device__ void apply_mt_bits(const double2* x, double2* y, const MaskBits& mb, 
 
 // Z = M Y - 1 (c^T Y) / MB from the row bitmasks; calls f(u, z) on one lane per row.
 template <typename F>
-__device__ void apply_m_bits(const double2* y, const MaskBits& mb, int MB, int NB, double* red,
+__device__ void apply_m_bits(const double2* y, const MaskBits& mb, int MB, int NB, Reducer& red,
                              F f) {
   const int t = threadIdx.x;
   double2 s = make_double2(0.0, 0.0);
@@ -268,25 +328,67 @@ __device__ void apply_m_bits(const double2* y, const MaskBits& mb, int MB, int N
   }
 }
 
-// Ascending bitonic sort of n (power of two) (key, val) pairs in LDS, ordered by
-// key and then by val.
-__device__ void bitonic_sort_pairs(uint64_t* key, uint32_t* val, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      __syncthreads();
-      for (int i = threadIdx.x; i < (n >> 1); i += kThreads) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint64_t ka = key[lo], kb = key[hi];
-        const uint32_t va = val[lo], vb = val[hi];
-        const bool greater = ka > kb || (ka == kb && va > vb);
-        if (greater == up) {
-          key[lo] = kb;
-          key[hi] = ka;
-          val[lo] = vb;
-          val[hi] = va;
-        }
+// Ascending sort of n (a power of two, at most 4 * kThreads) (key, val) pairs in
+// LDS, ordered by key and then by val; the pairs must be distinct.  Runs of 64 are
+// sorted inside one wavefront each (an element's rank is the number of smaller
+// elements of its run, counted with lane reads), then runs are merged pairwise:
+// an element's place in the merged run is its index in its own run plus the number
+// of smaller elements in the partner run, found by a binary search of fixed depth.
+__device__ inline bool pair_less(uint64_t ka, uint32_t va, uint64_t kb, uint32_t vb) {
+  return ka < kb || (ka == kb && va < vb);
+}
+
+__device__ void sort_pairs(uint64_t* key, uint32_t* val, int n) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int r0 = n < 64 ? n : 64;
+  __syncthreads();
+  for (int base = w * 64; base < n; base += kThreads) {
+    const bool act = lane < r0;
+    const uint64_t k = act ? key[base + lane] : ~0ull;
+    const uint32_t v = act ? val[base + lane] : ~0u;
+    const uint32_t klo = (uint32_t)k, khi = (uint32_t)(k >> 32);
+    int rank = 0;
+    for (int j = 0; j < r0; ++j) {
+      const uint32_t jlo = __builtin_amdgcn_readlane(klo, j);
+      const uint32_t jhi = __builtin_amdgcn_readlane(khi, j);
+      const uint32_t jv = __builtin_amdgcn_readlane(v, j);
+      rank += pair_less(((uint64_t)jhi << 32) | jlo, jv, k, v) ? 1 : 0;
+    }
+    if (act) {
+      key[base + rank] = k;
+      val[base + rank] = v;
+    }
+  }
+  for (int r = r0; r < n; r <<= 1) {
+    __syncthreads();
+    uint64_t kk[4];
+    uint32_t vv[4];
+    int dst[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = t + c * kThreads;
+      if (i < n) {
+        const uint64_t k = key[i];
+        const uint32_t v = val[i];
+        const int own = i & ~(r - 1);
+        const int part = own ^ r;
+        // Largest m with part[m - 1] < (k, v): lifted bit by bit, then one last step.
+        int m = 0;
+        for (int step = r >> 1; step > 0; step >>= 1)
+          if (pair_less(key[part + m + step - 1], val[part + m + step - 1], k, v)) m += step;
+        if (pair_less(key[part + m], val[part + m], k, v)) ++m;
+        dst[c] = (own & ~r) + (i - own) + m;
+        kk[c] = k;
+        vv[c] = v;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (t + c * kThreads < n) {
+        key[dst[c]] = kk[c];
+        val[dst[c]] = vv[c];
       }
     }
   }
@@ -304,7 +406,8 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
     int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm, uint8_t* __restrict__ skipped,
     double* __restrict__ angles, double* __restrict__ stats) {
   extern __shared__ double2 lds[];
-  __shared__ double red[2 * kWaves];
+  __shared__ double red_buf[2 * 4 * kWaves];
+  Reducer red{red_buf, 0};
   __shared__ long long redi[kWaves];
   __shared__ int redm[kWaves];
   const int h = blockIdx.x;
@@ -496,9 +599,9 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
     }
     for (int u = MB + t; u < n2; u += kThreads) {
       key[u] = ~0ull;
-      val[u] = ~0u;
+      val[u] = (uint32_t)u;  // distinct padding, after every row
     }
-    bitonic_sort_pairs(key, val, n2);
+    sort_pairs(key, val, n2);
   } else {
     if (ang_h)
       for (int u = t; u < MB; u += kThreads) ang_h[u] = __longlong_as_double(0x7ff8000000000000ll);
@@ -520,10 +623,10 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
         key[pos] = ((uint64_t)bucket << 40) | ((uint64_t)(NB - nnz_row) << 20) | (uint64_t)pos;
       } else {
         key[pos] = ~0ull;
-        val[pos] = ~0u;
+        val[pos] = (uint32_t)pos;
       }
     }
-    bitonic_sort_pairs(key, val, n2);
+    sort_pairs(key, val, n2);
   }
   for (int pos = t; pos < MB; pos += kThreads) {
     const int row = (int)val[pos];

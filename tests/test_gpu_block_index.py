@@ -48,6 +48,12 @@ def test_block_index_full_size_wan():
     _check(w.mask.cpu(), "wan75k full size")
 
 
+def test_block_index_full_size_hunyuan():
+    # 929 blocks: a ragged last 64-column and 64-row tile in the transposed pass.
+    w = synth.make_workload("hunyuan119k", device="cuda")
+    _check(w.mask.cpu(), "hunyuan119k full size")
+
+
 def test_block_index_capacity_truncation():
     dev = gpu()
     m = torch.ones(1, 8, 8, dtype=torch.uint8)
