@@ -15,6 +15,15 @@ attention launch alone (HIP events on the launch stream) against the dense bf16
 MFMA peak; the CPU baseline is the fp64 oracle timed on a bounded sample of the
 same workload.
 
+With ``--workload gsrs75k`` one step is the GSRS search step instead: a full
+pass with block LSE, block importance and Top-p(0.9) candidates, the reordered
+sparse pass over the candidates with a second Top-p(0.8) restricted to them, and
+the reordered sparse pass over that subset; the value counts the selected block
+pairs of all three passes.
+
+The reorder uses the adaptive skip with the thresholds of the stored calibration
+(``--skip never`` reorders every head).
+
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload wan75k]
 """
 
@@ -45,10 +54,11 @@ def _kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _counter_profile():
+def _counter_profile(workload: str):
     """Figures of the committed counter summary (HBM bytes, L2 hits) if it was taken
-    on the current attention kernel source; otherwise an empty dict."""
-    if not os.path.exists(TRAFFIC_FILE):
+    on the current attention kernel source and this workload; otherwise an empty
+    dict."""
+    if workload != "wan75k" or not os.path.exists(TRAFFIC_FILE):
         return {}
     kv = {}
     with open(TRAFFIC_FILE) as f:
@@ -105,6 +115,77 @@ def cpu_baseline(w, budget_s: float = 12.0):
                       f"workload ({dt:.1f} s, BLAS threads={threads}, host cpus={os.cpu_count()})"}
 
 
+def gsrs_main(args, w, params):
+    """The GSRS search step (full pass, candidates, restricted selection, sparse passes)."""
+    import torch
+
+    from cache_aware_query_amd.pipeline import GsrsSearch
+
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    b, d, L = w.block, w.head_dim, w.seq_len
+    dev = w.q.device
+    gs = GsrsSearch(H, L, d, b, dev, reorder=params, p1=0.9, p2=0.8)
+    _log(f"GSRS search step: H={H} L={L} MB={mb} capacity per pass={gs.dense.cap}")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        gs.dense.build_index(gs.ones)
+        gs.dense.attention(w.q, w.k, w.v)
+        if ev is not None:
+            ev[1].record()
+        gs.dense.select()
+        gs.s1.step(w.q, w.k, w.v, gs.mask1, w.x0)
+        gs.s2.step(w.q, w.k, w.v, gs.mask2, w.x0)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    pairs = gs.selected_pairs()
+    flops = [4.0 * b * b * d * n for n in pairs]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    dense_ms = sum(a.elapsed_time(b_) for a, b_ in evs) / args.steps
+    value = sum(flops) / (ms_per_step * 1e-3) / 1e12
+    achieved = flops[0] / (dense_ms * 1e-3) / 1e12
+    subset_violations = int((gs.mask2.to(torch.int16) > gs.mask1.to(torch.int16)).sum().item())
+    reps = max(3, args.steps // 2)
+    detail = {"pairs_full_pass": pairs[0], "pairs_s1_p0.9": pairs[1], "pairs_s2_p0.8": pairs[2],
+              "density_s1": round(pairs[1] / (H * mb * mb), 5),
+              "density_s2": round(pairs[2] / (H * mb * mb), 5),
+              "s2_outside_s1": subset_violations,
+              "full_pass_attn_ms": round(dense_ms, 4),
+              "skipped_heads_s1": int(gs.s1.skipped.sum().item()),
+              "skipped_heads_s2": int(gs.s2.skipped.sum().item())}
+    if not args.no_variants:
+        detail.update({
+            "full_select_ms": round(_time_calls(gs.dense.select, reps), 4),
+            "s1_reorder_ms": round(_time_calls(lambda: gs.s1.reorder_rows(w.x0), reps), 4),
+            "s1_attn_ms": round(_time_calls(lambda: gs.s1.attention(w.q, w.k, w.v), reps), 4),
+            "s1_select_ms": round(_time_calls(gs.s1.select, reps), 4),
+            "s2_attn_ms": round(_time_calls(lambda: gs.s2.attention(w.q, w.k, w.v), reps), 4)})
+    line = {
+        "metric": "selected-block attention TFLOP/s + HBM read GB + L2 hit %, "
+                  "L=75,600 H=40 d=128",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "heads": H, "seq_len": L, "head_dim": d,
+                   "block": b, "p1": 0.9, "p2": 0.8},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +194,9 @@ def main():
     ap.add_argument("--workload", default="wan75k")
     ap.add_argument("--iters", type=int, default=5,
                     help="subspace iterations T of the reorder (the pages use 5..15)")
+    ap.add_argument("--skip", choices=("adaptive", "never", "always"), default="adaptive",
+                    help="reorder skip rule: the stored calibration, reorder every head, or "
+                         "keep every head in its original order")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -139,8 +223,14 @@ def main():
     nnz = int(w.mask.sum())
     flops = 4.0 * b * b * d * nnz
     n_xcd, cus, wave = caq.schedule_info(0, d)
-    params = caq.ReorderParams(wave=wave, n_slices=n_xcd, iters=args.iters,
-                               skip_mode=caq.WA_SKIP_NEVER)
+    if args.skip == "adaptive":
+        params = caq.ReorderParams.calibrated(wave=wave, n_slices=n_xcd, iters=args.iters)
+    else:
+        params = caq.ReorderParams(wave=wave, n_slices=n_xcd, iters=args.iters,
+                                   skip_mode=(caq.WA_SKIP_NEVER if args.skip == "never"
+                                              else caq.WA_SKIP_ALWAYS))
+    if args.workload == "gsrs75k":
+        return gsrs_main(args, w, params)
     hp = HotPath(H, L, d, b, dev, capacity=nnz, reorder=params,
                  schedule=caq.WA_SCHED_XCD_SLICED, gsrs_p=0.9)
     _log(f"H={H} L={L} d={d} b={b} MB={mb} nnz={nnz} density={nnz / (H * mb * mb):.4f} "
@@ -181,11 +271,13 @@ def main():
     attn_ms = sum(a.elapsed_time(b_) for a, b_ in evs) / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    prof = _counter_profile()
+    prof = _counter_profile(args.workload)
 
     detail = {"attn_ms": round(attn_ms, 4), "nnz_pairs": nnz,
               "selected_tflop": round(flops / 1e12, 4),
               "skipped_heads": int(hp.skipped.sum().item()),
+              "skip_per_head": "".join(str(int(x)) for x in hp.skipped.cpu().tolist()),
+              "skip_rule": args.skip,
               "reorder_iters": args.iters,
               "hbm_read_gb_per_launch": (round(prof["hbm_read_bytes_per_launch"] / 1e9, 3)
                                          if "hbm_read_bytes_per_launch" in prof else None),
@@ -206,6 +298,19 @@ def main():
         hp_id.schedule = caq.WA_SCHED_NATURAL
         t_nat = _time_calls(lambda: hp_id.attention(w.q, w.k, w.v), reps)
         del hp_id
+        # Stage ablation (WaveAlign Fig. 12): each stage alone, every head reordered.
+        ablation = {}
+        for name, s1, s2 in (("stage1_only", True, False), ("stage2_only", False, True),
+                             ("both_no_skip", True, True)):
+            pa = caq.ReorderParams(wave=wave, n_slices=n_xcd, iters=args.iters, stage1=s1,
+                                   stage2=s2, skip_mode=caq.WA_SKIP_NEVER)
+            hp.set_reorder_params(pa)
+            hp.reorder_rows(w.x0)
+            ablation[f"attn_ms_{name}"] = round(
+                _time_calls(lambda: hp.attention(w.q, w.k, w.v), reps), 4)
+        hp.set_reorder_params(params)
+        hp.reorder_rows(w.x0)
+        detail.update(ablation)
         e2e_reord = t_index + t_reorder + t_reord
         e2e_plain = t_index_id + min(t_xcd, t_nat)
         detail.update({"index_ms": round(t_index, 4),

@@ -13,9 +13,9 @@ wa_reorder_rows:
                     and  selected FLOP >= flops_min
                     and  adjacent-row Jaccard < jaccard_max
 
-The fit picks, among the observed statistic values, the thresholds that make the
-most sweep points decide correctly (reorder exactly where index + reorder +
-reordered kernel beat index + the better unreordered kernel).  The result is
+The fit picks the thresholds that make the most sweep points decide correctly
+(reorder exactly where index + reorder + reordered kernel beat index + the
+better unreordered kernel), each placed in the middle of the gap it falls in.  The result is
 written as JSON next to this file and read by ReorderParams.calibrated().
 
 Usage (on the GPU):  python -m cache_aware_query_amd.calibrate [--out PATH]
@@ -104,27 +104,42 @@ def measure(frames: int, density: float, heads: int, iters: int) -> dict:
     }
 
 
+def _gaps(values, geometric: bool):
+    """Thresholds in the middle of every gap between consecutive distinct values,
+    plus one below the smallest and one above the largest."""
+    v = sorted(set(values))
+    mid = (lambda x, y: (x * y) ** 0.5) if geometric else (lambda x, y: 0.5 * (x + y))
+    out = [v[0] * 0.5 if geometric else v[0] - 1.0]
+    out += [mid(x, y) for x, y in zip(v, v[1:])]
+    out.append(v[-1] * 2.0 if geometric else v[-1] + 1.0)
+    return out
+
+
 def fit(points: list) -> dict:
     """Thresholds (ws_min_bytes, flops_min, jaccard_max) deciding most points right.
 
-    Candidates are the observed values (just below them for the minimums, just
-    above for the maximum) plus the bounds that decide every point alike
-    (jaccard_max = 0 never reorders); ties prefer the rule that
-    reorders less (the cheaper mistake is a missed gain, not a slowdown)."""
-    ws_c = sorted({0.0} | {pt["ws_bytes"] * 0.999 for pt in points})
-    fl_c = sorted({0.0} | {pt["flops_per_head"] * 0.999 for pt in points})
-    jc_c = sorted({0.0, 1.0 + 1e-9} | {pt["jaccard"] * 1.001 for pt in points})
+    Candidates sit in the middle of the gaps between observed statistic values
+    (geometric middles for the byte and FLOP counts), so a threshold is as far as
+    possible from the points on either side.  Among the rules that decide the
+    most points right, the one whose wrong reorders lose the least time wins, and
+    remaining ties go to the least restrictive rule (larger jaccard_max, then
+    smaller ws_min, then smaller flops_min): a statistic that the sweep does not
+    need in order to separate wins from losses does not cause skips."""
+    ws_c = _gaps([pt["ws_bytes"] for pt in points], True)
+    fl_c = _gaps([pt["flops_per_head"] for pt in points], True)
+    jc_c = [min(max(j, 0.0), 1.0 + 1e-9) for j in _gaps([pt["jaccard"] for pt in points], False)]
+    jc_c += [0.0, 1.0 + 1e-9]
     best = None
-    for ws, fl, jc in itertools.product(ws_c, fl_c, jc_c):
+    for ws, fl, jc in itertools.product(ws_c, fl_c, sorted(set(jc_c))):
         dec = [pt["ws_bytes"] > ws and pt["flops_per_head"] >= fl and pt["jaccard"] < jc
                for pt in points]
         correct = sum(d == pt["reorder_wins"] for d, pt in zip(dec, points))
         lost = sum(max(0.0, -pt["gain_ms"]) for d, pt in zip(dec, points) if d)
-        key = (correct, -lost, -sum(dec))
+        key = (correct, -lost, jc, -ws, -fl)
         if best is None or key > best[0]:
             best = (key, ws, fl, jc)
-    (correct, _, _), ws, fl, jc = best
-    return {"ws_min_bytes": ws, "flops_min": fl, "jaccard_max": jc,
+    (correct, _, _, _, _), ws, fl, jc = best
+    return {"ws_min_bytes": max(ws, 0.0), "flops_min": max(fl, 0.0), "jaccard_max": jc,
             "points_correct": correct, "points": len(points)}
 
 

@@ -11,7 +11,8 @@ synchronising:
   5. wa_topp_select         next block mask                   (GSRS Algorithm 3)
 
 Steps 4-5 run only when ``gsrs_p`` is set; step 2 is replaced by the identity
-order when ``reorder`` is None.
+order when ``reorder`` is None.  ``GsrsSearch`` chains three such passes into the
+GSRS search step (full pass, Top-p candidates, restricted second selection).
 """
 
 from __future__ import annotations
@@ -65,6 +66,13 @@ class HotPath:
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
         self._params = (reorder or ReorderParams())._c()
 
+    def set_reorder_params(self, reorder: ReorderParams) -> None:
+        """New reorder parameters for a path built with reordering."""
+        if self.reorder is None:
+            raise ValueError("this path was built without reordering")
+        self.reorder = reorder
+        self._params = reorder._c()
+
     def index(self) -> BlockIndex:
         return BlockIndex(self.row_ptr, self.col_idx, self.row_nnz, self.csc_ptr, self.csc_idx,
                           self.H, self.mb, self.mb)
@@ -114,3 +122,49 @@ class HotPath:
         self.attention(q, k, v)
         if self.gsrs_p is not None:
             self.select()
+
+
+class GsrsSearch:
+    """The GSRS search step around WaveAlign, with buffers allocated once.
+
+    ``step`` enqueues on the current stream:
+
+      1. a full (all blocks) pass that also emits the Phase-1 block LSE G
+         (GSRS §5.3 Phase 1) and the row LSE;
+      2. the Phase-2 block importance W (§5.3 Phase 2);
+      3. Top-p at ``p1`` over all blocks, giving the candidate set S1 (Algorithm 3);
+      4. the WaveAlign reorder and the sparse pass over S1, again with G;
+      5. W and Top-p at ``p2`` restricted to S1, giving S2 (a subset of S1, the mask
+         of a later denoising step), and the reordered sparse pass over S2.
+
+    Every pass has the full capacity H*MB*MB, so no selected set can overflow.
+    """
+
+    def __init__(self, heads: int, seq_len: int, head_dim: int, block: int, device,
+                 reorder: ReorderParams | None, p1: float = 0.9, p2: float = 0.8,
+                 schedule: int = WA_SCHED_XCD_SLICED):
+        self.dense = HotPath(heads, seq_len, head_dim, block, device, reorder=None,
+                             schedule=schedule, gsrs_p=p1)
+        self.s1 = HotPath(heads, seq_len, head_dim, block, device, reorder=reorder,
+                          schedule=schedule, gsrs_p=p2)
+        self.s2 = HotPath(heads, seq_len, head_dim, block, device, reorder=reorder,
+                          schedule=schedule, gsrs_p=None)
+        self.ones = torch.ones(heads, self.dense.mb, self.dense.mb, dtype=torch.uint8,
+                               device=self.dense.device)
+
+    @property
+    def mask1(self) -> torch.Tensor:
+        return self.dense.next_mask
+
+    @property
+    def mask2(self) -> torch.Tensor:
+        return self.s1.next_mask
+
+    def step(self, q, k, v, x0) -> None:
+        self.dense.step(q, k, v, self.ones, x0)      # steps 1-3
+        self.s1.step(q, k, v, self.mask1, x0)        # steps 4-5 (W and Top-p over S1)
+        self.s2.step(q, k, v, self.mask2, x0)        # the pass over S2
+
+    def selected_pairs(self) -> tuple[int, int, int]:
+        """Block pairs of the dense pass, S1 and S2 (reads back three counts)."""
+        return tuple(int(hp.row_ptr[-1].item()) for hp in (self.dense, self.s1, self.s2))

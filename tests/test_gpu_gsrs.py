@@ -138,3 +138,33 @@ def test_gsrs_search_pipeline_growing_sparsity():
     s1_ref = oracle.topp_select(w_ref, rp, ci, H, mb, mb, 0.9)
     diff = np.sum(s1_ref != s1n)
     assert diff <= max(2, 0.002 * s1_ref.sum()), diff
+
+
+def test_gsrs_search_class_matches_the_explicit_chain():
+    """The benchmark's GsrsSearch (buffers allocated once, reordered sparse passes)
+    selects the same S1 and S2 as the explicit chain of library calls."""
+    from cache_aware_query_amd.pipeline import GsrsSearch
+
+    dev = gpu()
+    w = synth.make_workload("gsrs75k", device="cuda", heads=2, grid=(3, 45, 80))
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    banner(f"gsrs search class H={H} MB={mb}")
+    params = caq.ReorderParams(wave=64, n_slices=8, iters=5, skip_mode=caq.WA_SKIP_NEVER)
+    gs = GsrsSearch(H, w.seq_len, w.head_dim, w.block, dev, reorder=params)
+    gs.step(w.q, w.k, w.v, w.x0)
+    _, _, _, wts = _g_and_w(w)
+    idx = caq.build_block_index(w.mask.to(dev))
+    s1 = caq.topp_select(wts, idx.row_ptr, idx.col_idx, H, mb, mb, 0.9)
+    idx1 = caq.build_block_index(s1)
+    _, lse1, g1 = caq.sparse_attn_fwd(w.q, w.k, w.v, w.seq_len, w.block, idx1.row_ptr,
+                                      idx1.col_idx, with_g=True)
+    w1 = caq.block_importance(g1, lse1, idx1.row_ptr, w.seq_len, w.block)
+    s2 = caq.topp_select(w1, idx1.row_ptr, idx1.col_idx, H, mb, mb, 0.8)
+    torch.cuda.synchronize()
+    assert torch.equal(gs.mask1, s1)
+    # Reordering changes which workgroup runs a query block, not its arithmetic, so
+    # S1's reordered pass gives the same G and LSE and the same second selection.
+    assert torch.equal(gs.mask2, s2)
+    assert int((gs.mask2.to(torch.int16) > gs.mask1.to(torch.int16)).sum()) == 0
+    n = gs.selected_pairs()
+    assert n[0] == H * mb * mb and n[1] == int(s1.sum()) and n[2] == int(gs.mask2.sum())
