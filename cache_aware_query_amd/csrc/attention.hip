@@ -95,8 +95,10 @@ struct Tile {
   static constexpr int kDT = D / 32;           // d tiles of O^T
 };
 
-// Entries of a query block's K/V list staged in LDS.
-constexpr int kListCap = 1024;
+// Entries of a query block's K/V list staged in LDS.  With NB <= kListCap every
+// list is staged and the loop reads block ids from LDS only; larger masks read
+// them from global memory.
+constexpr int kListCap = 2048;
 
 // Lazy softmax reference: the running maximum used as the exponent reference
 // only moves when a new block maximum exceeds it by more than kTau (log2
@@ -167,7 +169,7 @@ struct QuarterDecision {
   bool low;     // the quarter keeps its own maximum as offset (block LSE precision)
 };
 
-template <int BLOCK, int D, bool WITH_G>
+template <int BLOCK, int D, bool WITH_G, bool STAGED>
 __global__ __launch_bounds__(BLOCK * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, int H, int L, int MB,
@@ -181,7 +183,7 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   __shared__ __attribute__((aligned(1024))) char sk1[T::kSubBytes];
   __shared__ __attribute__((aligned(1024))) char sv0[T::kSubBytes];
   __shared__ __attribute__((aligned(1024))) char sv1[T::kSubBytes];
-  __shared__ int32_t blist[kListCap + 4];
+  __shared__ int32_t blist[STAGED ? kListCap + 4 : 4];
 
   const int Lp = MB * BLOCK;
   int h, pos;
@@ -218,16 +220,31 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     return;
   }
 
-  // The query block's K/V list, staged in LDS so that the loop reads block ids
-  // without scalar-memory waits (longer lists fall back to global reads).
+  // The query block's K/V list, staged in LDS (STAGED: the launch guarantees
+  // NB <= kListCap) so that the loop reads block ids with LDS reads only: a read
+  // from global memory there is a vector-memory load, and waiting for it waits
+  // for every K/V copy in flight as well.
   const int ntiles = e1 - e0;
-  const bool staged = ntiles <= kListCap;
-  for (int i = threadIdx.x; i < min(ntiles, kListCap); i += BLOCK * 2) blist[i] = col_idx[e0 + i];
+  if constexpr (STAGED) {
+    for (int i = threadIdx.x; i < ntiles; i += BLOCK * 2) blist[i] = col_idx[e0 + i];
+  }
+  // Q rows (the B operand of S^T): lane holds q[qrow][16*ks + 8*g .. +7].  Their
+  // loads complete here, before any copy is in flight, for the same reason.
+  bf16x8 qf[T::kKS];
+  {
+    const uint16_t* qp = Q + head_off + (size_t)qrow * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < T::kKS; ++ks)
+      qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * ks));
+#pragma unroll
+    for (int ks = 0; ks < T::kKS; ++ks) asm volatile("" ::"v"(qf[ks]));
+  }
   __syncthreads();
   // List entry of tile t (wave-uniform; t is clamped into the list).
   auto list_entry = [&](int t) {
     t = min(t, ntiles - 1);
-    return __builtin_amdgcn_readfirstlane(staged ? blist[t] : col_idx[e0 + t]);
+    if constexpr (STAGED) return __builtin_amdgcn_readfirstlane(blist[t]);
+    else return __builtin_amdgcn_readfirstlane(col_idx[e0 + t]);
   };
 
   // Per-lane byte offsets of this wave's copy chunks inside a K half (rows = keys)
@@ -276,14 +293,6 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
             lv[buf] + (uint32_t)((wave + j * T::kWaves) * 1024));
   };
 
-  // Q fragment (B operand of S^T): lane holds q[qrow][16*ks + 8*g .. +7].
-  bf16x8 qf[T::kKS];
-  {
-    const uint16_t* qp = Q + head_off + (size_t)qrow * D + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < T::kKS; ++ks)
-      qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * ks));
-  }
 
   // S^T of one 32-key tile (key tile mt of the half in a K buffer).
   auto compute_s = [&](f32x16& acc, const char* sk, int mt) {
@@ -532,12 +541,17 @@ hipError_t launch_typed(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   int grid = H * MB;
   if (schedule == WA_SCHED_XCD_SLICED) grid = H * kXcds * ((MB + kXcds - 1) / kXcds);
   const float sl2 = scale * kLog2e;
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(BLOCK * 2), 0, s, q, k, v, H, L, MB, row_ptr,
+                       col_idx, cap, perm, schedule, sl2, o, lse, g);
+  };
+  const bool staged = MB <= kListCap;  // NB = MB: every list fits in LDS
   if (g != nullptr) {
-    hipLaunchKernelGGL((k_sparse_attn<BLOCK, D, true>), dim3(grid), dim3(BLOCK * 2), 0, s, q, k,
-                       v, H, L, MB, row_ptr, col_idx, cap, perm, schedule, sl2, o, lse, g);
+    if (staged) launch(k_sparse_attn<BLOCK, D, true, true>);
+    else launch(k_sparse_attn<BLOCK, D, true, false>);
   } else {
-    hipLaunchKernelGGL((k_sparse_attn<BLOCK, D, false>), dim3(grid), dim3(BLOCK * 2), 0, s, q, k,
-                       v, H, L, MB, row_ptr, col_idx, cap, perm, schedule, sl2, o, lse, g);
+    if (staged) launch(k_sparse_attn<BLOCK, D, false, true>);
+    else launch(k_sparse_attn<BLOCK, D, false, false>);
   }
   return hipGetLastError();
 }
