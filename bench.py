@@ -77,6 +77,17 @@ def _counter_profile(workload: str):
     return out
 
 
+def _time_interleaved(fns: dict, rounds: int, reps: int) -> dict:
+    """Median over rounds of the average ms of each fn, the fns taking turns."""
+    import statistics
+
+    times = {k: [] for k in fns}
+    for _ in range(rounds):
+        for k, fn in fns.items():
+            times[k].append(_time_calls(fn, reps))
+    return {k: statistics.median(v) for k, v in times.items()}
+
+
 def _time_calls(fn, reps):
     """Average ms of fn() over reps calls, timed with events on the current stream."""
     import torch
@@ -118,6 +129,9 @@ def cpu_baseline(w, budget_s: float = 12.0):
 def gsrs_main(args, w, params):
     """The GSRS search step (full pass, candidates, restricted selection, sparse passes)."""
     import torch
+
+    if args.schedule_steps > 0:
+        return gsrs_schedule_main(args, w, params)
 
     from cache_aware_query_amd.pipeline import GsrsSearch
 
@@ -186,6 +200,90 @@ def gsrs_main(args, w, params):
     print(json.dumps(line), flush=True)
 
 
+def gsrs_schedule_main(args, w, params):
+    """The GSRS denoising schedule: warmup, four searches, mask reuse in between."""
+    import torch
+
+    import synth
+    from cache_aware_query_amd.pipeline import GsrsSchedule
+
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    b, d, L = w.block, w.head_dim, w.seq_len
+    search = (10, 20, 30, 40)
+    gs = GsrsSchedule(H, L, d, b, w.q.device, reorder=params, steps=args.schedule_steps,
+                      search_steps=search, thresholds=(0.95, 0.9, 0.85, 0.8))
+    # Inputs drift across steps: state k holds from search k on, state 0 before.
+    states = synth.drift_states(w, len(search) + 1)
+
+    def inputs(t):
+        k = sum(1 for s_ in search if t >= s_)
+        q, kk, v = states[k]
+        return q, kk, v, w.x0
+
+    def run_once(record):
+        evs, sizes = [], {}
+
+        def on_step(t, kind):
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                evs.append((t, kind, e))
+                if kind == "search":
+                    sizes[t] = (gs.search.row_ptr[-1:].clone(), gs.sparse.row_ptr[-1:].clone())
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gs.run(inputs, on_step)
+        return e0, evs, sizes
+
+    _log(f"GSRS schedule: {args.schedule_steps} steps, searches at {search}")
+    for _ in range(args.warmup):
+        run_once(False)
+    torch.cuda.synchronize()
+    per_kind = {"warmup": 0.0, "search": 0.0, "reuse": 0.0}
+    total_ms, pairs = 0.0, 0
+    full_pairs = H * mb * mb
+    t0 = time.perf_counter()
+    runs = [run_once(True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    densities = {}
+    for e0, evs, sizes in runs:
+        prev, cur_pairs = e0, full_pairs
+        for t, kind, e in evs:
+            dt = prev.elapsed_time(e)
+            per_kind[kind] += dt
+            total_ms += dt
+            if kind == "search":
+                s1_pairs = int(sizes[t][0].item())
+                step_pairs = full_pairs if t == search[0] else s1_pairs
+                cur_pairs = int(sizes[t][1].item())
+                densities[t] = round(cur_pairs / full_pairs, 4)
+            else:
+                step_pairs = full_pairs if kind == "warmup" else cur_pairs
+            pairs += step_pairs
+            prev = e
+    n = args.steps
+    ms_per_run = total_ms / n
+    flops = 4.0 * b * b * d * pairs / n
+    value = flops / (ms_per_run * 1e-3) / 1e12
+    line = {
+        "metric": "selected-block attention TFLOP/s + HBM read GB + L2 hit %, "
+                  "L=75,600 H=40 d=128",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": n,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_run, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gsrs75k-schedule", "heads": H, "seq_len": L, "head_dim": d,
+                   "block": b, "denoising_steps": args.schedule_steps,
+                   "search_steps": list(search), "p": [0.95, 0.9, 0.85, 0.8]},
+        "detail": {"ms_by_kind_per_run": {k: round(v / n, 3) for k, v in per_kind.items()},
+                   "steps_by_kind": {k: gs.kinds.count(k) for k in per_kind},
+                   "mask_density_after_search": densities,
+                   "selected_tflop_per_run": round(flops / 1e12, 3),
+                   "wall_ms_per_run": round(wall_ms, 3)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +295,9 @@ def main():
     ap.add_argument("--skip", choices=("adaptive", "never", "always"), default="adaptive",
                     help="reorder skip rule: the stored calibration, reorder every head, or "
                          "keep every head in its original order")
+    ap.add_argument("--schedule-steps", type=int, default=0,
+                    help="with --workload gsrs75k: run the whole GSRS denoising schedule of this "
+                         "many steps (searches at 10, 20, 30, 40) per bench step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -287,40 +388,55 @@ def main():
         # Stage times of the reordered step.
         t_index = _time_calls(lambda: hp.build_index(w.mask), reps)
         t_reorder = _time_calls(lambda: hp.reorder_rows(w.x0), reps)
-        t_reord = _time_calls(lambda: hp.attention(w.q, w.k, w.v), reps)
         t_select = _time_calls(hp.select, reps)
-        # The same kernel without reordering: identity order, natural and XCD-sliced
-        # schedules (the index it needs has no transposed lists).
+        # The same kernel without reordering (identity order; its index has no
+        # transposed lists), and the stage ablation (WaveAlign Fig. 12, every head
+        # reordered), each with buffers of its own.
         hp_id = HotPath(H, L, d, b, dev, capacity=nnz, reorder=None,
                         schedule=caq.WA_SCHED_XCD_SLICED, gsrs_p=0.9)
+        hp_id.build_index(w.mask)
         t_index_id = _time_calls(lambda: hp_id.build_index(w.mask), reps)
-        t_xcd = _time_calls(lambda: hp_id.attention(w.q, w.k, w.v), reps)
-        hp_id.schedule = caq.WA_SCHED_NATURAL
-        t_nat = _time_calls(lambda: hp_id.attention(w.q, w.k, w.v), reps)
-        del hp_id
-        # Stage ablation (WaveAlign Fig. 12): each stage alone, every head reordered.
         ablation = {}
         for name, s1, s2 in (("stage1_only", True, False), ("stage2_only", False, True),
                              ("both_no_skip", True, True)):
             pa = caq.ReorderParams(wave=wave, n_slices=n_xcd, iters=args.iters, stage1=s1,
                                    stage2=s2, skip_mode=caq.WA_SKIP_NEVER)
-            hp.set_reorder_params(pa)
-            hp.reorder_rows(w.x0)
-            ablation[f"attn_ms_{name}"] = round(
-                _time_calls(lambda: hp.attention(w.q, w.k, w.v), reps), 4)
-        hp.set_reorder_params(params)
-        hp.reorder_rows(w.x0)
-        detail.update(ablation)
-        e2e_reord = t_index + t_reorder + t_reord
-        e2e_plain = t_index_id + min(t_xcd, t_nat)
+            hpa = HotPath(H, L, d, b, dev, capacity=nnz, reorder=pa,
+                          schedule=caq.WA_SCHED_XCD_SLICED, gsrs_p=0.9)
+            hpa.build_index(w.mask)
+            hpa.reorder_rows(w.x0)
+            ablation[name] = hpa
+
+        def with_schedule(path, sched):
+            def run():
+                path.schedule = sched
+                path.attention(w.q, w.k, w.v)
+            return run
+
+        # Attention variants timed in interleaved rounds (medians), so that clock
+        # drift during the run does not favour whichever variant runs first.  The
+        # head-interleaved order is the concurrent-head execution of WaveAlign
+        # §VI-B ("Original" on the A40).
+        variants = {
+            "reordered_xcd": with_schedule(hp, caq.WA_SCHED_XCD_SLICED),
+            "identity_xcd": with_schedule(hp_id, caq.WA_SCHED_XCD_SLICED),
+            "natural_order": with_schedule(hp_id, caq.WA_SCHED_NATURAL),
+            "heads_interleaved": with_schedule(hp_id, caq.WA_SCHED_HEADS_INTERLEAVED),
+        }
+        for name, hpa in ablation.items():
+            variants[name] = with_schedule(hpa, caq.WA_SCHED_XCD_SLICED)
+        t = _time_interleaved(variants, rounds=5, reps=max(2, reps // 2))
+        hp.schedule = caq.WA_SCHED_XCD_SLICED
+        del hp_id, ablation
+        e2e_reord = t_index + t_reorder + t["reordered_xcd"]
+        e2e_plain = t_index_id + min(t["identity_xcd"], t["natural_order"],
+                                     t["heads_interleaved"])
         detail.update({"index_ms": round(t_index, 4),
                        "reorder_ms": round(t_reorder, 4),
-                       "attn_ms_reordered_xcd": round(t_reord, 4),
                        "gsrs_select_ms": round(t_select, 4),
-                       "index_ms_without_reorder": round(t_index_id, 4),
-                       "attn_ms_identity_xcd": round(t_xcd, 4),
-                       "attn_ms_natural_order": round(t_nat, 4),
-                       "e2e_ms_reordered": round(e2e_reord, 4),
+                       "index_ms_without_reorder": round(t_index_id, 4)})
+        detail.update({f"attn_ms_{k}": round(v, 4) for k, v in t.items()})
+        detail.update({"e2e_ms_reordered": round(e2e_reord, 4),
                        "e2e_ms_unreordered_best": round(e2e_plain, 4),
                        "reorder_speedup_incl_overhead": round(e2e_plain / e2e_reord, 4)})
 

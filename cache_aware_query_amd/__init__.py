@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libwavealign.so")
 
 WA_SCHED_NATURAL = 0
 WA_SCHED_XCD_SLICED = 1
+WA_SCHED_HEADS_INTERLEAVED = 2
 WA_SKIP_ADAPTIVE = 0
 WA_SKIP_NEVER = 1
 WA_SKIP_ALWAYS = 2

@@ -134,7 +134,8 @@ int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int
   if (!supported_shape(head_dim, block))
     return fail(WA_ERR_UNSUPPORTED, "head_dim %d / block %d not in {64, 128}", head_dim, block);
   if (capacity < 0) return fail(WA_ERR_INVALID_ARG, "negative capacity");
-  if (schedule != WA_SCHED_NATURAL && schedule != WA_SCHED_XCD_SLICED)
+  if (schedule != WA_SCHED_NATURAL && schedule != WA_SCHED_XCD_SLICED &&
+      schedule != WA_SCHED_HEADS_INTERLEAVED)
     return fail(WA_ERR_INVALID_ARG, "unknown schedule %d", schedule);
   if (!(scale > 0.0f) || !(scale < 1e30f)) return fail(WA_ERR_INVALID_ARG, "scale must be > 0");
   const int64_t MB = ((int64_t)L + block - 1) / block;

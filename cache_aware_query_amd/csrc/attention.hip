@@ -37,7 +37,9 @@
 //  * Workgroup -> query block: natural head-major order, or XCD-sliced: workgroup
 //    w runs on XCD w % 8 (round-robin dispatch), and XCD x takes the x-th
 //    contiguous slice of each head's execution order, so each XCD's L2 sees one
-//    contiguous run of the (reordered) schedule and all XCDs stay on one head.
+//    contiguous run of the (reordered) schedule and all XCDs stay on one head.  The
+//    head-interleaved order (position w / H of head w % H) runs all heads at once,
+//    the concurrent-head execution WaveAlign compares sequential heads with.
 #include <math.h>
 
 #include <type_traits>
@@ -194,6 +196,9 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     h = j / s;
     pos = x * s + j % s;
     if (pos >= MB) return;
+  } else if (schedule == WA_SCHED_HEADS_INTERLEAVED) {
+    h = blockIdx.x % H;
+    pos = blockIdx.x / H;
   } else {
     h = blockIdx.x / MB;
     pos = blockIdx.x % MB;

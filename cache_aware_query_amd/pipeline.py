@@ -104,6 +104,14 @@ class HotPath:
                                       _ptr(g), _ptr(self.workspace), self.ws_bytes, s),
                "wa_sparse_attn_fwd")
 
+    def attention_plain(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
+        """The attention pass without the block LSE, whatever ``gsrs_p`` is."""
+        saved, self.gsrs_p = self.gsrs_p, None
+        try:
+            self.attention(q, k, v)
+        finally:
+            self.gsrs_p = saved
+
     def select(self) -> None:
         lib, s = self.lib, _stream(self.device)
         _check(lib.wa_block_importance(_ptr(self.g), _ptr(self.lse), _ptr(self.row_ptr), self.cap,
@@ -168,3 +176,84 @@ class GsrsSearch:
     def selected_pairs(self) -> tuple[int, int, int]:
         """Block pairs of the dense pass, S1 and S2 (reads back three counts)."""
         return tuple(int(hp.row_ptr[-1].item()) for hp in (self.dense, self.s1, self.s2))
+
+
+class GsrsSchedule:
+    """The GSRS inference schedule over denoising steps, around WaveAlign.
+
+    The GSRS page describes its pipeline (warmup, fused evaluation, growing sparsity,
+    reduced search, mask reuse; §4-5 and Algorithm 4, whose listing the text only
+    summarises).  Read plainly, step t of ``steps`` runs:
+
+      * t < T[0] (warmup): full attention;
+      * t = T[0] (first search): full attention with the block LSE, then block
+        importance and Top-p at p[0]; the kept set is the candidate set S1 and the
+        current mask;
+      * t = T[k], k >= 1 (reduced search): attention over S1 with the block LSE,
+        importance normalised over S1, Top-p at p[k]; the kept set (inside S1) is the
+        current mask;
+      * any other t > T[0]: attention under the current mask (mask reuse).
+
+    Every sparse pass runs in the WaveAlign order of its mask; a mask's index and
+    reorder are built once, when the mask is chosen, and reused until it changes.
+    ``inputs(t)`` returns the (q, k, v, x0) of step t.
+    """
+
+    def __init__(self, heads: int, seq_len: int, head_dim: int, block: int, device,
+                 reorder: ReorderParams | None, steps: int = 50,
+                 search_steps=(10, 20, 30, 40), thresholds=(0.95, 0.9, 0.85, 0.8),
+                 schedule: int = WA_SCHED_XCD_SLICED):
+        if len(search_steps) != len(thresholds) or not search_steps:
+            raise ValueError("one threshold per search step")
+        if list(search_steps) != sorted(search_steps) or search_steps[-1] >= steps:
+            raise ValueError("search steps must be increasing and below the step count")
+        self.steps, self.T, self.p = steps, tuple(search_steps), tuple(thresholds)
+        self.full = HotPath(heads, seq_len, head_dim, block, device, reorder=None,
+                            schedule=schedule, gsrs_p=thresholds[0])
+        self.search = HotPath(heads, seq_len, head_dim, block, device, reorder=reorder,
+                              schedule=schedule, gsrs_p=thresholds[-1])
+        self.sparse = HotPath(heads, seq_len, head_dim, block, device, reorder=reorder,
+                              schedule=schedule, gsrs_p=None)
+        mb = self.full.mb
+        self.ones = torch.ones(heads, mb, mb, dtype=torch.uint8, device=self.full.device)
+        self.s1 = torch.zeros_like(self.ones)     # candidate set of the first search
+        self.mask = torch.zeros_like(self.ones)   # current mask
+        self.kinds: list[str] = []                # what each step ran
+
+    def run(self, inputs, on_step=None) -> None:
+        """Enqueue the whole schedule; ``on_step(t, kind)`` is called after each step."""
+        self.kinds = []
+        self.full.build_index(self.ones)
+        for t in range(self.steps):
+            q, k, v, x0 = inputs(t)
+            if t < self.T[0]:
+                kind = "warmup"
+                self.full.attention_plain(q, k, v)
+            elif t == self.T[0]:
+                kind = "search"
+                self.full.attention(q, k, v)
+                self.full.select()
+                self.s1.copy_(self.full.next_mask)
+                self.mask.copy_(self.s1)
+                self.search.build_index(self.s1)
+                if self.search.reorder is not None:
+                    self.search.reorder_rows(x0)
+                self._choose_mask(x0)
+            elif t in self.T:
+                kind = "search"
+                self.search.gsrs_p = self.p[self.T.index(t)]
+                self.search.attention(q, k, v)
+                self.search.select()
+                self.mask.copy_(self.search.next_mask)
+                self._choose_mask(x0)
+            else:
+                kind = "reuse"
+                self.sparse.attention(q, k, v)
+            self.kinds.append(kind)
+            if on_step is not None:
+                on_step(t, kind)
+
+    def _choose_mask(self, x0) -> None:
+        self.sparse.build_index(self.mask)
+        if self.sparse.reorder is not None:
+            self.sparse.reorder_rows(x0)

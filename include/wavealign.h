@@ -48,6 +48,9 @@ extern "C" {
 /* Attention schedules (how workgroups map to query blocks). */
 #define WA_SCHED_NATURAL 0     /* workgroup w runs position w of the head-major order      */
 #define WA_SCHED_XCD_SLICED 1  /* XCD x runs the x-th contiguous slice of each head's order */
+#define WA_SCHED_HEADS_INTERLEAVED 2 /* workgroup w runs position w / H of head w % H: all heads
+                                        at once, the concurrent-head execution that WaveAlign
+                                        VI-B contrasts with sequential heads */
 
 /* Skip modes of wa_reorder_rows. */
 #define WA_SKIP_ADAPTIVE 0
@@ -175,7 +178,7 @@ int wa_sparse_attn_workspace_size(int32_t H, int32_t L, int32_t head_dim, int32_
  *   perm      int32 [H][MB] or NULL  execution order [WA §V]: position p of head h runs
  *             query block perm[h][p]; O, LSE and G stay in the original order (the
  *             permutation is applied by indexing, the inverse reorder is implicit)
- *   schedule  WA_SCHED_NATURAL or WA_SCHED_XCD_SLICED
+ *   schedule  WA_SCHED_NATURAL, WA_SCHED_XCD_SLICED or WA_SCHED_HEADS_INTERLEAVED
  *   o         bf16 [H][L_pad][head_dim] out
  *   lse       float [H][L_pad] out, natural log
  *   g         float [row_ptr[H*MB]][block] out or NULL  [GSRS §5.3 Phase 1] for CSR

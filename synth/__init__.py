@@ -11,6 +11,7 @@ from .workloads import (  # noqa: F401
     CONFIGS,
     Workload,
     WorkloadConfig,
+    drift_states,
     get_config,
     make_workload,
     random_tiny_case,

@@ -26,6 +26,9 @@ Five workloads are defined (``CONFIGS``):
                  (0.9) over the softmax of pooled block scores.
 ``gsrs75k``      The ``wan75k`` tensors with an all-ones mask (the first, dense
                  search pass of the GSRS pipeline).
+``random20``     The Wan shape with structureless masks: every block Bernoulli(0.2)
+                 plus the diagonal, the random-mask locality floor of WaveAlign
+                 Table I.
 
 Any field can be overridden (``make_workload("wan75k", grid=(9, 45, 80),
 heads=16, density=0.1)``): ``density`` fixes the Top-k budget of every head,
@@ -64,7 +67,7 @@ class WorkloadConfig:
     grid: tuple  # (frames, height, width)
     block: int
     qkv: str     # "gaussian" | "smooth"
-    mask: str    # "bernoulli" | "neighbour" | "topk" | "topp" | "dense"
+    mask: str    # "bernoulli" | "neighbour" | "topk" | "topp" | "dense" | "random"
     hilbert: bool = False
     density: float | None = None  # "topk": a fixed k = round(density * NB) for every head
 
@@ -89,6 +92,8 @@ CONFIGS = {
     "hunyuan119k": WorkloadConfig("hunyuan119k", 3, 24, 128, (33, 45, 80), 128, "smooth", "topp",
                                   hilbert=True),
     "gsrs75k": WorkloadConfig("gsrs75k", 4, 40, 128, (21, 45, 80), 128, "smooth", "dense"),
+    "random20": WorkloadConfig("random20", 5, 40, 128, (21, 45, 80), 128, "smooth", "random",
+                               density=0.2),
 }
 
 
@@ -210,6 +215,17 @@ def _mask_bernoulli(cfg: WorkloadConfig, device, seed: int) -> torch.Tensor:
     return m
 
 
+def _mask_random(cfg: WorkloadConfig, device, seed: int) -> torch.Tensor:
+    """Every block Bernoulli(density) plus the diagonal (no structure to exploit)."""
+    H, nb = cfg.heads, cfg.num_blocks
+    m = torch.zeros(H, nb, nb, dtype=torch.uint8, device=device)
+    for h in range(H):
+        g = _gen(device, cfg.index, "mask", h, seed)
+        m[h] = (torch.rand(nb, nb, generator=g, device=device) < cfg.density).to(torch.uint8)
+        m[h].fill_diagonal_(1)
+    return m
+
+
 def _mask_neighbour(cfg: WorkloadConfig, device, seed: int) -> torch.Tensor:
     """Chebyshev-2 neighbours on the (frame, row band) block grid + lognormal far blocks."""
     H, nb = cfg.heads, cfg.num_blocks
@@ -286,6 +302,8 @@ def make_workload(name_or_cfg, device="cpu", seed: int = BASE_SEED, **overrides)
         mask = _mask_topp(cfg, q, k, device)
     elif cfg.mask == "dense":
         mask = torch.ones(cfg.heads, cfg.num_blocks, cfg.num_blocks, dtype=torch.uint8, device=device)
+    elif cfg.mask == "random":
+        mask = _mask_random(cfg, device, seed)
     else:
         raise ValueError(cfg.mask)
     x0 = torch.empty(cfg.heads, cfg.num_blocks, 2, dtype=torch.float32, device=device)
@@ -317,3 +335,24 @@ def random_tiny_case(seed: int, heads: int = 2, seq_len: int = 300, head_dim: in
     cfg = WorkloadConfig(f"random{seed}", 100 + seed, heads, head_dim, (1, 1, seq_len), block,
                          "gaussian", "bernoulli")
     return Workload(cfg, q, k, v, mask, x0, seq_len, block)
+
+
+def drift_states(w: Workload, n_states: int, sigma: float = 0.3, seed: int = BASE_SEED):
+    """Q, K, V that drift across denoising steps: state s (0 <= s < n_states) is
+    x + (s / (n_states - 1)) * delta_x for x in Q, K, V, with delta_x ~ N(0, sigma^2)
+    drawn once per tensor from the seed (rows past L stay zero).  Returns a list of
+    (q, k, v) in bf16 on the workload's device."""
+    cfg = w.cfg
+    dev = w.q.device
+    deltas = []
+    for name, x in (("noise_q", w.q), ("noise_k", w.k), ("noise_v", w.v)):
+        g = _gen(dev, cfg.index + 1000, name, 0, seed)
+        d = torch.randn(x.shape, generator=g, device=dev, dtype=torch.float32) * sigma
+        d[:, w.seq_len:, :] = 0.0
+        deltas.append(d)
+    states = []
+    for s in range(n_states):
+        a = s / max(n_states - 1, 1)
+        states.append(tuple((x.float() + a * d).to(torch.bfloat16)
+                            for x, d in zip((w.q, w.k, w.v), deltas)))
+    return states

@@ -88,7 +88,7 @@ def test_output_is_independent_of_execution_order():
     o0, l0, g0, _ = _run(w, schedule=caq.WA_SCHED_NATURAL, with_g=True)
     gen = torch.Generator().manual_seed(5)
     perm = torch.stack([torch.randperm(mb, generator=gen) for _ in range(3)]).to(torch.int32)
-    for sched in (caq.WA_SCHED_NATURAL, caq.WA_SCHED_XCD_SLICED):
+    for sched in (caq.WA_SCHED_NATURAL, caq.WA_SCHED_XCD_SLICED, caq.WA_SCHED_HEADS_INTERLEAVED):
         o1, l1, g1, _ = _run(w, perm=perm, schedule=sched, with_g=True)
         assert torch.equal(o0, o1) and torch.equal(l0, l1) and torch.equal(g0, g1)
     # repeated runs are bitwise identical

@@ -168,3 +168,44 @@ def test_gsrs_search_class_matches_the_explicit_chain():
     assert int((gs.mask2.to(torch.int16) > gs.mask1.to(torch.int16)).sum()) == 0
     n = gs.selected_pairs()
     assert n[0] == H * mb * mb and n[1] == int(s1.sum()) and n[2] == int(gs.mask2.sum())
+
+
+def test_gsrs_schedule_reduced_search_and_mask_reuse():
+    """Warmup, a full first search, reduced searches inside S1, mask reuse between."""
+    from cache_aware_query_amd.pipeline import GsrsSchedule
+
+    dev = gpu()
+    w = synth.make_workload("gsrs75k", device="cuda", heads=2, grid=(3, 45, 80))
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    banner(f"gsrs schedule H={H} MB={mb}")
+    search = (2, 4, 6)
+    states = synth.drift_states(w, len(search) + 1)
+    params = caq.ReorderParams(wave=64, n_slices=8, iters=5, skip_mode=caq.WA_SKIP_NEVER)
+    gs = GsrsSchedule(H, w.seq_len, w.head_dim, w.block, dev, reorder=params, steps=8,
+                      search_steps=search, thresholds=(0.95, 0.9, 0.8))
+
+    def inputs(t):
+        q, k, v = states[sum(1 for s in search if t >= s)]
+        return q, k, v, w.x0
+
+    masks = {}
+
+    def on_step(t, kind):
+        if kind == "search":
+            masks[t] = gs.mask.clone()
+
+    gs.run(inputs, on_step)
+    torch.cuda.synchronize()
+    assert gs.kinds == ["warmup", "warmup", "search", "reuse", "search", "reuse", "search",
+                        "reuse"]
+    s1 = gs.s1.to(torch.int16)
+    assert 0 < int(s1.sum()) < H * mb * mb
+    for t, m in masks.items():
+        assert int((m.to(torch.int16) > s1).sum()) == 0, t   # every mask lies inside S1
+        assert int(m.sum()) > 0
+    # The last step reuses the last search's mask: same output as a plain pass.
+    q, k, v, _ = inputs(7)
+    idx = caq.build_block_index(masks[6])
+    o, lse, _ = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx)
+    torch.cuda.synchronize()
+    assert torch.equal(o, gs.sparse.o) and torch.equal(lse, gs.sparse.lse)

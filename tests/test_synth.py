@@ -59,3 +59,12 @@ def test_random_tiny_case():
     assert w.q.shape == (2, 320, 64)
     assert int(w.mask[:, 1].sum()) == 0
     assert torch.all(w.q[:, 300:] == 0)
+
+
+def test_random_mask_density_and_diagonal():
+    w = synth.make_workload("random20", heads=2, grid=(3, 45, 80))
+    m = w.mask
+    nb = m.shape[1]
+    assert torch.all(torch.diagonal(m, dim1=1, dim2=2) == 1)
+    dens = m.float().mean().item()
+    assert abs(dens - (0.2 + 0.8 / nb)) < 0.03, dens
