@@ -262,6 +262,17 @@ def gsrs_schedule_main(args, w, params):
                 step_pairs = full_pairs if kind == "warmup" else cur_pairs
             pairs += step_pairs
             prev = e
+    # Diagnostics outside the timed runs (GSRS §3 attention recall, Fig. 2): with the
+    # last step's inputs, the share of the full attention that the candidate set S1
+    # and the final mask keep.
+    import cache_aware_query_amd as caq
+
+    q, kk, v, _ = inputs(args.schedule_steps - 1)
+    gs.full.attention(q, kk, v)
+    gs.full.importance()
+    recall = {name: round(float(caq.mask_recall(gs.full.w, gs.full.row_ptr, gs.full.col_idx,
+                                                m).mean().item()), 4)
+              for name, m in (("candidate_set_s1", gs.s1), ("final_mask", gs.mask))}
     n = args.steps
     ms_per_run = total_ms / n
     flops = 4.0 * b * b * d * pairs / n
@@ -278,6 +289,7 @@ def gsrs_schedule_main(args, w, params):
         "detail": {"ms_by_kind_per_run": {k: round(v / n, 3) for k, v in per_kind.items()},
                    "steps_by_kind": {k: gs.kinds.count(k) for k in per_kind},
                    "mask_density_after_search": densities,
+                   "recall_at_last_step": recall,
                    "selected_tflop_per_run": round(flops / 1e12, 3),
                    "wall_ms_per_run": round(wall_ms, 3)},
     }

@@ -32,7 +32,8 @@ EXPORTED = (
     "wa_abi_version", "wa_last_error", "wa_schedule_info", "wa_build_block_index",
     "wa_reorder_rows", "wa_reorder_needs_csc", "wa_sparse_attn_workspace_size",
     "wa_sparse_attn_fwd",
-    "wa_block_importance", "wa_topp_select", "wa_gather_blocks", "wa_scatter_blocks",
+    "wa_block_importance", "wa_topp_select", "wa_mask_recall", "wa_gather_blocks",
+    "wa_scatter_blocks",
 )
 
 
@@ -118,6 +119,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                _P]),
         "wa_topp_select": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, ctypes.c_double,
                                           _P, _P]),
+        "wa_mask_recall": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P]),
         "wa_gather_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I64, _P]),
         "wa_scatter_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I64, _P]),
     }
@@ -334,6 +336,25 @@ def topp_select(w: torch.Tensor, row_ptr: torch.Tensor, col_idx: torch.Tensor, h
     _check(lib.wa_topp_select(_ptr(w), _ptr(row_ptr), _ptr(col_idx), cap, heads, mb, nb, float(p),
                               _ptr(m), _stream(w.device)), "wa_topp_select")
     return m
+
+
+def mask_recall(w: torch.Tensor, row_ptr: torch.Tensor, col_idx: torch.Tensor,
+                mask: torch.Tensor) -> torch.Tensor:
+    """GSRS attention recall of ``mask`` [H, MB, NB] per query block, float [H, MB], from
+    the block weights ``w`` of an evaluated pass (its index row_ptr / col_idx)."""
+    lib = load_library()
+    _need(w, torch.float32, "w", 1)
+    _need(row_ptr, torch.int32, "row_ptr", 1)
+    _need(col_idx, torch.int32, "col_idx", 1)
+    _need(mask, torch.uint8, "mask", 3)
+    heads, mb, nb = mask.shape
+    if row_ptr.numel() != heads * mb + 1:
+        raise ValueError("row_ptr does not match the mask's H * MB rows")
+    out = torch.empty(heads, mb, dtype=torch.float32, device=w.device)
+    cap = min(w.numel(), col_idx.numel())
+    _check(lib.wa_mask_recall(_ptr(w), _ptr(row_ptr), _ptr(col_idx), cap, heads, mb, nb,
+                              _ptr(mask), _ptr(out), _stream(w.device)), "wa_mask_recall")
+    return out
 
 
 def gather_blocks(src: torch.Tensor, perm: torch.Tensor, rows_per_block: int) -> torch.Tensor:

@@ -183,6 +183,20 @@ int wa_topp_select(const float* w, const int32_t* row_ptr, const int32_t* col_id
                     "wa_topp_select");
 }
 
+int wa_mask_recall(const float* w, const int32_t* row_ptr, const int32_t* col_idx,
+                   int64_t capacity, int32_t H, int32_t MB, int32_t NB, const uint8_t* mask,
+                   float* recall_out, void* stream) {
+  if (!w || !row_ptr || !col_idx || !mask || !recall_out)
+    return fail(WA_ERR_INVALID_ARG, "null pointer argument");
+  if (H < 1 || MB < 1 || NB < 1) return fail(WA_ERR_INVALID_ARG, "H, MB, NB must be >= 1");
+  if (NB > WA_MAX_BLOCKS) return fail(WA_ERR_UNSUPPORTED, "NB must be <= %d", WA_MAX_BLOCKS);
+  if (capacity < 0) return fail(WA_ERR_INVALID_ARG, "negative capacity");
+  if ((int64_t)H * MB >= ((int64_t)1 << 31)) return fail(WA_ERR_UNSUPPORTED, "too many rows");
+  return hip_status(wa::launch_mask_recall(w, row_ptr, col_idx, capacity, H, MB, NB, mask,
+                                           recall_out, static_cast<hipStream_t>(stream)),
+                    "wa_mask_recall");
+}
+
 static int permute_common(const void* src, void* dst, const int32_t* perm, int32_t H, int32_t MB,
                           int64_t block_bytes, bool scatter, void* stream) {
   if (!src || !dst || !perm) return fail(WA_ERR_INVALID_ARG, "null pointer argument");

@@ -126,7 +126,41 @@ __global__ __launch_bounds__(64) void k_topp(const float* __restrict__ W,
   }
 }
 
+// Attention recall of a mask per query block: one wavefront per CSR row; lanes
+// walk the row's entries 64 apart and add the weight of every entry whose block
+// the mask keeps (in fp64), and a fixed shuffle tree adds the lanes.
+__global__ __launch_bounds__(256) void k_mask_recall(const float* __restrict__ W,
+                                                     const int32_t* __restrict__ row_ptr,
+                                                     const int32_t* __restrict__ col_idx, int cap,
+                                                     int rows, int NB,
+                                                     const uint8_t* __restrict__ mask,
+                                                     float* __restrict__ out) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const int lo = min(row_ptr[r], cap), hi = min(row_ptr[r + 1], cap);
+  const uint8_t* m = mask + (size_t)r * NB;
+  double acc = 0.0;
+  for (int k = lo + lane; k < hi; k += 64) {
+    const int v = col_idx[k];
+    if ((unsigned)v < (unsigned)NB && m[v] != 0) acc += (double)W[k];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) out[r] = (float)acc;
+}
+
 }  // namespace
+
+hipError_t launch_mask_recall(const float* w, const int32_t* row_ptr, const int32_t* col_idx,
+                              int64_t cap64, int H, int MB, int NB, const uint8_t* mask,
+                              float* out, hipStream_t s) {
+  const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
+  const int rows = H * MB;
+  hipLaunchKernelGGL(k_mask_recall, dim3((rows + 3) / 4), dim3(256), 0, s, w, row_ptr, col_idx,
+                     cap, rows, NB, mask, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_block_importance(const float* g, const float* lse, const int32_t* row_ptr,
                                    int64_t cap64, int H, int MB, int L, int block, float* w,

@@ -36,6 +36,9 @@ int attn_resident_wgs_per_cu(int head_dim, int block);
 
 hipError_t launch_block_importance(const float* g, const float* lse, const int32_t* row_ptr,
                                    int64_t cap, int H, int MB, int L, int block, float* w, hipStream_t s);
+hipError_t launch_mask_recall(const float* w, const int32_t* row_ptr, const int32_t* col_idx,
+                              int64_t cap, int H, int MB, int NB, const uint8_t* mask, float* out,
+                              hipStream_t s);
 hipError_t launch_topp(const float* w, const int32_t* row_ptr, const int32_t* col_idx,
                        int64_t cap, int H,
                        int MB, int NB, double p, uint8_t* mask_out, hipStream_t s);

@@ -112,6 +112,13 @@ class HotPath:
         finally:
             self.gsrs_p = saved
 
+    def importance(self) -> None:
+        """Block weights W of the last attention pass (it must have emitted G)."""
+        lib, s = self.lib, _stream(self.device)
+        _check(lib.wa_block_importance(_ptr(self.g), _ptr(self.lse), _ptr(self.row_ptr), self.cap,
+                                       self.H, self.mb, self.L, self.b, _ptr(self.w), s),
+               "wa_block_importance")
+
     def select(self) -> None:
         lib, s = self.lib, _stream(self.device)
         _check(lib.wa_block_importance(_ptr(self.g), _ptr(self.lse), _ptr(self.row_ptr), self.cap,

@@ -227,6 +227,24 @@ int wa_topp_select(const float* w, const int32_t* row_ptr, const int32_t* col_id
                    uint8_t* mask_out, void* stream);
 
 /*
+ * wa_mask_recall - [GSRS §3, attention recall] the share of the attention weight
+ * that a block mask keeps, per query block.  With w the block weights of a pass
+ * over the evaluated blocks (wa_block_importance after a wa_sparse_attn_fwd with
+ * g, e.g. over all blocks for the full attention), recall[h][u] is the sum of
+ * w[e] over the CSR entries e = (h, u, v) whose block v the mask keeps: the mean,
+ * over the valid rows of u, of the attention those rows put on the kept blocks.
+ * The sum runs in fp64 in a fixed order.  A row with no entries gets 0.
+ *   w          float [capacity], row_ptr int32 [H*MB+1], col_idx int32 [capacity]:
+ *              the index and weights of the evaluated pass
+ *   mask       uint8 [H][MB][NB], non-zero = kept
+ *   recall_out float [H][MB] out
+ * Errors: WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED (NB > WA_MAX_BLOCKS), WA_ERR_HIP.
+ */
+int wa_mask_recall(const float* w, const int32_t* row_ptr, const int32_t* col_idx,
+                   int64_t capacity, int32_t H, int32_t MB, int32_t NB, const uint8_t* mask,
+                   float* recall_out, void* stream);
+
+/*
  * wa_gather_blocks / wa_scatter_blocks - [WA §V] explicit reorder operators.
  * Row blocks of block_bytes bytes: gather dst[h][s] = src[h][perm[h][s]];
  * scatter dst[h][perm[h][s]] = src[h][s].  Used for Q blocks, mask rows, O and

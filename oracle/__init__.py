@@ -45,6 +45,7 @@ from .reorder import (  # noqa: F401
 from .gsrs import (  # noqa: F401
     block_importance,
     block_importance_from_probs,
+    mask_recall,
     block_lse,
     cached_lse_scores,
     topp_select,

@@ -160,3 +160,31 @@ def topp_select(w: np.ndarray, row_ptr: np.ndarray, col_idx: np.ndarray, heads: 
                 out[h, u, cand[j]] = 1
                 acc += float(ww[j])
     return out
+
+
+def mask_recall(q: np.ndarray, k: np.ndarray, mask: np.ndarray, seq_len: int, block: int,
+                scale: float) -> np.ndarray:
+    """GSRS §3 attention recall of a block mask, per query block [H, MB].
+
+    The share of the full attention A = softmax(scale * q k^T) (over all keys below
+    seq_len) that falls on the key blocks the mask keeps, averaged over the valid
+    rows of each query block.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    H, lp, _ = q.shape
+    mb = lp // block
+    out = np.zeros((H, mb))
+    for h in range(H):
+        z = scale * (q[h, :seq_len] @ k[h, :seq_len].T)
+        z = z - z.max(axis=1, keepdims=True)
+        a = np.exp(z)
+        a = a / a.sum(axis=1, keepdims=True)
+        for u in range(mb):
+            r0, r1 = u * block, min((u + 1) * block, seq_len)
+            kept = [v for v in range(mb) if mask[h, u, v]]
+            if r1 <= r0 or not kept:
+                continue
+            keys = np.concatenate([_valid_keys(v, seq_len, block) for v in kept])
+            out[h, u] = a[r0:r1][:, keys].sum() / (r1 - r0)
+    return out

@@ -55,6 +55,9 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert lib.wa_topp_select(fake, fake, fake, 4, 1, 1, 1, 1.5, fake, None) == -1
     assert lib.wa_topp_select(fake, fake, fake, 4, 1, 1, 5000, 0.5, fake, None) == -2
     assert lib.wa_topp_select(fake, fake, fake, -1, 1, 1, 1, 0.5, fake, None) == -1
+    assert lib.wa_mask_recall(None, fake, fake, 4, 1, 1, 1, fake, fake, None) == -1
+    assert lib.wa_mask_recall(fake, fake, fake, 4, 1, 1, 5000, fake, fake, None) == -2
+    assert lib.wa_mask_recall(fake, fake, fake, -1, 1, 1, 1, fake, fake, None) == -1
     p = caq.ReorderParams(wave=0)._c()
     assert lib.wa_reorder_rows(fake, fake, fake, fake, 16, fake, 1, 4, 4, 128, 128,
                                ctypes.byref(p), fake, fake, fake, None, None, None) == -1

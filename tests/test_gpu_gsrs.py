@@ -209,3 +209,29 @@ def test_gsrs_schedule_reduced_search_and_mask_reuse():
     o, lse, _ = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx)
     torch.cuda.synchronize()
     assert torch.equal(o, gs.sparse.o) and torch.equal(lse, gs.sparse.lse)
+
+
+@pytest.mark.parametrize("case", ["ragged128", "ragged64"])
+def test_mask_recall_matches_oracle(case):
+    """Recall of a mask from the block weights of a full pass, against the full softmax."""
+    dev = gpu()
+    if case == "ragged128":
+        w = synth.random_tiny_case(31, heads=2, seq_len=1000, head_dim=128, block=128,
+                                   density=0.4)
+    else:
+        w = synth.random_tiny_case(32, heads=2, seq_len=700, head_dim=64, block=64, density=0.3)
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    banner(f"mask recall {case}")
+    q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+    ones = torch.ones(H, mb, mb, dtype=torch.uint8, device=dev)
+    idx = caq.build_block_index(ones)
+    _, lse, g = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx,
+                                    with_g=True)
+    wts = caq.block_importance(g, lse, idx.row_ptr, w.seq_len, w.block)
+    rec = caq.mask_recall(wts, idx.row_ptr, idx.col_idx, w.mask.to(dev))
+    rec_all = caq.mask_recall(wts, idx.row_ptr, idx.col_idx, ones)
+    torch.cuda.synchronize()
+    ref = oracle.mask_recall(np64(w.q), np64(w.k), w.mask.cpu().numpy(), w.seq_len, w.block,
+                             w.scale)
+    np.testing.assert_allclose(rec.cpu().numpy(), ref, rtol=0, atol=2e-4)
+    np.testing.assert_allclose(rec_all.cpu().numpy(), 1.0, rtol=0, atol=2e-4)

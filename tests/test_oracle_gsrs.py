@@ -152,3 +152,40 @@ def test_topp_extremes(p):
     w = np.array([0.1, 0.6, 0.3], dtype=np.float32)
     got = _one_row(w, p)
     assert got == ({1} if p == 0.0 else {0, 1, 2})
+
+
+def _dense_recall(q, k, mask, L, b, s):
+    """Recall from the whole L x L attention matrix and the element mask it expands to."""
+    H, lp, _ = q.shape
+    nb = lp // b
+    out = np.zeros((H, nb))
+    for h in range(H):
+        z = s * np.einsum("id,jd->ij", q[h, :L], k[h, :L])
+        a = np.exp(z - logsumexp(z, axis=1, keepdims=True))
+        m = np.kron(mask[h], np.ones((b, b)))[:L, :L]
+        per_row = (a * m).sum(axis=1)
+        for u in range(nb):
+            out[h, u] = per_row[u * b:min((u + 1) * b, L)].mean()
+    return out
+
+
+def test_mask_recall_definition_and_identities():
+    q, k, mask, L, b, s = _case(6, L=230, empty=(1,))
+    H, nb = mask.shape[0], mask.shape[1]
+    rec = oracle.mask_recall(q, k, mask, L, b, s)
+    np.testing.assert_allclose(rec, _dense_recall(q, k, mask, L, b, s), rtol=0, atol=1e-13)
+    ones = np.ones_like(mask)
+    np.testing.assert_allclose(oracle.mask_recall(q, k, ones, L, b, s), 1.0, rtol=0, atol=1e-12)
+    assert np.all(oracle.mask_recall(q, k, np.zeros_like(mask), L, b, s) == 0.0)
+    # additive over disjoint masks
+    other = (ones - mask).astype(np.uint8)
+    tot = rec + oracle.mask_recall(q, k, other, L, b, s)
+    np.testing.assert_allclose(tot, 1.0, rtol=0, atol=1e-12)
+    # equals the sum of the full pass's block weights over the kept blocks (GSRS eq. (5))
+    rp, ci, _, _, _ = oracle.block_index(ones)
+    wfull = oracle.block_importance_from_probs(q, k, rp, ci, L, b, s)
+    for h in range(H):
+        for u in range(nb):
+            lo = rp[h * nb + u]
+            kept = sum(wfull[lo + v] for v in range(nb) if mask[h, u, v])
+            assert abs(kept - rec[h, u]) < 1e-12
