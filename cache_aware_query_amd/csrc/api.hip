@@ -123,11 +123,12 @@ int wa_sparse_attn_workspace_size(int32_t H, int32_t L, int32_t head_dim, int32_
   return ok();
 }
 
-int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
-                       int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
-                       const int32_t* col_idx, int64_t capacity, const int32_t* perm,
-                       int32_t schedule, float scale, wa_bf16* o, float* lse, float* g,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+static int sparse_attn_common(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
+                              int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
+                              const int32_t* col_idx, int64_t capacity, const int32_t* perm,
+                              int32_t schedule, float scale, wa_bf16* o, float* lse, float* g,
+                              float* entropy, void* workspace, size_t workspace_bytes,
+                              void* stream, const char* name) {
   if (!q || !k || !v || !row_ptr || !col_idx || !o || !lse)
     return fail(WA_ERR_INVALID_ARG, "null pointer argument");
   if (H < 1 || L < 1) return fail(WA_ERR_INVALID_ARG, "H and L must be >= 1");
@@ -151,9 +152,31 @@ int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int
     return fail(WA_ERR_CAPACITY, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
   return hip_status(wa::launch_sparse_attn(q, k, v, H, L, head_dim, block, row_ptr, col_idx,
                                            capacity, perm,
-                                           schedule, scale, o, lse, g, workspace,
+                                           schedule, scale, o, lse, g, entropy, workspace,
                                            static_cast<hipStream_t>(stream)),
-                    "wa_sparse_attn_fwd");
+                    name);
+}
+
+int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
+                       int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
+                       const int32_t* col_idx, int64_t capacity, const int32_t* perm,
+                       int32_t schedule, float scale, wa_bf16* o, float* lse, float* g,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_attn_common(q, k, v, H, L, head_dim, block, row_ptr, col_idx, capacity, perm,
+                            schedule, scale, o, lse, g, nullptr, workspace, workspace_bytes,
+                            stream, "wa_sparse_attn_fwd");
+}
+
+int wa_sparse_attn_fwd_entropy(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
+                               int32_t L, int32_t head_dim, int32_t block,
+                               const int32_t* row_ptr, const int32_t* col_idx, int64_t capacity,
+                               const int32_t* perm, int32_t schedule, float scale, wa_bf16* o,
+                               float* lse, float* g, float* entropy, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!entropy) return fail(WA_ERR_INVALID_ARG, "null pointer argument");
+  return sparse_attn_common(q, k, v, H, L, head_dim, block, row_ptr, col_idx, capacity, perm,
+                            schedule, scale, o, lse, g, entropy, workspace, workspace_bytes,
+                            stream, "wa_sparse_attn_fwd_entropy");
 }
 
 int wa_block_importance(const float* g, const float* lse, const int32_t* row_ptr,

@@ -30,8 +30,8 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
                               int L, int head_dim, int block, const int32_t* row_ptr,
                               const int32_t* col_idx, int64_t cap, const int32_t* perm,
                               int schedule,
-                              float scale, uint16_t* o, float* lse, float* g, void* workspace,
-                              hipStream_t s);
+                              float scale, uint16_t* o, float* lse, float* g, float* ent,
+                              void* workspace, hipStream_t s);
 int attn_resident_wgs_per_cu(int head_dim, int block);
 
 hipError_t launch_block_importance(const float* g, const float* lse, const int32_t* row_ptr,

@@ -111,3 +111,31 @@ def test_fully_masked_block_gives_zero_and_neg_inf():
     assert torch.all(o[0, 7 * b:8 * b] == 0)
     assert torch.all(torch.isneginf(lse[0, 7 * b:8 * b]))
     assert torch.all(torch.isfinite(lse[0, :7 * b]))
+
+
+@pytest.mark.parametrize("with_g", [False, True])
+@pytest.mark.parametrize("shape", [(128, 128), (64, 64)])
+def test_entropy_matches_oracle(shape, with_g):
+    """Row entropy from the same pass (LSE - E[z]) against the explicit softmax entropy;
+    O and LSE are unchanged by asking for it."""
+    d, b = shape
+    dev = gpu()
+    w = synth.random_tiny_case(41 + d, heads=2, seq_len=900, head_dim=d, block=b, density=0.4,
+                               empty_rows=(2,))
+    banner(f"attention entropy d={d} b={b} with_g={with_g}")
+    q, k, v, mask = (t.to(dev) for t in (w.q, w.k, w.v, w.mask))
+    idx = caq.build_block_index(mask)
+    ent = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    o, lse, _ = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx,
+                                    with_g=with_g, entropy_out=ent)
+    o2, lse2, _ = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx,
+                                      with_g=with_g)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    L = w.seq_len
+    ref = oracle.attention_entropy(np64(w.q), np64(w.k), w.mask.cpu().numpy(), L, w.block,
+                                   w.scale)
+    got = ent.cpu().numpy().astype(np.float64)[:, :L]
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, ref[:, :L], rtol=0, atol=2e-2)
+    assert np.all(got[:, 2 * b:3 * b] == 0.0)   # the fully masked query block

@@ -147,3 +147,41 @@ def test_rows_subset_matches_full():
     o2, l2 = oracle.masked_attention_rows(q[0], k[0], v[0], mask[0], rows, L, b, 0.4)
     np.testing.assert_allclose(o2, o[0, rows], rtol=0, atol=1e-14)
     np.testing.assert_allclose(l2, lse[0, rows], rtol=0, atol=1e-14)
+
+
+def test_entropy_closed_forms_and_scipy():
+    from scipy.stats import entropy as sp_entropy
+
+    H, L, d, b = 1, 150, 8, 32
+    nb = -(-L // b)
+    lp = nb * b
+    mask = np.ones((H, nb, nb), dtype=np.uint8)
+    mask[0, 1] = 0                       # an empty row block
+    mask[0, 2] = 0
+    mask[0, 2, 4] = 1                    # the last, ragged block alone: 150 - 128 = 22 keys
+    # Zero queries: uniform attention over the allowed keys, entropy ln(#keys).
+    q0 = np.zeros((H, lp, d))
+    k = np.zeros((H, lp, d))
+    k[:, :L] = _rand((H, L, d), 7)
+    ent = oracle.attention_entropy(q0, k, mask, L, b, 1.0)
+    assert np.allclose(ent[0, :b], math.log(L), atol=1e-12)
+    assert np.all(ent[0, b:2 * b] == 0.0)
+    assert np.allclose(ent[0, 2 * b:3 * b], math.log(L - 4 * b), atol=1e-12)
+    assert np.all(np.isnan(ent[0, L:]))
+    # Random queries: scipy's entropy of the explicit probabilities.
+    q = np.zeros((H, lp, d))
+    q[:, :L] = _rand((H, L, d), 8)
+    s = 1.0 / math.sqrt(d)
+    ent = oracle.attention_entropy(q, k, mask, L, b, s)
+    for i in (0, 5, 31, 70, 100, 149):
+        u = i // b
+        keys = [j for j in range(L) if mask[0, u, j // b]]
+        if not keys:
+            continue
+        z = s * np.array([q[0, i] @ k[0, j] for j in keys])
+        p = np.exp(z - logsumexp(z))
+        assert abs(ent[0, i] - sp_entropy(p)) < 1e-12
+    # A dominant key drives the entropy to zero.
+    qd = q.copy()
+    qd[0, 0] = 200.0 * k[0, 3]
+    assert oracle.attention_entropy(qd, k, mask, L, b, s)[0, 0] < 1e-6
