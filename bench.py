@@ -41,7 +41,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_wan75k_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "cache_aware_query_amd", "csrc", "attention.hip")
 
 
@@ -55,13 +55,13 @@ def _kernel_hash() -> str:
 
 
 def _counter_profile(workload: str):
-    """Figures of the committed counter summary (HBM bytes, L2 hits) if it was taken
-    on the current attention kernel source and this workload; otherwise an empty
-    dict."""
-    if workload != "wan75k" or not os.path.exists(TRAFFIC_FILE):
+    """Figures of the committed counter summary of this workload (HBM bytes, L2 hits)
+    if it was taken on the current attention kernel source; otherwise an empty dict."""
+    path = os.path.join(PROFILES, f"attn_{workload}_traffic.txt")
+    if not os.path.exists(path):
         return {}
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if "=" in line and not line.startswith("#"):
                 a, b = line.split("=", 1)
