@@ -92,3 +92,33 @@ def test_full_size_gsrs_dense_pass_sampled():
             np.testing.assert_allclose(g_gpu, g_ref[:, :nrows], atol=5e-3, rtol=0)
             np.testing.assert_allclose(wts[lo:lo + mb], w_ref, atol=2e-4, rtol=1e-3)
             banner(f"gsrs75k h={h} u={u} kept {int(sel[h, u].sum())} of {mb}")
+
+
+def test_more_blocks_than_the_staged_list_cap():
+    """2,100 query blocks (block 64): the attention kernel reads its lists from global
+    memory, the reorder gathers through the transposed lists and sorts 4,096 keys."""
+    dev = gpu()
+    L, b, d, mb = 2100 * 64, 64, 64, 2100
+    banner(f"large MB: L={L} b={b} d={d} MB={mb}")
+    w = synth.random_tiny_case(71, heads=1, seq_len=L, head_dim=d, block=b, density=0.002,
+                               empty_rows=(5,))
+    assert mb == w.mask.shape[1] and caq.reorder_needs_csc(mb, mb)
+    q, k, v, mask, x0 = (t.to(dev) for t in (w.q, w.k, w.v, w.mask, w.x0))
+    idx = caq.build_block_index(mask)
+    params = caq.ReorderParams(wave=64, n_slices=8, iters=5, skip_mode=caq.WA_SKIP_NEVER)
+    ro = caq.reorder_rows(idx, x0, b, d, params)
+    o, lse, _ = caq.sparse_attn_fwd(q, k, v, L, b, idx.row_ptr, idx.col_idx, perm=ro.perm)
+    o_id, lse_id, _ = caq.sparse_attn_fwd(q, k, v, L, b, idx.row_ptr, idx.col_idx)
+    torch.cuda.synchronize()
+    perm = ro.perm.cpu().numpy()[0]
+    assert sorted(perm.tolist()) == list(range(mb))
+    assert torch.equal(o, o_id) and torch.equal(lse, lse_id)
+    # sampled rows against the oracle (the empty block 5 included)
+    qn, kn, vn = np64(w.q)[0], np64(w.k)[0], np64(w.v)[0]
+    m = w.mask.cpu().numpy()[0]
+    rng = np.random.default_rng(3)
+    for u in sorted(set([0, 5, mb - 1] + rng.choice(mb, size=6, replace=False).tolist())):
+        rows = np.arange(u * b, min((u + 1) * b, L))[::9]
+        o_ref, l_ref = oracle.masked_attention_rows(qn, kn, vn, m, rows, L, b, w.scale)
+        assert_attention_close(np64(o[0, rows]), lse[0, rows].cpu().numpy().astype(np.float64),
+                               o_ref, l_ref, f"row block {u}")
