@@ -80,12 +80,18 @@ def test_reorder_matches_oracle(name, over, params):
     _compare_with_oracle(w, params)
 
 
-def test_reorder_from_transposed_lists_matches_oracle():
+@pytest.mark.parametrize("mb,density", [
+    (760, 0.01),   # short lists: one lane per list, pair statistics by merging lists
+    (760, 0.05),   # four lanes per list
+    (760, 0.3),    # four lanes per list, pair statistics walked row by row per wave
+    (2100, 0.05),  # 2,100 blocks, 4,096-key sorts, statistics per wave
+])
+def test_reorder_from_transposed_lists_matches_oracle(mb, density):
     """A mask too large for the LDS bitmasks takes the CSR + CSC gather form."""
-    w = synth.random_tiny_case(5, heads=2, seq_len=760 * 64, head_dim=64, block=64,
-                               density=0.05)
-    assert caq.reorder_needs_csc(760, 760)
-    banner("reorder 760 x 760 (CSC form)")
+    w = synth.random_tiny_case(5, heads=2, seq_len=mb * 64, head_dim=64, block=64,
+                               density=density, empty_rows=(3,))
+    assert caq.reorder_needs_csc(mb, mb)
+    banner(f"reorder {mb} x {mb} (CSC form) rho={density}")
     _compare_with_oracle(w, caq.ReorderParams(wave=64, n_slices=8,
                                               skip_mode=caq.WA_SKIP_NEVER))
 
