@@ -26,7 +26,8 @@ unpinned (near-ties of fp64 angles may order differently); what is pinned is
 listed in each module.
 """
 
-from .attention import attention_entropy, masked_attention, masked_attention_rows  # noqa: F401
+from .attention import (attention_distance, attention_entropy, masked_attention,  # noqa: F401
+                        masked_attention_rows)
 from .block_index import block_index  # noqa: F401
 from .reorder import (  # noqa: F401
     ReorderParams,

@@ -91,3 +91,31 @@ def attention_entropy(q: np.ndarray, k: np.ndarray, mask: np.ndarray, seq_len: i
                 terms = np.where(a > 0, a * np.log(a), 0.0)
             out[h, r0:r1] = -terms.sum(axis=1)
     return out
+
+
+def attention_distance(q: np.ndarray, k: np.ndarray, mask: np.ndarray, seq_len: int, block: int,
+                       scale: float) -> np.ndarray:
+    """Mean attention distance of each row, D(i) = sum_j A_ij |i - j| over the row's
+    allowed keys, with i and j token positions in the stored sequence order (GSRS §4,
+    Fig. 1, and the appendix on fused attention statistics), [H, L_pad]; 0 for a row
+    with no allowed key, NaN on padding rows."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    H, lp, _ = q.shape
+    out = np.full((H, lp), np.nan)
+    for h in range(H):
+        for u in range(lp // block):
+            r0, r1 = u * block, min((u + 1) * block, seq_len)
+            if r1 <= r0:
+                continue
+            keys = _keys_of_row(mask[h, u], seq_len, block)
+            if keys.size == 0:
+                out[h, r0:r1] = 0.0
+                continue
+            z = scale * (q[h, r0:r1] @ k[h, keys].T)
+            z = z - z.max(axis=1, keepdims=True)
+            a = np.exp(z)
+            a = a / a.sum(axis=1, keepdims=True)
+            dist = np.abs(np.arange(r0, r1)[:, None] - keys[None, :]).astype(np.float64)
+            out[h, r0:r1] = (a * dist).sum(axis=1)
+    return out

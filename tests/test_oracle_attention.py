@@ -185,3 +185,43 @@ def test_entropy_closed_forms_and_scipy():
     qd = q.copy()
     qd[0, 0] = 200.0 * k[0, 3]
     assert oracle.attention_entropy(qd, k, mask, L, b, s)[0, 0] < 1e-6
+
+
+def test_distance_closed_forms_and_brute_force():
+    H, L, d, b = 1, 150, 8, 32
+    nb = -(-L // b)
+    lp = nb * b
+    mask = np.ones((H, nb, nb), dtype=np.uint8)
+    mask[0, 1] = 0                       # an empty row block
+    mask[0, 2] = 0
+    mask[0, 2, 4] = 1                    # keys 128..149 only: all to the right of rows 64..95
+    q0 = np.zeros((H, lp, d))
+    k = np.zeros((H, lp, d))
+    k[:, :L] = _rand((H, L, d), 9)
+    dist = oracle.attention_distance(q0, k, mask, L, b, 1.0)
+    # Uniform weights over all L keys: the mean of |i - j| over j, summed as two series.
+    for i in range(b):
+        assert abs(dist[0, i] - (i * (i + 1) / 2 + (L - 1 - i) * (L - i) / 2) / L) < 1e-10
+    assert np.all(dist[0, b:2 * b] == 0.0)
+    for i in range(2 * b, 3 * b):
+        assert abs(dist[0, i] - ((128 + 149) / 2 - i)) < 1e-10
+    assert np.all(np.isnan(dist[0, L:]))
+    # Random queries: explicit weights and distances, one key at a time.
+    q = np.zeros((H, lp, d))
+    q[:, :L] = _rand((H, L, d), 10)
+    s = 1.0 / math.sqrt(d)
+    dist = oracle.attention_distance(q, k, mask, L, b, s)
+    for i in (0, 5, 31, 70, 100, 149):
+        keys = [j for j in range(L) if mask[0, i // b, j // b]]
+        if not keys:
+            continue
+        z = [s * sum(q[0, i, c] * k[0, j, c] for c in range(d)) for j in keys]
+        zm = max(z)
+        w = [math.exp(x - zm) for x in z]
+        tot = sum(w)
+        ref = sum(wj / tot * abs(i - j) for wj, j in zip(w, keys))
+        assert abs(dist[0, i] - ref) < 1e-9
+    # A dominant key: the distance tends to |i - j*|.
+    qd = q.copy()
+    qd[0, 7] = 200.0 * k[0, 120]
+    assert abs(oracle.attention_distance(qd, k, mask, L, b, s)[0, 7] - 113.0) < 1e-6
