@@ -31,7 +31,7 @@ WA_SKIP_ALWAYS = 2
 EXPORTED = (
     "wa_abi_version", "wa_last_error", "wa_schedule_info", "wa_build_block_index",
     "wa_reorder_rows", "wa_reorder_needs_csc", "wa_sparse_attn_workspace_size",
-    "wa_sparse_attn_fwd", "wa_sparse_attn_fwd_entropy",
+    "wa_sparse_attn_fwd", "wa_sparse_attn_fwd_diag",
     "wa_block_importance", "wa_topp_select", "wa_mask_recall", "wa_gather_blocks",
     "wa_scatter_blocks",
 )
@@ -115,9 +115,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "wa_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _I64, _P,
                                               _I32, ctypes.c_float, _P, _P, _P, _P,
                                               ctypes.c_size_t, _P]),
-        "wa_sparse_attn_fwd_entropy": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P,
-                                                      _I64, _P, _I32, ctypes.c_float, _P, _P, _P,
-                                                      _P, _P, ctypes.c_size_t, _P]),
+        "wa_sparse_attn_fwd_diag": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P,
+                                                   _I64, _P, _I32, ctypes.c_float, _P, _P, _P,
+                                                   _P, _P, _P, ctypes.c_size_t, _P]),
         "wa_block_importance": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P,
                                                _P]),
         "wa_topp_select": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, ctypes.c_double,
@@ -264,13 +264,15 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len: 
                     perm: torch.Tensor | None = None, schedule: int = WA_SCHED_XCD_SLICED,
                     scale: float | None = None, with_g: bool = False,
                     out: tuple | None = None, workspace: torch.Tensor | None = None,
-                    entropy_out: torch.Tensor | None = None):
+                    entropy_out: torch.Tensor | None = None,
+                    distance_out: torch.Tensor | None = None):
     """Block-sparse attention forward.  Returns (O bf16, LSE fp32, G fp32 or None).
 
     ``out`` may hold preallocated (O, LSE, G) tensors and ``workspace`` a uint8
     buffer of sparse_attn_workspace_size bytes, so that repeated calls allocate
-    nothing.  With ``entropy_out`` (float [H, L_pad]) the same pass also writes each
-    row's attention entropy (wa_sparse_attn_fwd_entropy).
+    nothing.  With ``entropy_out`` and/or ``distance_out`` (float [H, L_pad]) the same
+    pass also writes each row's attention entropy and mean attention distance in
+    tokens (wa_sparse_attn_fwd_diag).
     """
     lib = load_library()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -306,14 +308,17 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len: 
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     cap = col_idx.numel() if g is None else min(col_idx.numel(), g.shape[0])
-    if entropy_out is not None:
-        _need(entropy_out, torch.float32, "entropy_out", 2)
-        if tuple(entropy_out.shape) != (H, lp):
-            raise ValueError("entropy_out must be [H, L_pad]")
-        _check(lib.wa_sparse_attn_fwd_entropy(
+    if entropy_out is not None or distance_out is not None:
+        for t, n in ((entropy_out, "entropy_out"), (distance_out, "distance_out")):
+            if t is not None:
+                _need(t, torch.float32, n, 2)
+                if tuple(t.shape) != (H, lp):
+                    raise ValueError(f"{n} must be [H, L_pad]")
+        _check(lib.wa_sparse_attn_fwd_diag(
             _ptr(q), _ptr(k), _ptr(v), H, seq_len, d, block, _ptr(row_ptr), _ptr(col_idx), cap,
             _ptr(perm), schedule, scale, _ptr(o), _ptr(lse), _ptr(g), _ptr(entropy_out),
-            _ptr(workspace), workspace.numel(), _stream(dev)), "wa_sparse_attn_fwd_entropy")
+            _ptr(distance_out), _ptr(workspace), workspace.numel(), _stream(dev)),
+            "wa_sparse_attn_fwd_diag")
         return o, lse, g
     _check(lib.wa_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), H, seq_len, d, block,
                                   _ptr(row_ptr), _ptr(col_idx), cap, _ptr(perm), schedule, scale,

@@ -36,7 +36,7 @@ bool supported_shape(int head_dim, int block) {
 
 extern "C" {
 
-int wa_abi_version(void) { return 1; }
+int wa_abi_version(void) { return 2; }
 
 const char* wa_last_error(void) { return g_err; }
 
@@ -127,8 +127,8 @@ static int sparse_attn_common(const wa_bf16* q, const wa_bf16* k, const wa_bf16*
                               int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
                               const int32_t* col_idx, int64_t capacity, const int32_t* perm,
                               int32_t schedule, float scale, wa_bf16* o, float* lse, float* g,
-                              float* entropy, void* workspace, size_t workspace_bytes,
-                              void* stream, const char* name) {
+                              float* entropy, float* distance, void* workspace,
+                              size_t workspace_bytes, void* stream, const char* name) {
   if (!q || !k || !v || !row_ptr || !col_idx || !o || !lse)
     return fail(WA_ERR_INVALID_ARG, "null pointer argument");
   if (H < 1 || L < 1) return fail(WA_ERR_INVALID_ARG, "H and L must be >= 1");
@@ -152,7 +152,8 @@ static int sparse_attn_common(const wa_bf16* q, const wa_bf16* k, const wa_bf16*
     return fail(WA_ERR_CAPACITY, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
   return hip_status(wa::launch_sparse_attn(q, k, v, H, L, head_dim, block, row_ptr, col_idx,
                                            capacity, perm,
-                                           schedule, scale, o, lse, g, entropy, workspace,
+                                           schedule, scale, o, lse, g, entropy, distance,
+                                           workspace,
                                            static_cast<hipStream_t>(stream)),
                     name);
 }
@@ -163,20 +164,21 @@ int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int
                        int32_t schedule, float scale, wa_bf16* o, float* lse, float* g,
                        void* workspace, size_t workspace_bytes, void* stream) {
   return sparse_attn_common(q, k, v, H, L, head_dim, block, row_ptr, col_idx, capacity, perm,
-                            schedule, scale, o, lse, g, nullptr, workspace, workspace_bytes,
-                            stream, "wa_sparse_attn_fwd");
+                            schedule, scale, o, lse, g, nullptr, nullptr, workspace,
+                            workspace_bytes, stream, "wa_sparse_attn_fwd");
 }
 
-int wa_sparse_attn_fwd_entropy(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
-                               int32_t L, int32_t head_dim, int32_t block,
-                               const int32_t* row_ptr, const int32_t* col_idx, int64_t capacity,
-                               const int32_t* perm, int32_t schedule, float scale, wa_bf16* o,
-                               float* lse, float* g, float* entropy, void* workspace,
-                               size_t workspace_bytes, void* stream) {
-  if (!entropy) return fail(WA_ERR_INVALID_ARG, "null pointer argument");
+int wa_sparse_attn_fwd_diag(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
+                            int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
+                            const int32_t* col_idx, int64_t capacity, const int32_t* perm,
+                            int32_t schedule, float scale, wa_bf16* o, float* lse, float* g,
+                            float* entropy, float* distance, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!entropy && !distance)
+    return fail(WA_ERR_INVALID_ARG, "entropy and distance are both null");
   return sparse_attn_common(q, k, v, H, L, head_dim, block, row_ptr, col_idx, capacity, perm,
-                            schedule, scale, o, lse, g, entropy, workspace, workspace_bytes,
-                            stream, "wa_sparse_attn_fwd_entropy");
+                            schedule, scale, o, lse, g, entropy, distance, workspace,
+                            workspace_bytes, stream, "wa_sparse_attn_fwd_diag");
 }
 
 int wa_block_importance(const float* g, const float* lse, const int32_t* row_ptr,

@@ -171,14 +171,14 @@ struct QuarterDecision {
   bool low;     // the quarter keeps its own maximum as offset (block LSE precision)
 };
 
-template <int BLOCK, int D, bool WITH_G, bool STAGED, bool WITH_ENT>
+template <int BLOCK, int D, bool WITH_G, bool STAGED, bool DIAG>
 __global__ __launch_bounds__(BLOCK * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, int H, int L, int MB,
                    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                    int cap, const int32_t* __restrict__ perm, int schedule, float scale_log2,
                    uint16_t* __restrict__ O, float* __restrict__ lse, float* __restrict__ G,
-                   float* __restrict__ ENT) {
+                   float* __restrict__ ENT, float* __restrict__ DIST) {
   using T = Tile<BLOCK, D>;
   // Two K and two V^T half-tile buffers, separate LDS objects so that the compiler
   // can tell the asynchronous copies into one from the reads of another.
@@ -223,7 +223,8 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       *dst = make_uint4(0, 0, 0, 0);
     }
     if (g == 0) lse[(size_t)h * Lp + qrow] = -INFINITY;
-    if (WITH_ENT && g == 0) ENT[(size_t)h * Lp + qrow] = 0.0f;
+    if (DIAG && ENT != nullptr && g == 0) ENT[(size_t)h * Lp + qrow] = 0.0f;
+    if (DIAG && DIST != nullptr && g == 0) DIST[(size_t)h * Lp + qrow] = 0.0f;
     return;
   }
 
@@ -337,7 +338,8 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.0f;
   float m_run = -INFINITY;  // exponent reference (log2 units)
   float l_run = 0.0f;       // this lane's part of the running sum
-  float es_run = 0.0f;      // with ENT: this lane's part of sum p * score, rescaled like l_run
+  float es_run = 0.0f;      // DIAG: this lane's part of sum p * score, rescaled like l_run
+  float ds_run = 0.0f;      // DIAG: this lane's part of sum p * |i - j|, rescaled like l_run
   constexpr int kQ = BLOCK / 32;  // quarters per list tile
   float c_q[kQ], r_q[kQ];         // per-quarter block statistics of the current tile
 #pragma unroll
@@ -406,15 +408,23 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         }
       }
     }
-    if constexpr (WITH_ENT) {
+    if constexpr (DIAG) {
       // Masked keys have p = 0 and score -inf; clamping the score keeps 0 * score = 0.
-      float es = 0.0f;
+      // Key 16*ps + j of the quarter sits at token key0 + 16*ps + j.
+      const int vb = (unsigned)v < (unsigned)MB ? v : 0;
+      const int key0 = vb * BLOCK + 64 * ((q >> 1) % T::kHalves) + 32 * (q & 1) + 8 * g;
+      const float d0 = (float)(qrow - key0);
+      float es = 0.0f, ds = 0.0f;
 #pragma unroll
       for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          es = fmaf((float)pb[ps][j], fmaxf(acc[8 * ps + j], -3.0e38f), es);
+        for (int j = 0; j < 8; ++j) {
+          const float p = (float)pb[ps][j];
+          es = fmaf(p, fmaxf(acc[8 * ps + j], -3.0e38f), es);
+          ds = fmaf(p, fabsf(d0 - (float)(16 * ps + j)), ds);
+        }
       es_run = es_run * d.alpha + es;
+      ds_run = ds_run * d.alpha + ds;
     }
     l_run = l_run * d.alpha + lsum;
     m_run = d.m_ref;
@@ -549,10 +559,13 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
   const float lse_row = (m_run + __log2f(l_tot)) * kLn2;
   if (g == 0) lse[(size_t)h * Lp + qrow] = lse_row;
-  if constexpr (WITH_ENT) {
-    // Entropy of the row's attention: LSE - E[z] with z = scale * q.k (natural log).
+  if constexpr (DIAG) {
+    // Entropy of the row's attention: LSE - E[z] with z = scale * q.k (natural log);
+    // mean attention distance: E[|i - j|] in tokens.
     const float ez = pair_sum(es_run) * inv_l * (scale_log2 * kLn2);
-    if (g == 0) ENT[(size_t)h * Lp + qrow] = lse_row - ez;
+    const float ed = pair_sum(ds_run) * inv_l;
+    if (ENT != nullptr && g == 0) ENT[(size_t)h * Lp + qrow] = lse_row - ez;
+    if (DIST != nullptr && g == 0) DIST[(size_t)h * Lp + qrow] = ed;
   }
 }
 
@@ -560,18 +573,18 @@ template <int BLOCK, int D>
 hipError_t launch_typed(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H, int L,
                         const int32_t* row_ptr, const int32_t* col_idx, int cap,
                         const int32_t* perm, int schedule, float scale, uint16_t* o, float* lse,
-                        float* g, float* ent, hipStream_t s) {
+                        float* g, float* ent, float* dist, hipStream_t s) {
   const int MB = (L + BLOCK - 1) / BLOCK;
   int grid = H * MB;
   if (schedule == WA_SCHED_XCD_SLICED) grid = H * kXcds * ((MB + kXcds - 1) / kXcds);
   const float sl2 = scale * kLog2e;
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(BLOCK * 2), 0, s, q, k, v, H, L, MB, row_ptr,
-                       col_idx, cap, perm, schedule, sl2, o, lse, g, ent);
+                       col_idx, cap, perm, schedule, sl2, o, lse, g, ent, dist);
   };
   const bool staged = MB <= kListCap;  // NB = MB: every list fits in LDS
-  auto pick = [&](auto with_ent) {
-    constexpr bool E = decltype(with_ent)::value;
+  auto pick = [&](auto diag) {
+    constexpr bool E = decltype(diag)::value;
     if (g != nullptr) {
       if (staged) launch(k_sparse_attn<BLOCK, D, true, true, E>);
       else launch(k_sparse_attn<BLOCK, D, true, false, E>);
@@ -580,7 +593,7 @@ hipError_t launch_typed(const uint16_t* q, const uint16_t* k, const uint16_t* v,
       else launch(k_sparse_attn<BLOCK, D, false, false, E>);
     }
   };
-  if (ent != nullptr) pick(std::true_type());
+  if (ent != nullptr || dist != nullptr) pick(std::true_type());
   else pick(std::false_type());
   return hipGetLastError();
 }
@@ -604,20 +617,20 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
                               int L, int head_dim, int block, const int32_t* row_ptr,
                               const int32_t* col_idx, int64_t cap64, const int32_t* perm,
                               int schedule, float scale, uint16_t* o, float* lse, float* g,
-                              float* ent, void* workspace, hipStream_t s) {
+                              float* ent, float* dist, void* workspace, hipStream_t s) {
   (void)workspace;
   const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
   if (block == 128 && head_dim == 128)
     return launch_typed<128, 128>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o,
-                                  lse, g, ent, s);
+                                  lse, g, ent, dist, s);
   if (block == 128 && head_dim == 64)
     return launch_typed<128, 64>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o,
-                                 lse, g, ent, s);
+                                 lse, g, ent, dist, s);
   if (block == 64 && head_dim == 128)
     return launch_typed<64, 128>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o,
-                                 lse, g, ent, s);
+                                 lse, g, ent, dist, s);
   return launch_typed<64, 64>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o, lse,
-                              g, ent, s);
+                              g, ent, dist, s);
 }
 
 }  // namespace wa

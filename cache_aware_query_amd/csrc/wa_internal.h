@@ -31,6 +31,7 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
                               const int32_t* col_idx, int64_t cap, const int32_t* perm,
                               int schedule,
                               float scale, uint16_t* o, float* lse, float* g, float* ent,
+                              float* dist,
                               void* workspace, hipStream_t s);
 int attn_resident_wgs_per_cu(int head_dim, int block);
 

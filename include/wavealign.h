@@ -197,19 +197,25 @@ int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int
                        size_t workspace_bytes, void* stream);
 
 /*
- * wa_sparse_attn_fwd_entropy - wa_sparse_attn_fwd that also writes each row's
- * attention entropy [GSRS §4, Fig. 1 (attention entropy across denoising steps)]:
- * entropy[h][i] = -sum_j A_ij ln A_ij over the row's attended keys, computed in the
- * same pass as LSE_i - E[z_ij] (E under A, z = scale * q.k).  A row with no keys
- * gets 0.  All other arguments and errors as wa_sparse_attn_fwd.
- *   entropy  float [H][L_pad] out (required)
+ * wa_sparse_attn_fwd_diag - wa_sparse_attn_fwd that also writes per-row attention
+ * statistics from the same pass [GSRS §4, Fig. 1 (attention entropy and mean
+ * attention distance across denoising steps), and its appendix on computing both
+ * inside the attention kernel with two running sums rescaled like the output]:
+ *   entropy[h][i]  = -sum_j A_ij ln A_ij, computed as LSE_i - E[z_ij] (E under A,
+ *                    z = scale * q.k)
+ *   distance[h][i] = sum_j A_ij |i - j|, i and j token positions in the stored order
+ * over the row's attended keys.  A row with no keys gets 0 in both.  Values for rows
+ * >= L are unspecified.  All other arguments and errors as wa_sparse_attn_fwd, plus
+ * WA_ERR_INVALID_ARG when both outputs are NULL.
+ *   entropy   float [H][L_pad] out or NULL
+ *   distance  float [H][L_pad] out or NULL
  */
-int wa_sparse_attn_fwd_entropy(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
-                               int32_t L, int32_t head_dim, int32_t block,
-                               const int32_t* row_ptr, const int32_t* col_idx, int64_t capacity,
-                               const int32_t* perm, int32_t schedule, float scale, wa_bf16* o,
-                               float* lse, float* g, float* entropy, void* workspace,
-                               size_t workspace_bytes, void* stream);
+int wa_sparse_attn_fwd_diag(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
+                            int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
+                            const int32_t* col_idx, int64_t capacity, const int32_t* perm,
+                            int32_t schedule, float scale, wa_bf16* o, float* lse, float* g,
+                            float* entropy, float* distance, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * wa_block_importance - [GSRS §5.3 Phase 2, Appendix A.2] block weights.

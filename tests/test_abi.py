@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.wa_abi_version() == 1
+    assert lib.wa_abi_version() == 2
 
 
 def test_host_validation_rejects_bad_arguments(lib):

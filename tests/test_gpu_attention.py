@@ -113,29 +113,76 @@ def test_fully_masked_block_gives_zero_and_neg_inf():
     assert torch.all(torch.isfinite(lse[0, :7 * b]))
 
 
-@pytest.mark.parametrize("with_g", [False, True])
-@pytest.mark.parametrize("shape", [(128, 128), (64, 64)])
-def test_entropy_matches_oracle(shape, with_g):
-    """Row entropy from the same pass (LSE - E[z]) against the explicit softmax entropy;
-    O and LSE are unchanged by asking for it."""
-    d, b = shape
+def _diag(w, with_g=False):
     dev = gpu()
-    w = synth.random_tiny_case(41 + d, heads=2, seq_len=900, head_dim=d, block=b, density=0.4,
-                               empty_rows=(2,))
-    banner(f"attention entropy d={d} b={b} with_g={with_g}")
     q, k, v, mask = (t.to(dev) for t in (w.q, w.k, w.v, w.mask))
     idx = caq.build_block_index(mask)
     ent = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    dist = torch.empty_like(ent)
     o, lse, _ = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx,
-                                    with_g=with_g, entropy_out=ent)
+                                    with_g=with_g, entropy_out=ent, distance_out=dist)
     o2, lse2, _ = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx,
                                       with_g=with_g)
+    # each output alone equals the same output of the joint call
+    ent1 = torch.empty_like(ent)
+    dist1 = torch.empty_like(ent)
+    caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx, with_g=with_g,
+                        entropy_out=ent1)
+    caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx, with_g=with_g,
+                        distance_out=dist1)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
     L = w.seq_len
-    ref = oracle.attention_entropy(np64(w.q), np64(w.k), w.mask.cpu().numpy(), L, w.block,
-                                   w.scale)
-    got = ent.cpu().numpy().astype(np.float64)[:, :L]
-    assert np.all(np.isfinite(got))
-    np.testing.assert_allclose(got, ref[:, :L], rtol=0, atol=2e-2)
-    assert np.all(got[:, 2 * b:3 * b] == 0.0)   # the fully masked query block
+    assert torch.equal(ent1[:, :L], ent[:, :L]) and torch.equal(dist1[:, :L], dist[:, :L])
+    return (ent.cpu().numpy().astype(np.float64)[:, :L],
+            dist.cpu().numpy().astype(np.float64)[:, :L])
+
+
+@pytest.mark.parametrize("with_g", [False, True])
+@pytest.mark.parametrize("shape", [(128, 128), (64, 64)])
+def test_diagnostics_match_oracle(shape, with_g):
+    """Row entropy (LSE - E[z]) and mean attention distance from the same pass against
+    the explicit softmax statistics; O and LSE are unchanged by asking for them."""
+    d, b = shape
+    w = synth.random_tiny_case(41 + d, heads=2, seq_len=900, head_dim=d, block=b, density=0.4,
+                               empty_rows=(2,))
+    banner(f"attention diagnostics d={d} b={b} with_g={with_g}")
+    ent, dist = _diag(w, with_g)
+    L = w.seq_len
+    m = w.mask.cpu().numpy()
+    ref_e = oracle.attention_entropy(np64(w.q), np64(w.k), m, L, w.block, w.scale)[:, :L]
+    ref_d = oracle.attention_distance(np64(w.q), np64(w.k), m, L, w.block, w.scale)[:, :L]
+    assert np.all(np.isfinite(ent)) and np.all(np.isfinite(dist))
+    np.testing.assert_allclose(ent, ref_e, rtol=0, atol=2e-2)
+    # P is rounded to bf16 (relative error <= 2^-9 per weight) and normalised by the sum
+    # of the rounded weights, so |D~ - D| <= 2^-9 * max_j |j - i| / (1 - 2^-9) < 2^-8 * L.
+    # Independent roundings average out, so the mean error is far smaller; a key index
+    # off by one would move every row by about one token.
+    err = np.abs(dist - ref_d)
+    assert err.max() < 2.0 ** -8 * L, err.max()
+    assert err.mean() < 2.0 ** -4, err.mean()
+    assert np.all(ent[:, 2 * b:3 * b] == 0.0) and np.all(dist[:, 2 * b:3 * b] == 0.0)
+
+
+@pytest.mark.parametrize("shape", [(128, 128), (64, 64)])
+def test_distance_with_uniform_attention(shape):
+    """Zero queries: every allowed key has weight exactly 1 in bf16, so the mean attention
+    distance is the plain mean of |i - j| over the allowed keys (fp32 sums only) and the
+    entropy is ln(#keys)."""
+    d, b = shape
+    w = synth.random_tiny_case(57 + d, heads=2, seq_len=1000, head_dim=d, block=b, density=0.5,
+                               empty_rows=(1,))
+    w.q.zero_()
+    banner(f"attention distance, uniform weights d={d} b={b}")
+    ent, dist = _diag(w)
+    L = w.seq_len
+    m = w.mask.cpu().numpy()
+    for h in range(m.shape[0]):
+        for i in range(L):
+            keys = np.concatenate([np.arange(vb * b, min((vb + 1) * b, L))
+                                   for vb in np.nonzero(m[h, i // b])[0]] or [np.zeros(0, int)])
+            if keys.size == 0:
+                assert dist[h, i] == 0.0 and ent[h, i] == 0.0
+                continue
+            assert abs(dist[h, i] - np.abs(keys - i).mean()) < 1e-2
+            assert abs(ent[h, i] - np.log(keys.size)) < 1e-3
