@@ -166,9 +166,10 @@ struct QuarterDecision {
   float m_ref;  // exponent reference after this quarter
   float c;      // exponent offset used for the probabilities (finite)
   float c_g;    // the same offset as a block statistic (-inf if nothing is valid)
-  float alpha;  // rescale of the previous output and sum
-  bool grow;    // the reference moved
-  bool low;     // the quarter keeps its own maximum as offset (block LSE precision)
+  float alpha;    // rescale of the previous output and sum
+  bool any_grow;  // (wave-uniform) the reference moved on some lane
+  bool any_low;   // (wave-uniform) some lane keeps its quarter maximum as offset (block
+                  // LSE precision); per lane: m_h < m_ref - kLow
 };
 
 template <int BLOCK, int D, bool WITH_G, bool STAGED, bool DIAG>
@@ -341,12 +342,9 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   float es_run = 0.0f;      // DIAG: this lane's part of sum p * score, rescaled like l_run
   float ds_run = 0.0f;      // DIAG: this lane's part of sum p * |i - j|, rescaled like l_run
   constexpr int kQ = BLOCK / 32;  // quarters per list tile
-  float c_q[kQ], r_q[kQ];         // per-quarter block statistics of the current tile
-#pragma unroll
-  for (int i = 0; i < kQ; ++i) {
-    c_q[i] = -INFINITY;
-    r_q[i] = 0.0f;
-  }
+  // Block statistics of the current tile: offset and this lane's part of the sum of
+  // exp2(score - offset); quarters with another offset are rescaled into it.
+  float blk_m = -INFINITY, blk_s = 0.0f;
   float g_pending = 0.0f;  // G of the last finished tile, stored at the next half start
   int e_pending = -1;
 
@@ -357,11 +355,16 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
     QuarterDecision d;
     d.m_h = pair_max(mx) * scale_log2;
-    d.grow = d.m_h > m_run + kTau;
-    d.m_ref = d.grow ? d.m_h : m_run;
-    d.alpha = d.grow ? __builtin_amdgcn_exp2f(m_run - d.m_h) : 1.0f;
-    d.low = WITH_G && d.m_h < d.m_ref - kLow;
-    d.c_g = d.low ? d.m_h : d.m_ref;
+    const bool grow = d.m_h > m_run + kTau;
+    d.any_grow = __builtin_amdgcn_ballot_w64(grow) != 0;
+    d.m_ref = grow ? d.m_h : m_run;
+    d.alpha = 1.0f;
+    if (d.any_grow) {  // rare: only then is an exponential spent on the rescale
+      if (d.m_h > m_run + kTau) d.alpha = __builtin_amdgcn_exp2f(m_run - d.m_h);
+    }
+    const bool low = WITH_G && d.m_h < d.m_ref - kLow;
+    d.any_low = WITH_G && __builtin_amdgcn_ballot_w64(low) != 0;
+    d.c_g = low ? d.m_h : d.m_ref;
     d.c = d.c_g == -INFINITY ? 0.0f : d.c_g;
     return d;
   };
@@ -379,12 +382,10 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     float lsum = psum;
     if constexpr (WITH_G) {
       const int qi = q % kQ;
-      c_q[qi] = d.c_g;
-      r_q[qi] = psum;
-      if (__builtin_amdgcn_ballot_w64(d.low) != 0) {
+      if (d.any_low) {
         // Lanes whose quarter sits far below the reference: their output share uses
         // the common reference (a value 2^-64 below it or smaller).
-        if (d.low) {
+        if (d.m_h < d.m_ref - kLow) {
           const float cr = d.m_ref == -INFINITY ? 0.0f : d.m_ref;
 #pragma unroll
           for (int ps = 0; ps < 2; ++ps)
@@ -394,16 +395,23 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
           lsum = sum8(pb[1], sum8(pb[0], 0.0f));
         }
       }
+      if (qi == 0) {
+        blk_m = d.c_g;
+        blk_s = psum;
+      } else if (__builtin_amdgcn_ballot_w64(d.c_g != blk_m) == 0) {
+        blk_s += psum;  // the usual case: the tile keeps one offset
+      } else {
+        const float nm = fmaxf(blk_m, d.c_g);
+        if (nm != -INFINITY)
+          blk_s = blk_s * __builtin_amdgcn_exp2f(blk_m - nm) +
+                  psum * __builtin_amdgcn_exp2f(d.c_g - nm);
+        blk_m = nm;
+      }
       if (qi == kQ - 1) {
         const int e = e0 + q / kQ;
         if ((unsigned)v < (unsigned)MB) {
-          float M = -INFINITY;
-#pragma unroll
-          for (int i = 0; i < kQ; ++i) M = fmaxf(M, c_q[i]);
-          float sum = 0.0f;
-#pragma unroll
-          for (int i = 0; i < kQ; ++i) sum += pair_sum(r_q[i]) * __builtin_amdgcn_exp2f(c_q[i] - M);
-          g_pending = M == -INFINITY ? -INFINITY : (M + __log2f(sum)) * kLn2;
+          g_pending = blk_m == -INFINITY ? -INFINITY
+                                         : (blk_m + __log2f(pair_sum(blk_s))) * kLn2;
           e_pending = e;
         }
       }
@@ -491,7 +499,7 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     if constexpr (MT == 0) compute_s(acc[1], P ? sk1 : sk0, 1);
     else compute_s(acc[0], P ? sk0 : sk1, 0);
     softmax(acc[MT], dec, id_of_half(hh), q, pb);
-    if (__builtin_amdgcn_ballot_w64(dec.grow) != 0) {
+    if (dec.any_grow) {
 #pragma unroll
       for (int dt = 0; dt < T::kDT; ++dt)
 #pragma unroll
