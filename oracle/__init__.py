@@ -18,6 +18,8 @@ Every function restates a computation from the two source pages:
   log-sum-exp (§3 preliminaries), the two-phase block importance (§5.3,
   Appendix A.2), fully masked rows (note to Algorithm 2) and Top-p selection
   (Algorithm 3).
+* The MinHash row order that WaveAlign's Table II compares against
+  (``comparators``), from the published min-wise hashing it names.
 
 Floating point is fp64 throughout; bf16 inputs are widened exactly.  Where the
 pages leave a step open the reading taken is stated in the function's
@@ -52,3 +54,5 @@ from .gsrs import (  # noqa: F401
     topp_select,
 )
 from .permute import gather_blocks, scatter_blocks  # noqa: F401
+from .comparators import (MINHASH_P, minhash_order, minhash_order_head,  # noqa: F401
+                          minhash_signatures)

@@ -14,6 +14,7 @@ from .workloads import (  # noqa: F401
     drift_states,
     get_config,
     make_workload,
+    minhash_params,
     random_tiny_case,
 )
 from .hilbert import gilbert2d, video_hilbert_order  # noqa: F401

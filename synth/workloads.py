@@ -356,3 +356,15 @@ def drift_states(w: Workload, n_states: int, sigma: float = 0.3, seed: int = BAS
         states.append(tuple((x.float() + a * d).to(torch.bfloat16)
                             for x, d in zip((w.q, w.k, w.v), deltas)))
     return states
+
+
+def minhash_params(n_hash: int = 2, seed: int = BASE_SEED):
+    """Coefficients of n_hash linear hash functions v -> (a v + b) mod (2^31 - 1) for the
+    MinHash comparator order: a in [1, 2^31 - 2], b in [0, 2^31 - 2], drawn from the
+    seed.  Returns two lists of Python ints."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(_seed(seed, 7919, n_hash))
+    p = (1 << 31) - 1
+    a = torch.randint(1, p, (n_hash,), generator=g, dtype=torch.int64).tolist()
+    b = torch.randint(0, p, (n_hash,), generator=g, dtype=torch.int64).tolist()
+    return a, b

@@ -1,0 +1,86 @@
+"""Pins of the MinHash comparator order (oracle/comparators.py) against the
+definition of min-wise hashing: exact values of single-element rows, the subset
+property, identical and empty rows, and the Jaccard estimate it is used for."""
+
+import numpy as np
+
+import oracle
+
+P = (1 << 31) - 1
+
+
+def test_single_element_rows_have_the_hash_value():
+    m = np.zeros((3, 8), dtype=np.uint8)
+    m[0, 7] = 1
+    m[1, 5] = 1
+    sig = oracle.minhash_signatures(m, [48271, (1 << 30) + 3], [11, 1])
+    assert sig[0, 0] == 337908                     # 48271 * 7 + 11
+    assert sig[1, 1] == 1073741842                 # ((2^30 + 3) * 5 + 1) mod (2^31 - 1)
+    assert sig[2, 0] == P and sig[2, 1] == P       # empty row
+    assert oracle.MINHASH_P == P
+
+
+def test_signature_of_a_superset_is_not_larger():
+    rng = np.random.default_rng(1)
+    for _ in range(20):
+        a = rng.random(64) < 0.2
+        b = a | (rng.random(64) < 0.2)
+        m = np.stack([a, b]).astype(np.uint8)
+        ha = rng.integers(1, P, size=4)
+        hb = rng.integers(0, P, size=4)
+        sig = oracle.minhash_signatures(m, ha, hb)
+        if a.any():
+            assert np.all(sig[1] <= sig[0])
+
+
+def test_identical_rows_are_neighbours_and_empty_rows_last():
+    rng = np.random.default_rng(2)
+    m = (rng.random((12, 40)) < 0.25).astype(np.uint8)
+    m[9] = m[2]
+    m[5] = 0
+    perm = oracle.minhash_order_head(m, [1234567, 7654321], [3, 5], wave=4, n_slices=1,
+                                     stage2=False)
+    assert sorted(perm.tolist()) == list(range(12))
+    pos = {int(r): i for i, r in enumerate(perm)}
+    sig = oracle.minhash_signatures(m, [1234567, 7654321], [3, 5])
+    lo, hi = sorted((pos[2], pos[9]))
+    # nothing but rows with the very same signature can sit between two equal rows
+    assert all(np.array_equal(sig[perm[i]], sig[2]) for i in range(lo, hi + 1))
+    assert perm[-1] == 5
+
+
+def test_equal_leading_hash_tracks_jaccard():
+    """Agreement of one hash value estimates the Jaccard similarity.  Linear hashing
+    mod P is only approximately min-wise independent on small integer sets, so the
+    pin allows 0.1 of bias and checks the ordering of two pairs instead of equality."""
+    rng = np.random.default_rng(3)
+    def pair(lo_b, hi_b):
+        a = np.zeros(200, dtype=bool)
+        b = np.zeros(200, dtype=bool)
+        a[:60] = True
+        b[lo_b:hi_b] = True
+        return np.stack([a, b]).astype(np.uint8)
+    n = 3000
+    ha = rng.integers(1, P, size=n)
+    hb = rng.integers(0, P, size=n)
+    fr = []
+    for m, jac in ((pair(30, 100), 0.3), (pair(10, 70), 50 / 70)):
+        sig = oracle.minhash_signatures(m, ha, hb)
+        f = float(np.mean(sig[0] == sig[1]))
+        assert abs(f - jac) < 0.1, (f, jac)
+        fr.append(f)
+    assert fr[1] > fr[0] + 0.25
+
+
+def test_stage2_inside_buckets():
+    rng = np.random.default_rng(4)
+    mask = (rng.random((2, 30, 30)) < 0.3).astype(np.uint8)
+    perm, inv = oracle.minhash_order(mask, [99991, 31337], [7, 8], wave=4, n_slices=2)
+    for h in range(2):
+        assert sorted(perm[h].tolist()) == list(range(30))
+        assert np.array_equal(inv[h][perm[h]], np.arange(30))
+        nnz = mask[h].sum(axis=1)
+        base = oracle.minhash_order_head(mask[h], [99991, 31337], [7, 8], 4, 2, stage2=False)
+        for lo, hi in oracle.wave_buckets(30, 2, 4):
+            assert sorted(perm[h][lo:hi].tolist()) == sorted(base[lo:hi].tolist())
+            assert list(-nnz[perm[h][lo:hi]]) == sorted(-nnz[perm[h][lo:hi]])
