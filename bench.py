@@ -418,6 +418,21 @@ def main():
             hpa.build_index(w.mask)
             hpa.reorder_rows(w.x0)
             ablation[name] = hpa
+        # The MinHash comparator of WaveAlign Table II (min-wise hashing of each row's
+        # K/V block set, rows by signature, then the same Stage 2), every head.
+        hp_mh = HotPath(H, L, d, b, dev, capacity=nnz,
+                        reorder=caq.ReorderParams(wave=wave, n_slices=n_xcd,
+                                                  skip_mode=caq.WA_SKIP_NEVER),
+                        schedule=caq.WA_SCHED_XCD_SLICED, gsrs_p=0.9)
+        hp_mh.build_index(w.mask)
+        mh_a, mh_b = synth.minhash_params(2)
+
+        def minhash():
+            caq.minhash_order(hp_mh.index(), mh_a, mh_b, wave, n_xcd, True,
+                              out=(hp_mh.perm, hp_mh.inv_perm))
+        minhash()
+        t_minhash = _time_calls(minhash, reps)
+        ablation["minhash_order"] = hp_mh
 
         def with_schedule(path, sched):
             def run():
@@ -448,6 +463,8 @@ def main():
                        "gsrs_select_ms": round(t_select, 4),
                        "index_ms_without_reorder": round(t_index_id, 4)})
         detail.update({f"attn_ms_{k}": round(v, 4) for k, v in t.items()})
+        detail["minhash_order_ms"] = round(t_minhash, 4)
+        detail["e2e_ms_minhash"] = round(t_index + t_minhash + t["minhash_order"], 4)
         detail.update({"e2e_ms_reordered": round(e2e_reord, 4),
                        "e2e_ms_unreordered_best": round(e2e_plain, 4),
                        "reorder_speedup_incl_overhead": round(e2e_plain / e2e_reord, 4)})

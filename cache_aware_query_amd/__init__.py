@@ -30,7 +30,7 @@ WA_SKIP_ALWAYS = 2
 
 EXPORTED = (
     "wa_abi_version", "wa_last_error", "wa_schedule_info", "wa_build_block_index",
-    "wa_reorder_rows", "wa_reorder_needs_csc", "wa_sparse_attn_workspace_size",
+    "wa_reorder_rows", "wa_reorder_needs_csc", "wa_minhash_order", "wa_sparse_attn_workspace_size",
     "wa_sparse_attn_fwd", "wa_sparse_attn_fwd_diag",
     "wa_block_importance", "wa_topp_select", "wa_mask_recall", "wa_gather_blocks",
     "wa_scatter_blocks",
@@ -110,6 +110,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                            ctypes.POINTER(_ReorderParams), _P, _P, _P, _P, _P,
                                            _P]),
         "wa_reorder_needs_csc": (ctypes.c_int, [_I32, _I32]),
+        "wa_minhash_order": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _P, _P, _I32, _I32,
+                                            _I32, _I32, _P, _P, _P]),
         "wa_sparse_attn_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32,
                                                          ctypes.POINTER(ctypes.c_size_t)]),
         "wa_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _I64, _P,
@@ -242,6 +244,28 @@ def reorder_rows(index: BlockIndex, x0: torch.Tensor, block: int, head_dim: int,
                                ctypes.byref(cp), _ptr(perm), _ptr(inv), _ptr(skipped),
                                _ptr(angles), _ptr(stats), _stream(dev)), "wa_reorder_rows")
     return Reorder(perm, inv, skipped, angles, stats)
+
+
+def minhash_order(index: BlockIndex, hash_a, hash_b, wave: int, n_slices: int,
+                  stage2: bool = True, out: tuple | None = None):
+    """The MinHash comparator order (wa_minhash_order): returns (perm, inv_perm)."""
+    lib = load_library()
+    H, MB, NB = index.heads, index.mb, index.nb
+    n = len(hash_a)
+    if n != len(hash_b) or n not in (1, 2):
+        raise ValueError("hash_a and hash_b must both hold 1 or 2 coefficients")
+    dev = index.row_ptr.device
+    if out is None:
+        perm = torch.empty(H, MB, dtype=torch.int32, device=dev)
+        inv = torch.empty(H, MB, dtype=torch.int32, device=dev)
+    else:
+        perm, inv = out
+    a = (ctypes.c_uint32 * n)(*[int(x) for x in hash_a])
+    b = (ctypes.c_uint32 * n)(*[int(x) for x in hash_b])
+    _check(lib.wa_minhash_order(_ptr(index.row_ptr), _ptr(index.col_idx), index.col_idx.numel(),
+                                H, MB, NB, a, b, n, wave, n_slices, 1 if stage2 else 0, _ptr(perm),
+                                _ptr(inv), _stream(dev)), "wa_minhash_order")
+    return perm, inv
 
 
 def reorder_needs_csc(mb: int, nb: int) -> bool:

@@ -431,6 +431,37 @@ __device__ void sort_pairs(uint64_t* key, uint32_t* val, int n) {
   __syncthreads();
 }
 
+// Stage 2 (§IV-D) on the Stage-1 order in val[0, MB) (key and val are the sort
+// arrays, n2 >= MB a power of two): inside each wave bucket of each slice, rows by
+// descending NNZ, ties in Stage-1 position; then perm[pos] = row and inv_perm[row] = pos.
+__device__ void stage2_and_write(uint64_t* key, uint32_t* val, int n2, const int32_t* rp, int cap,
+                                 int MB, int NB, int wave, int n_slices, bool stage2,
+                                 int32_t* perm_h, int32_t* inv_h) {
+  const int t = threadIdx.x;
+  if (stage2) {
+    const int s = (MB + n_slices - 1) / n_slices;
+    const int per_slice = (s + wave - 1) / wave;
+    for (int pos = t; pos < n2; pos += kThreads) {
+      if (pos < MB) {
+        const int row = (int)val[pos];
+        const int nnz_row = min(rp[row + 1], cap) - min(rp[row], cap);
+        const int x = pos / s;
+        const int bucket = x * per_slice + (pos - x * s) / wave;
+        key[pos] = ((uint64_t)bucket << 40) | ((uint64_t)(NB - nnz_row) << 20) | (uint64_t)pos;
+      } else {
+        key[pos] = ~0ull;
+        val[pos] = (uint32_t)pos;
+      }
+    }
+    sort_pairs(key, val, n2);
+  }
+  for (int pos = t; pos < MB; pos += kThreads) {
+    const int row = (int)val[pos];
+    perm_h[pos] = row;
+    inv_h[row] = pos;
+  }
+}
+
 // BITS: the head's mask is first expanded into row and column bitmasks in LDS and
 // every product with M or M^T reads those (the CSC is not used); otherwise the
 // products gather through the CSR and CSC lists in global memory.
@@ -696,29 +727,66 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
   }
   // val[pos] is the Stage-1 order.
 
-  // ---- Stage 2: NNZ-descending inside each wave bucket (§IV-D) ----
-  if (p.stage2) {
-    const int s = (MB + p.n_slices - 1) / p.n_slices;
-    const int per_slice = (s + p.wave - 1) / p.wave;
-    for (int pos = t; pos < n2; pos += kThreads) {
-      if (pos < MB) {
-        const int row = (int)val[pos];
-        const int nnz_row = min(rp[row + 1], cap) - min(rp[row], cap);
-        const int x = pos / s;
-        const int bucket = x * per_slice + (pos - x * s) / p.wave;
-        key[pos] = ((uint64_t)bucket << 40) | ((uint64_t)(NB - nnz_row) << 20) | (uint64_t)pos;
-      } else {
-        key[pos] = ~0ull;
-        val[pos] = (uint32_t)pos;
+  stage2_and_write(key, val, n2, rp, cap, MB, NB, p.wave, p.n_slices, p.stage2 != 0, perm_h,
+                   inv_h);
+}
+
+// ---- The MinHash comparator order (WaveAlign Table II) ----
+constexpr uint32_t kMinhashP = 0x7fffffffu;  // 2^31 - 1
+
+// (a v + b) mod (2^31 - 1) for a, b < 2^31 and v < 2^12, by folding the high bits.
+__device__ inline uint32_t minhash(uint32_t a, uint32_t b, int v) {
+  const uint64_t x = (uint64_t)a * (uint32_t)v + b;
+  uint32_t r = (uint32_t)(x & kMinhashP) + (uint32_t)(x >> 31);
+  if (r >= kMinhashP) r -= kMinhashP;
+  return r;
+}
+
+__device__ inline uint32_t wave_min_u32(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, off));
+  return x;
+}
+
+// One workgroup per head: the MinHash signature of every row (a wavefront per row,
+// minimum over the row's list), a sort of the rows by (signature, row), then the
+// same Stage 2 and output as the spectral order.
+__global__ __launch_bounds__(kThreads) void k_minhash_order(
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int cap, int MB,
+    int NB, uint32_t a0, uint32_t b0, uint32_t a1, uint32_t b1, int n_hash, int wave,
+    int n_slices, int stage2, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  extern __shared__ double2 lds[];
+  const int h = blockIdx.x, t = threadIdx.x;
+  const int w = t >> 6, lane = t & 63;
+  const int32_t* rp = row_ptr + (size_t)h * MB;
+  int n2 = 1;
+  while (n2 < MB) n2 <<= 1;
+  uint64_t* key = reinterpret_cast<uint64_t*>(lds);
+  uint32_t* val = reinterpret_cast<uint32_t*>(key + n2);
+  for (int u = w; u < MB; u += kWaves) {
+    uint32_t m0 = kMinhashP, m1 = kMinhashP;
+    const int lo = min(rp[u], cap), hi = min(rp[u + 1], cap);
+    for (int k = lo + lane; k < hi; k += 64) {
+      const int v = col_idx[k];
+      if ((unsigned)v < (unsigned)NB) {
+        m0 = min(m0, minhash(a0, b0, v));
+        m1 = min(m1, minhash(a1, b1, v));
       }
     }
-    sort_pairs(key, val, n2);
+    m0 = wave_min_u32(m0);
+    m1 = wave_min_u32(m1);
+    if (lane == 0) {
+      key[u] = n_hash == 2 ? (((uint64_t)m0 << 31) | m1) : (uint64_t)m0;
+      val[u] = (uint32_t)u;
+    }
   }
-  for (int pos = t; pos < MB; pos += kThreads) {
-    const int row = (int)val[pos];
-    perm_h[pos] = row;
-    inv_h[row] = pos;
+  for (int u = MB + t; u < n2; u += kThreads) {
+    key[u] = ~0ull;
+    val[u] = (uint32_t)u;
   }
+  sort_pairs(key, val, n2);
+  stage2_and_write(key, val, n2, rp, cap, MB, NB, wave, n_slices, stage2 != 0,
+                   perm + (size_t)h * MB, inv_perm + (size_t)h * MB);
 }
 
 }  // namespace
@@ -771,6 +839,20 @@ hipError_t launch_reorder(const int32_t* row_ptr, const int32_t* col_idx, const 
                        csc_ptr, csc_idx, cap, x0, MB, NB, block, head_dim, dp, perm, inv_perm,
                        skipped, angles, stats);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_minhash_order(const int32_t* row_ptr, const int32_t* col_idx, int64_t cap64,
+                                int H, int MB, int NB, const uint32_t* hash_a,
+                                const uint32_t* hash_b, int n_hash, int wave, int n_slices,
+                                int stage2, int32_t* perm, int32_t* inv_perm, hipStream_t s) {
+  int n2 = 1;
+  while (n2 < MB) n2 <<= 1;
+  const size_t lds = (size_t)n2 * (sizeof(uint64_t) + sizeof(uint32_t));  // <= 48 KiB
+  const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
+  hipLaunchKernelGGL(k_minhash_order, dim3(H), dim3(kThreads), lds, s, row_ptr, col_idx, cap, MB,
+                     NB, hash_a[0], hash_b[0], n_hash > 1 ? hash_a[1] : 0u,
+                     n_hash > 1 ? hash_b[1] : 0u, n_hash, wave, n_slices, stage2, perm, inv_perm);
   return hipGetLastError();
 }
 

@@ -20,6 +20,10 @@ hipError_t launch_reorder(const int32_t* row_ptr, const int32_t* col_idx, const 
                           int block, int head_dim, const wa_reorder_params& p, int32_t* perm,
                           int32_t* inv_perm, uint8_t* skipped, double* angles, double* stats,
                           hipStream_t s);
+hipError_t launch_minhash_order(const int32_t* row_ptr, const int32_t* col_idx, int64_t cap,
+                                int H, int MB, int NB, const uint32_t* hash_a,
+                                const uint32_t* hash_b, int n_hash, int wave, int n_slices,
+                                int stage2, int32_t* perm, int32_t* inv_perm, hipStream_t s);
 
 // True if the reorder of an MB x NB mask cannot hold the mask as bitmasks in LDS
 // and must read the transposed lists (CSC) instead.

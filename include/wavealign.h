@@ -155,6 +155,28 @@ int wa_reorder_rows(const int32_t* row_ptr, const int32_t* col_idx, const int32_
                     int32_t* perm, int32_t* inv_perm, uint8_t* skipped, double* angles,
                     double* stats, void* stream);
 
+/*
+ * wa_minhash_order - the MinHash comparator row order of [WA §VI, Table II
+ * (comparison with other reordering algorithms)], from min-wise hashing of sets:
+ * per head, row u's signature is sig_i(u) = min over the K/V blocks v of its list of
+ * (hash_a[i] * v + hash_b[i]) mod (2^31 - 1), i < n_hash (an empty row gets 2^31 - 1
+ * in each); rows are sorted by (sig_1, ..., sig_n_hash, row); with stage2 = 1 the
+ * order then goes through the same wave buckets and NNZ-descending Stage 2 as
+ * wa_reorder_rows [WA §IV-D].  No skip rule: every head is reordered.  Integer work,
+ * bit-exact.
+ *   row_ptr, col_idx, capacity  the CSR from wa_build_block_index
+ *   hash_a, hash_b  host arrays of n_hash (1 or 2) coefficients, 1 <= a < 2^31 - 1,
+ *                   0 <= b < 2^31 - 1 (drawn by the caller)
+ *   wave, n_slices  the bucket geometry, as in wa_reorder_params
+ *   perm, inv_perm  int32 [H][MB] out, as in wa_reorder_rows
+ * Errors: WA_ERR_INVALID_ARG (null pointer, sizes, coefficients, n_hash, wave,
+ * n_slices, stage2), WA_ERR_UNSUPPORTED (MB or NB > WA_MAX_BLOCKS), WA_ERR_HIP.
+ */
+int wa_minhash_order(const int32_t* row_ptr, const int32_t* col_idx, int64_t capacity, int32_t H,
+                     int32_t MB, int32_t NB, const uint32_t* hash_a, const uint32_t* hash_b,
+                     int32_t n_hash, int32_t wave, int32_t n_slices, int32_t stage2,
+                     int32_t* perm, int32_t* inv_perm, void* stream);
+
 /* 1 if wa_reorder_rows needs the CSC (csc_ptr, csc_idx) for an MB x NB mask,
  * 0 if it reads only the CSR (see wa_reorder_rows), negative on bad sizes. */
 int wa_reorder_needs_csc(int32_t MB, int32_t NB);

@@ -68,6 +68,23 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert lib.wa_reorder_rows(fake, fake, None, None, 16, fake, 1, 760, 760, 128, 128,
                                ctypes.byref(p), fake, fake, fake, None, None, None) == -1
     assert b"csc" in lib.wa_last_error()
+    # MinHash order: coefficient ranges, hash count, geometry and sizes are checked first
+    ga = (ctypes.c_uint32 * 2)(5, 7)
+    gb = (ctypes.c_uint32 * 2)(1, 2)
+    zero = (ctypes.c_uint32 * 2)(0, 7)
+    big = (ctypes.c_uint32 * 2)(5, 0x7fffffff)
+    assert lib.wa_minhash_order(fake, fake, 16, 1, 4, 4, zero, gb, 2, 4, 1, 1, fake, fake,
+                                None) == -1
+    assert lib.wa_minhash_order(fake, fake, 16, 1, 4, 4, ga, big, 2, 4, 1, 1, fake, fake,
+                                None) == -1
+    assert lib.wa_minhash_order(fake, fake, 16, 1, 4, 4, ga, gb, 3, 4, 1, 1, fake, fake,
+                                None) == -1
+    assert lib.wa_minhash_order(fake, fake, 16, 1, 4, 4, ga, gb, 2, 0, 1, 1, fake, fake,
+                                None) == -1
+    assert lib.wa_minhash_order(fake, fake, 16, 1, 5000, 4, ga, gb, 2, 4, 1, 1, fake, fake,
+                                None) == -2
+    assert lib.wa_minhash_order(None, fake, 16, 1, 4, 4, ga, gb, 2, 4, 1, 1, fake, fake,
+                                None) == -1
     # negative capacity, bad schedule and non-positive scale are refused on the host
     assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, -1, None, 1,
                                   0.1, fake, fake, None, None, 0, None) == -1
