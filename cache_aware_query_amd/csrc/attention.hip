@@ -116,20 +116,35 @@ __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4,
-// saddr form: wave-uniform base in SGPRs plus a per-lane 32-bit offset; the LDS
-// destination is the wave-uniform lds_addr plus 16 bytes per lane).  Issued
-// through inline assembly so that the compiler does not serialise the copy
+// Copies from global memory straight into LDS, 16 bytes per lane
+// (global_load_lds_dwordx4, saddr form: wave-uniform base in SGPRs plus a per-lane
+// 32-bit offset; the LDS destination is the wave-uniform M0 plus 16 bytes per lane).
+// Issued through inline assembly so that the compiler does not serialise the copies
 // against later LDS reads of other buffers; completion is awaited explicitly with
-// wait_vmcnt (vector-memory loads retire in issue order).  M0 (the LDS
-// destination register) is declared clobbered.
-__device__ inline void dma16(const char* base, uint32_t off, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(lds_addr), "v"(off), "s"(base)
-      : "memory", "m0");
+// wait_vmcnt (vector-memory loads retire in issue order).  M0 is declared clobbered.
+//
+template <int N>
+__device__ inline void dma16_group(const char* base, const uint32_t (&off)[4], uint32_t lds_addr) {
+  static_assert(N == 2 || N == 4, "copy groups of 2 or 4");
+  if constexpr (N == 4) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, %5\n\t"
+        "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+        "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
+        "global_load_lds_dwordx4 %4, %5 offset:3072"
+        :
+        : "s"(lds_addr), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(base)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\t"
+        "global_load_lds_dwordx4 %2, %3 offset:1024"
+        :
+        : "s"(lds_addr), "v"(off[0]), "v"(off[1]), "s"(base)
+        : "memory", "m0");
+  }
 }
 
 __device__ inline uint32_t lds_address(const char* p) {
@@ -256,25 +271,30 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     else return __builtin_amdgcn_readfirstlane(col_idx[e0 + t]);
   };
 
-  // Per-lane byte offsets of this wave's copy chunks inside a K half (rows = keys)
-  // and a V^T half (rows = d, 64 keys wide), relative to the half's global base.
-  // Where the swizzle does not depend on the chunk round j (every shape but
-  // block 64 with d 128) round j adds a uniform stride, kept in the scalar base.
-  constexpr bool kAffine = !(BLOCK == 64 && D == 128);
-  constexpr int kOffRegs = kAffine ? 1 : T::kSubInst;
-  uint32_t koff[kOffRegs], voff[kOffRegs];
+  // Copies of a K or V half (64 keys x D, 1 KiB chunks of whole rows): wave w copies
+  // the kSubInst consecutive chunks from chunk w * kSubInst on, in groups of up to
+  // four that share one scalar base and one M0 (the instruction offset j KiB moves
+  // both the global and the LDS address).  The per-lane offsets inside chunk j of a
+  // group carry the swizzle; it depends on the row modulo 16 only, and every group
+  // starts at a multiple of 16 rows, so the offsets are the same for every group.
+  constexpr int kGroup = T::kSubInst < 4 ? T::kSubInst : 4;
+  constexpr int kRowsPerChunk = 1024 / (D * 2);
+  constexpr int kLanesPerRow = (D * 2) / 16;
+  static_assert((T::kSubInst * kRowsPerChunk) % 16 == 0 && (kGroup * kRowsPerChunk) % 16 == 0,
+                "copy groups must start at a multiple of 16 rows");
+  uint32_t koff[4], voff[4];
 #pragma unroll
-  for (int j = 0; j < kOffRegs; ++j) {
-    const int flat = (wave + j * T::kWaves) * 1024 + lane * 16;
-    const int r = flat / (D * 2);
-    const int ks = (flat % (D * 2)) / 16;
-    koff[j] = (uint32_t)(r * D * 2 + ((ks ^ swz_k<T::kKChunks>(r)) * 16));
-    voff[j] = (uint32_t)(r * D * 2 + ((ks ^ swz_v<T::kKChunks>(r)) * 16));
+  for (int j = 0; j < 4; ++j) {
+    const int rr = lane / kLanesPerRow, ks = lane % kLanesPerRow;
+    const int r = j * kRowsPerChunk + rr;  // row modulo 16 within the group
+    koff[j] = (uint32_t)(rr * D * 2 + ((ks ^ swz_k<T::kKChunks>(r)) * 16));
+    voff[j] = (uint32_t)(rr * D * 2 + ((ks ^ swz_v<T::kKChunks>(r)) * 16));
   }
-  const char* kbytes = reinterpret_cast<const char*>(K + head_off);
-  const char* vbytes = reinterpret_cast<const char*>(V + head_off);
-  const uint32_t lk[2] = {lds_address(sk0), lds_address(sk1)};
-  const uint32_t lv[2] = {lds_address(sv0), lds_address(sv1)};
+  const char* kbytes = reinterpret_cast<const char*>(K + head_off) + wave * T::kSubInst * 1024;
+  const char* vbytes = reinterpret_cast<const char*>(V + head_off) + wave * T::kSubInst * 1024;
+  const uint32_t wl = (uint32_t)(wave * T::kSubInst * 1024);
+  const uint32_t lk[2] = {lds_address(sk0) + wl, lds_address(sk1) + wl};
+  const uint32_t lv[2] = {lds_address(sv0) + wl, lds_address(sv1) + wl};
 
   // The list is walked in 32-key quarters q = 0 .. NQ-1: quarter q is key tile q % 2
   // of half q / 2; half hh is part hh % kHalves of list tile hh / kHalves and
@@ -289,19 +309,16 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const char* base =
         kbytes + ((size_t)copy_block(v) * BLOCK + 64 * (hh % T::kHalves)) * D * 2;
 #pragma unroll
-    for (int j = 0; j < T::kSubInst; ++j)
-      dma16(kAffine ? base + (size_t)j * T::kWaves * 1024 : base, koff[kAffine ? 0 : j],
-            lk[buf] + (uint32_t)((wave + j * T::kWaves) * 1024));
+    for (int gq = 0; gq < T::kSubInst / kGroup; ++gq)
+      dma16_group<kGroup>(base + gq * 4096, koff, lk[buf] + (uint32_t)(gq * 4096));
   };
   auto issue_v = [&](int v, int hh, int buf) {
     const char* base =
         vbytes + ((size_t)copy_block(v) * BLOCK + 64 * (hh % T::kHalves)) * D * 2;
 #pragma unroll
-    for (int j = 0; j < T::kSubInst; ++j)
-      dma16(kAffine ? base + (size_t)j * T::kWaves * 1024 : base, voff[kAffine ? 0 : j],
-            lv[buf] + (uint32_t)((wave + j * T::kWaves) * 1024));
+    for (int gq = 0; gq < T::kSubInst / kGroup; ++gq)
+      dma16_group<kGroup>(base + gq * 4096, voff, lv[buf] + (uint32_t)(gq * 4096));
   };
-
 
   // S^T of one 32-key tile (key tile mt of the half in a K buffer).
   auto compute_s = [&](f32x16& acc, const char* sk, int mt) {
