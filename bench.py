@@ -344,8 +344,12 @@ def main():
                                               else caq.WA_SKIP_ALWAYS))
     if args.workload == "gsrs75k":
         return gsrs_main(args, w, params)
-    hp = HotPath(H, L, d, b, dev, capacity=nnz, reorder=params,
-                 schedule=caq.WA_SCHED_XCD_SLICED, gsrs_p=0.9)
+    # With the adaptive skip the attention follows the skip flags on the device: the
+    # default (all heads at once) path when every head kept its order, XCD-sliced
+    # otherwise.  A forced skip rule keeps the XCD-sliced schedule, so that "always"
+    # measures the identity order under the same schedule as the reordered one.
+    main_sched = caq.WA_SCHED_AUTO if args.skip == "adaptive" else caq.WA_SCHED_XCD_SLICED
+    hp = HotPath(H, L, d, b, dev, capacity=nnz, reorder=params, schedule=main_sched, gsrs_p=0.9)
     _log(f"H={H} L={L} d={d} b={b} MB={mb} nnz={nnz} density={nnz / (H * mb * mb):.4f} "
          f"xcd={n_xcd} cus/xcd={cus} wave={wave} T={args.iters} csc={hp.with_csc}")
 
@@ -444,7 +448,9 @@ def main():
         # drift during the run does not favour whichever variant runs first.  The
         # head-interleaved order is the concurrent-head execution of WaveAlign
         # §VI-B ("Original" on the A40).
+        caq.attn_schedule_select(hp.skipped, hp.workspace)  # AUTO follows hp's skip flags
         variants = {
+            "reordered_auto": with_schedule(hp, caq.WA_SCHED_AUTO),
             "reordered_xcd": with_schedule(hp, caq.WA_SCHED_XCD_SLICED),
             "identity_xcd": with_schedule(hp_id, caq.WA_SCHED_XCD_SLICED),
             "natural_order": with_schedule(hp_id, caq.WA_SCHED_NATURAL),
@@ -453,9 +459,9 @@ def main():
         for name, hpa in ablation.items():
             variants[name] = with_schedule(hpa, caq.WA_SCHED_XCD_SLICED)
         t = _time_interleaved(variants, rounds=5, reps=max(2, reps // 2))
-        hp.schedule = caq.WA_SCHED_XCD_SLICED
+        hp.schedule = main_sched
         del hp_id, ablation
-        e2e_reord = t_index + t_reorder + t["reordered_xcd"]
+        e2e_reord = t_index + t_reorder + t["reordered_auto"]
         e2e_plain = t_index_id + min(t["identity_xcd"], t["natural_order"],
                                      t["heads_interleaved"])
         detail.update({"index_ms": round(t_index, 4),

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libwavealign.so")
 WA_SCHED_NATURAL = 0
 WA_SCHED_XCD_SLICED = 1
 WA_SCHED_HEADS_INTERLEAVED = 2
+WA_SCHED_AUTO = 3
 WA_SKIP_ADAPTIVE = 0
 WA_SKIP_NEVER = 1
 WA_SKIP_ALWAYS = 2
@@ -31,7 +32,7 @@ WA_SKIP_ALWAYS = 2
 EXPORTED = (
     "wa_abi_version", "wa_last_error", "wa_schedule_info", "wa_build_block_index",
     "wa_reorder_rows", "wa_reorder_needs_csc", "wa_minhash_order", "wa_sparse_attn_workspace_size",
-    "wa_sparse_attn_fwd", "wa_sparse_attn_fwd_diag",
+    "wa_sparse_attn_fwd", "wa_sparse_attn_fwd_diag", "wa_attn_schedule_select",
     "wa_block_importance", "wa_topp_select", "wa_mask_recall", "wa_gather_blocks",
     "wa_scatter_blocks",
 )
@@ -114,6 +115,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             _I32, _I32, _P, _P, _P]),
         "wa_sparse_attn_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32,
                                                          ctypes.POINTER(ctypes.c_size_t)]),
+        "wa_attn_schedule_select": (ctypes.c_int, [_P, _I32, _P, ctypes.c_size_t, _P]),
         "wa_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _I64, _P,
                                               _I32, ctypes.c_float, _P, _P, _P, _P,
                                               ctypes.c_size_t, _P]),
@@ -283,6 +285,18 @@ def sparse_attn_workspace_size(heads: int, seq_len: int, head_dim: int, block: i
     return n.value
 
 
+def attn_schedule_select(skipped: torch.Tensor, workspace: torch.Tensor) -> None:
+    """Write the WA_SCHED_AUTO choice for these skip flags into ``workspace``
+    (wa_attn_schedule_select): all heads at once if every head was skipped, else
+    XCD-sliced.  Pass the same workspace to sparse_attn_fwd(schedule=WA_SCHED_AUTO)."""
+    lib = load_library()
+    _need(skipped, torch.uint8, "skipped", 1)
+    _need(workspace, torch.uint8, "workspace", 1)
+    _check(lib.wa_attn_schedule_select(_ptr(skipped), skipped.numel(), _ptr(workspace),
+                                       workspace.numel(), _stream(skipped.device)),
+           "wa_attn_schedule_select")
+
+
 def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len: int,
                     block: int, row_ptr: torch.Tensor, col_idx: torch.Tensor,
                     perm: torch.Tensor | None = None, schedule: int = WA_SCHED_XCD_SLICED,
@@ -329,6 +343,9 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len: 
         if not with_g:
             g = None
     ws_bytes = sparse_attn_workspace_size(H, seq_len, d, block)
+    if schedule == WA_SCHED_AUTO and workspace is None:
+        raise ValueError("WA_SCHED_AUTO reads its choice from the workspace that "
+                         "attn_schedule_select wrote; pass that workspace")
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     cap = col_idx.numel() if g is None else min(col_idx.numel(), g.shape[0])

@@ -159,7 +159,7 @@ static int sparse_attn_common(const wa_bf16* q, const wa_bf16* k, const wa_bf16*
     return fail(WA_ERR_UNSUPPORTED, "head_dim %d / block %d not in {64, 128}", head_dim, block);
   if (capacity < 0) return fail(WA_ERR_INVALID_ARG, "negative capacity");
   if (schedule != WA_SCHED_NATURAL && schedule != WA_SCHED_XCD_SLICED &&
-      schedule != WA_SCHED_HEADS_INTERLEAVED)
+      schedule != WA_SCHED_HEADS_INTERLEAVED && schedule != WA_SCHED_AUTO)
     return fail(WA_ERR_INVALID_ARG, "unknown schedule %d", schedule);
   if (!(scale > 0.0f) || !(scale < 1e30f)) return fail(WA_ERR_INVALID_ARG, "scale must be > 0");
   const int64_t MB = ((int64_t)L + block - 1) / block;
@@ -179,6 +179,17 @@ static int sparse_attn_common(const wa_bf16* q, const wa_bf16* k, const wa_bf16*
                                            workspace,
                                            static_cast<hipStream_t>(stream)),
                     name);
+}
+
+int wa_attn_schedule_select(const uint8_t* skipped, int32_t H, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!skipped || !workspace) return fail(WA_ERR_INVALID_ARG, "null pointer argument");
+  if (H < 1) return fail(WA_ERR_INVALID_ARG, "H must be >= 1");
+  const size_t need = wa::attn_workspace_bytes(H, 0, 0);
+  if (workspace_bytes < need)
+    return fail(WA_ERR_CAPACITY, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  return hip_status(wa::launch_sched_select(skipped, H, workspace, static_cast<hipStream_t>(stream)),
+                    "wa_attn_schedule_select");
 }
 
 int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,

@@ -194,7 +194,8 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
                    int cap, const int32_t* __restrict__ perm, int schedule, float scale_log2,
                    uint16_t* __restrict__ O, float* __restrict__ lse, float* __restrict__ G,
-                   float* __restrict__ ENT, float* __restrict__ DIST) {
+                   float* __restrict__ ENT, float* __restrict__ DIST,
+                   const int* __restrict__ sched_ws) {
   using T = Tile<BLOCK, D>;
   // Two K and two V^T half-tile buffers, separate LDS objects so that the compiler
   // can tell the asynchronous copies into one from the reads of another.
@@ -206,6 +207,9 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
   const int Lp = MB * BLOCK;
   int h, pos;
+  if (schedule == WA_SCHED_AUTO)  // the choice of k_sched_select (XCD-sliced unless all-skipped)
+    schedule = sched_ws[0] == WA_SCHED_HEADS_INTERLEAVED ? WA_SCHED_HEADS_INTERLEAVED
+                                                         : WA_SCHED_XCD_SLICED;
   if (schedule == WA_SCHED_XCD_SLICED) {
     const int s = (MB + kXcds - 1) / kXcds;
     const int x = blockIdx.x % kXcds;
@@ -216,6 +220,7 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   } else if (schedule == WA_SCHED_HEADS_INTERLEAVED) {
     h = blockIdx.x % H;
     pos = blockIdx.x / H;
+    if (pos >= MB) return;  // an AUTO launch has the larger XCD-sliced grid
   } else {
     h = blockIdx.x / MB;
     pos = blockIdx.x % MB;
@@ -598,14 +603,15 @@ template <int BLOCK, int D>
 hipError_t launch_typed(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H, int L,
                         const int32_t* row_ptr, const int32_t* col_idx, int cap,
                         const int32_t* perm, int schedule, float scale, uint16_t* o, float* lse,
-                        float* g, float* ent, float* dist, hipStream_t s) {
+                        float* g, float* ent, float* dist, const int* sched_ws, hipStream_t s) {
   const int MB = (L + BLOCK - 1) / BLOCK;
   int grid = H * MB;
-  if (schedule == WA_SCHED_XCD_SLICED) grid = H * kXcds * ((MB + kXcds - 1) / kXcds);
+  if (schedule == WA_SCHED_XCD_SLICED || schedule == WA_SCHED_AUTO)
+    grid = H * kXcds * ((MB + kXcds - 1) / kXcds);  // >= H * MB, the other schedules' grid
   const float sl2 = scale * kLog2e;
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(BLOCK * 2), 0, s, q, k, v, H, L, MB, row_ptr,
-                       col_idx, cap, perm, schedule, sl2, o, lse, g, ent, dist);
+                       col_idx, cap, perm, schedule, sl2, o, lse, g, ent, dist, sched_ws);
   };
   const bool staged = MB <= kListCap;  // NB = MB: every list fits in LDS
   auto pick = [&](auto diag) {
@@ -629,7 +635,25 @@ size_t attn_workspace_bytes(int H, int L_pad, int head_dim) {
   (void)H;
   (void)L_pad;
   (void)head_dim;
-  return 0;  // V is read in its own layout; no staging buffer
+  return 256;  // the schedule chosen for WA_SCHED_AUTO; K and V are read in place
+}
+
+namespace {
+// One wavefront: WA_SCHED_HEADS_INTERLEAVED if every head was skipped, else
+// WA_SCHED_XCD_SLICED, into out[0].
+__global__ __launch_bounds__(64) void k_sched_select(const uint8_t* __restrict__ skipped, int H,
+                                                     int* __restrict__ out) {
+  bool all = true;
+  for (int i = threadIdx.x; i < H; i += 64) all = all && skipped[i] != 0;
+  const bool some_reordered = __builtin_amdgcn_ballot_w64(!all) != 0;
+  if (threadIdx.x == 0) out[0] = some_reordered ? WA_SCHED_XCD_SLICED : WA_SCHED_HEADS_INTERLEAVED;
+}
+}  // namespace
+
+hipError_t launch_sched_select(const uint8_t* skipped, int H, void* workspace, hipStream_t s) {
+  hipLaunchKernelGGL(k_sched_select, dim3(1), dim3(64), 0, s, skipped, H,
+                     static_cast<int*>(workspace));
+  return hipGetLastError();
 }
 
 int attn_resident_wgs_per_cu(int head_dim, int block) {
@@ -643,19 +667,19 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
                               const int32_t* col_idx, int64_t cap64, const int32_t* perm,
                               int schedule, float scale, uint16_t* o, float* lse, float* g,
                               float* ent, float* dist, void* workspace, hipStream_t s) {
-  (void)workspace;
+  const int* sched_ws = static_cast<const int*>(workspace);
   const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
   if (block == 128 && head_dim == 128)
     return launch_typed<128, 128>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o,
-                                  lse, g, ent, dist, s);
+                                  lse, g, ent, dist, sched_ws, s);
   if (block == 128 && head_dim == 64)
     return launch_typed<128, 64>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o,
-                                 lse, g, ent, dist, s);
+                                 lse, g, ent, dist, sched_ws, s);
   if (block == 64 && head_dim == 128)
     return launch_typed<64, 128>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o,
-                                 lse, g, ent, dist, s);
+                                 lse, g, ent, dist, sched_ws, s);
   return launch_typed<64, 64>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o, lse,
-                              g, ent, dist, s);
+                              g, ent, dist, sched_ws, s);
 }
 
 }  // namespace wa

@@ -30,6 +30,7 @@ hipError_t launch_minhash_order(const int32_t* row_ptr, const int32_t* col_idx, 
 bool reorder_needs_csc(int MB, int NB);
 
 size_t attn_workspace_bytes(int H, int L_pad, int head_dim);
+hipError_t launch_sched_select(const uint8_t* skipped, int H, void* workspace, hipStream_t s);
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H,
                               int L, int head_dim, int block, const int32_t* row_ptr,
                               const int32_t* col_idx, int64_t cap, const int32_t* perm,

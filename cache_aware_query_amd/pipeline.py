@@ -21,7 +21,7 @@ import ctypes
 
 import torch
 
-from . import (WA_SCHED_XCD_SLICED, BlockIndex, ReorderParams, _check, _ptr, _stream,
+from . import (WA_SCHED_AUTO, WA_SCHED_XCD_SLICED, BlockIndex, ReorderParams, _check, _ptr, _stream,
                load_library, reorder_needs_csc, sparse_attn_workspace_size)
 
 
@@ -36,6 +36,8 @@ class HotPath:
         self.device = torch.device(device)
         self.cap = heads * self.mb * self.mb if capacity is None else int(capacity)
         self.reorder = reorder
+        if schedule == WA_SCHED_AUTO and reorder is None:
+            raise ValueError("WA_SCHED_AUTO follows the reorder's skip flags; give a reorder")
         self.schedule = schedule
         self.gsrs_p = gsrs_p
         dev = self.device
@@ -93,6 +95,11 @@ class HotPath:
                                    self.b, self.d, ctypes.byref(self._params), _ptr(self.perm),
                                    _ptr(self.inv_perm), _ptr(self.skipped), _ptr(self.angles),
                                    _ptr(self.stats), s), "wa_reorder_rows")
+        if self.schedule == WA_SCHED_AUTO:
+            # all heads skipped: the attention falls back to the default (all heads at
+            # once) path, chosen on the device (WaveAlign §VI-F)
+            _check(lib.wa_attn_schedule_select(_ptr(self.skipped), self.H, _ptr(self.workspace),
+                                               self.ws_bytes, s), "wa_attn_schedule_select")
 
     def attention(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
         lib, s = self.lib, _stream(self.device)

@@ -51,6 +51,9 @@ extern "C" {
 #define WA_SCHED_HEADS_INTERLEAVED 2 /* workgroup w runs position w / H of head w % H: all heads
                                         at once, the concurrent-head execution that WaveAlign
                                         VI-B contrasts with sequential heads */
+#define WA_SCHED_AUTO 3 /* the schedule wa_attn_schedule_select wrote into the workspace:
+                           XCD-sliced if some head was reordered, all heads at once (the
+                           default path) if every head kept its order */
 
 /* Skip modes of wa_reorder_rows. */
 #define WA_SKIP_ADAPTIVE 0
@@ -181,8 +184,9 @@ int wa_minhash_order(const int32_t* row_ptr, const int32_t* col_idx, int64_t cap
  * 0 if it reads only the CSR (see wa_reorder_rows), negative on bad sizes. */
 int wa_reorder_needs_csc(int32_t MB, int32_t NB);
 
-/* Workspace bytes wa_sparse_attn_fwd needs for these sizes (host output).  The
- * current kernels read K and V in place and need none (0 bytes). */
+/* Workspace bytes wa_sparse_attn_fwd needs for these sizes (host output): 256 bytes,
+ * which hold the schedule wa_attn_schedule_select chooses for WA_SCHED_AUTO (K and V
+ * are read in place). */
 int wa_sparse_attn_workspace_size(int32_t H, int32_t L, int32_t head_dim, int32_t block,
                                   size_t* bytes);
 
@@ -200,14 +204,14 @@ int wa_sparse_attn_workspace_size(int32_t H, int32_t L, int32_t head_dim, int32_
  *   perm      int32 [H][MB] or NULL  execution order [WA §V]: position p of head h runs
  *             query block perm[h][p]; O, LSE and G stay in the original order (the
  *             permutation is applied by indexing, the inverse reorder is implicit)
- *   schedule  WA_SCHED_NATURAL, WA_SCHED_XCD_SLICED or WA_SCHED_HEADS_INTERLEAVED
+ *   schedule  WA_SCHED_NATURAL, WA_SCHED_XCD_SLICED, WA_SCHED_HEADS_INTERLEAVED or
+ *             WA_SCHED_AUTO (reads the choice of wa_attn_schedule_select from workspace)
  *   o         bf16 [H][L_pad][head_dim] out
  *   lse       float [H][L_pad] out, natural log
  *   g         float [row_ptr[H*MB]][block] out or NULL  [GSRS §5.3 Phase 1] for CSR
  *             entry e = (u, v) and row r of u, the block log-sum-exp
  *             G = m + ln sum_{j in v, j < L} exp(z_rj - m), m the block maximum
- *   workspace device buffer of at least wa_sparse_attn_workspace_size bytes (may be
- *             NULL when that size is 0)
+ *   workspace device buffer of at least wa_sparse_attn_workspace_size bytes
  * Errors: WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED (head_dim/block), WA_ERR_CAPACITY
  * (workspace too small), WA_ERR_HIP.
  */
@@ -217,6 +221,22 @@ int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int
                        int32_t schedule,
                        float scale, wa_bf16* o, float* lse, float* g, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * wa_attn_schedule_select - [WA §VI-F, Fig. 13: when the adaptive skip leaves every
+ * head in its order, execution falls back to the default sparse-attention path]
+ * writes into workspace the schedule WA_SCHED_AUTO runs: WA_SCHED_XCD_SLICED if some
+ * skipped[h] is 0, WA_SCHED_HEADS_INTERLEAVED (all heads at once) if every one is
+ * non-zero.  One small kernel on the device, so the choice follows the reorder
+ * without a host synchronisation.
+ *   skipped   uint8 [H] from wa_reorder_rows
+ *   workspace device buffer of at least wa_sparse_attn_workspace_size bytes, passed to
+ *             the wa_sparse_attn_fwd calls that use WA_SCHED_AUTO afterwards
+ * Errors: WA_ERR_INVALID_ARG (null pointer, H < 1), WA_ERR_CAPACITY (workspace too
+ * small), WA_ERR_HIP.
+ */
+int wa_attn_schedule_select(const uint8_t* skipped, int32_t H, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * wa_sparse_attn_fwd_diag - wa_sparse_attn_fwd that also writes per-row attention

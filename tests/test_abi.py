@@ -49,7 +49,7 @@ def test_host_validation_rejects_bad_arguments(lib):
     n = ctypes.c_size_t()
     assert lib.wa_sparse_attn_workspace_size(2, 1000, 96, 128, ctypes.byref(n)) == -2
     assert lib.wa_sparse_attn_workspace_size(2, 1000, 128, 128, ctypes.byref(n)) == 0
-    assert n.value == 0  # K and V are read in place
+    assert n.value == 256  # the WA_SCHED_AUTO choice; K and V are read in place
     assert lib.wa_last_error() == b""
     fake = ctypes.c_void_p(16)
     assert lib.wa_topp_select(fake, fake, fake, 4, 1, 1, 1, 1.5, fake, None) == -1
@@ -92,6 +92,12 @@ def test_host_validation_rejects_bad_arguments(lib):
                                   0.1, fake, fake, None, None, 0, None) == -1
     assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 1,
                                   -0.1, fake, fake, None, None, 0, None) == -1
+    # the workspace is required (it carries the WA_SCHED_AUTO choice)
+    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 3,
+                                  0.1, fake, fake, None, None, 0, None) == -3
+    assert lib.wa_attn_schedule_select(fake, 4, fake, 16, None) == -3
+    assert lib.wa_attn_schedule_select(None, 4, fake, 256, None) == -1
+    assert lib.wa_attn_schedule_select(fake, 0, fake, 256, None) == -1
     # unaligned pointer
     odd = ctypes.c_void_p(18)
     assert lib.wa_sparse_attn_fwd(odd, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 1,

@@ -186,3 +186,30 @@ def test_distance_with_uniform_attention(shape):
                 continue
             assert abs(dist[h, i] - np.abs(keys - i).mean()) < 1e-2
             assert abs(ent[h, i] - np.log(keys.size)) < 1e-3
+
+
+@pytest.mark.parametrize("skip_mode,expect", [(caq.WA_SKIP_ALWAYS, caq.WA_SCHED_HEADS_INTERLEAVED),
+                                              (caq.WA_SKIP_NEVER, caq.WA_SCHED_XCD_SLICED)])
+def test_auto_schedule_follows_the_skip_flags(skip_mode, expect):
+    """WA_SCHED_AUTO runs all heads at once when every head kept its order and the
+    XCD-sliced schedule otherwise; the output is the same either way."""
+    dev = gpu()
+    w = synth.random_tiny_case(23, heads=3, seq_len=1500, head_dim=128, block=128, density=0.4,
+                               empty_rows=(2,))
+    banner(f"attention AUTO schedule skip_mode={skip_mode}")
+    q, k, v, mask, x0 = (t.to(dev) for t in (w.q, w.k, w.v, w.mask, w.x0))
+    idx = caq.build_block_index(mask)
+    ro = caq.reorder_rows(idx, x0, w.block, w.head_dim,
+                          caq.ReorderParams(wave=8, n_slices=8, skip_mode=skip_mode))
+    ws = torch.empty(caq.sparse_attn_workspace_size(3, w.seq_len, 128, 128), dtype=torch.uint8,
+                     device=dev)
+    caq.attn_schedule_select(ro.skipped, ws)
+    o, lse, g = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx,
+                                    perm=ro.perm, schedule=caq.WA_SCHED_AUTO, with_g=True,
+                                    workspace=ws)
+    o2, lse2, g2 = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx,
+                                       perm=ro.perm, schedule=expect, with_g=True)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == expect
+    assert torch.equal(o, o2) and torch.equal(lse, lse2) and torch.equal(g, g2)
+    _compare(w, o, lse, f"AUTO skip_mode={skip_mode}")
