@@ -17,19 +17,66 @@ __device__ inline uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
 }
 
+// The mask read four bytes per lane.  Words are counted from the 4-byte aligned
+// address at or below the mask (o = misalignment); a word that does not lie wholly
+// inside the mask is assembled from its in-range bytes, so no byte outside the
+// buffer is read.  Row r covers bytes [o + r*NB, o + r*NB + NB) of that word space.
+struct MaskWords {
+  const uint32_t* aligned;
+  const uint8_t* bytes;  // == aligned as bytes
+  int64_t o, total;      // misalignment and mask size in bytes
+
+  __device__ explicit MaskWords(const uint8_t* mask, int64_t size) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(mask);
+    aligned = reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
+    bytes = reinterpret_cast<const uint8_t*>(aligned);
+    o = (int64_t)(a & 3);
+    total = size;
+  }
+  __device__ uint32_t word(int64_t w) const {
+    if (4 * w >= o && 4 * w + 4 <= o + total) return aligned[w];
+    uint32_t x = 0;
+    for (int b = 0; b < 4; ++b) {
+      const int64_t i = 4 * w + b;
+      if (i >= o && i < o + total) x |= (uint32_t)bytes[i] << (8 * b);
+    }
+    return x;
+  }
+};
+
+// Flags (bit b) of the non-zero bytes of word w that belong to columns [0, NB) of
+// the row starting at byte rs; *v0 receives the column of byte 0 of the word.
+__device__ inline uint32_t row_word_flags(const MaskWords& mw, int64_t w, int64_t rs, int NB,
+                                          int64_t* v0) {
+  const uint32_t x = mw.word(w);
+  const int64_t c0 = 4 * w - rs;
+  uint32_t f = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int64_t v = c0 + b;
+    if (v >= 0 && v < NB && ((x >> (8 * b)) & 0xffu) != 0) f |= 1u << b;
+  }
+  *v0 = c0;
+  return f;
+}
+
 // One wavefront per mask row: row_nnz[r] = number of non-zero bytes.
 __global__ __launch_bounds__(256) void k_row_counts(const uint8_t* __restrict__ mask, int rows,
                                                     int NB, int32_t* __restrict__ row_nnz) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= rows) return;
-  const uint8_t* m = mask + (size_t)r * NB;
+  const MaskWords mw(mask, (int64_t)rows * NB);
+  const int64_t rs = mw.o + (int64_t)r * NB;
+  const int64_t w_end = (rs + NB + 3) / 4;
   int cnt = 0;
-  for (int v0 = 0; v0 < NB; v0 += kWave) {
-    const int v = v0 + lane;
-    const bool bit = v < NB && m[v] != 0;
-    cnt += __popcll(__ballot(bit));
+  for (int64_t w = rs / 4 + lane; w < w_end; w += kWave) {
+    int64_t c0;
+    cnt += __popc(row_word_flags(mw, w, rs, NB, &c0));
   }
+  // wavefront sum (integers: exact in any order)
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
   if (lane == 0) row_nnz[r] = cnt;
 }
 

@@ -62,3 +62,30 @@ def test_block_index_capacity_truncation():
     torch.cuda.synchronize()
     assert int(idx.row_ptr[-1]) == 64           # the true total is still reported
     assert idx.col_idx.cpu().tolist()[:10] == list(range(8)) + [0, 1]
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_block_index_unaligned_mask_and_odd_rows(offset):
+    """The kernels read the mask four bytes per lane: a mask that starts off a 4-byte
+    boundary, rows whose length is not a multiple of 4, non-zero values other than 1
+    and non-zero bytes right outside the mask must all give the oracle's lists."""
+    dev = gpu()
+    rng = np.random.default_rng(offset)
+    for H, MB, NB in ((1, 3, 5), (2, 7, 131), (3, 33, 2), (1, 2, 1)):
+        m = (rng.random((H, MB, NB)) < 0.4).astype(np.uint8) * rng.integers(1, 255, (H, MB, NB),
+                                                                             dtype=np.uint8)
+        n = H * MB * NB
+        buf = torch.full((offset + n + 5,), 255, dtype=torch.uint8, device=dev)
+        buf[offset:offset + n] = torch.from_numpy(m.reshape(-1)).to(dev)
+        mask = buf[offset:offset + n].view(H, MB, NB)
+        assert mask.data_ptr() % 4 == offset % 4
+        banner(f"block_index unaligned offset={offset} H={H} MB={MB} NB={NB}")
+        idx = caq.build_block_index(mask)
+        torch.cuda.synchronize()
+        rp, ci, nnz, cp, csi = oracle.block_index((m != 0).astype(np.uint8))
+        total = int(rp[-1])
+        assert np.array_equal(idx.row_ptr.cpu().numpy(), rp)
+        assert np.array_equal(idx.row_nnz.cpu().numpy(), nnz)
+        assert np.array_equal(idx.col_idx.cpu().numpy()[:total], ci)
+        assert np.array_equal(idx.csc_ptr.cpu().numpy(), cp)
+        assert np.array_equal(idx.csc_idx.cpu().numpy()[:total], csi)
