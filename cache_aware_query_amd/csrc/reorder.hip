@@ -469,7 +469,7 @@ template <bool BITS>
 __global__ __launch_bounds__(kThreads) void k_reorder(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ csc_ptr, const int32_t* __restrict__ csc_idx, int cap,
-    const float* __restrict__ x0, int MB, int NB, int block, int head_dim, DevParams p,
+    const float* __restrict__ x0, int MB, int NB, int block, int head_dim, DevParams p, int rowbits,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm, uint8_t* __restrict__ skipped,
     double* __restrict__ angles, double* __restrict__ stats) {
   extern __shared__ double2 lds[];
@@ -517,16 +517,34 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
   // ---- statistics and the skip decision (§IV-E) ----
   const long long nnz = (long long)rp[MB] - (long long)rp[0];
   long long inter = 0, uni = 0;
-  if (BITS || nnz < kStatsWaveMin * (long long)MB) {
-    // One thread per adjacent pair: popcounts of the bitmask rows, else a merge of
+  // Without the bitmasks of the BITS form, row bitmasks alone still fit in LDS for
+  // moderate sizes (rowbits): built here from the lists, they only serve the pairs.
+  const uint32_t* prm = BITS ? bits.rm : reinterpret_cast<const uint32_t*>(lds);
+  const int pnw = BITS ? bits.NW : (NB + 31) / 32;
+  if constexpr (!BITS) {
+    if (rowbits) {
+      uint32_t* rmw = reinterpret_cast<uint32_t*>(lds);
+      for (int i = t; i < MB * pnw; i += kThreads) rmw[i] = 0u;
+      __syncthreads();
+      const int w = t >> 6, lane = t & 63;
+      for (int u = w; u < MB; u += kWaves)
+        for (int k = min(rp[u], cap) + lane, e = min(rp[u + 1], cap); k < e; k += 64) {
+          const int v = col_idx[k];
+          if ((unsigned)v < (unsigned)NB) atomicOr(&rmw[(size_t)u * pnw + (v >> 5)], 1u << (v & 31));
+        }
+      __syncthreads();
+    }
+  }
+  if (BITS || rowbits || nnz < kStatsWaveMin * (long long)MB) {
+    // One thread per adjacent pair: popcounts of the row bitmasks, else a merge of
     // the two sorted lists (short lists: cheaper than walking rows per wave).
     for (int u = t; u + 1 < MB; u += kThreads) {
       const int na = min(rp[u + 1], cap) - min(rp[u], cap);
       const int nb = min(rp[u + 2], cap) - min(rp[u + 1], cap);
       int common = 0;
-      if constexpr (BITS) {
-        for (int i = 0; i < bits.NW; ++i)
-          common += __popc(bits.rm[(size_t)u * bits.NW + i] & bits.rm[(size_t)(u + 1) * bits.NW + i]);
+      if (BITS || rowbits) {
+        for (int i = 0; i < pnw; ++i)
+          common += __popc(prm[(size_t)u * pnw + i] & prm[(size_t)(u + 1) * pnw + i]);
       } else {
         int a = min(rp[u], cap), ae = min(rp[u + 1], cap);
         int b = ae, be = min(rp[u + 2], cap);
@@ -810,6 +828,10 @@ hipError_t launch_reorder(const int32_t* row_ptr, const int32_t* col_idx, const 
   size_t embed_bytes = use_bits ? reorder_bits_lds_bytes(MB, NB)
                                 : (size_t)(MB + NB) * sizeof(double2);
   if (!use_bits && stats_bytes > embed_bytes) embed_bytes = stats_bytes;
+  // Row bitmasks for the pair statistics of the transposed-list form, when they fit.
+  const size_t rowbits_bytes = (size_t)MB * ((NB + 31) / 32) * sizeof(uint32_t);
+  const int rowbits = !use_bits && rowbits_bytes <= kBitsLdsLimit ? 1 : 0;
+  if (rowbits && rowbits_bytes > embed_bytes) embed_bytes = rowbits_bytes;
   const size_t sort_bytes = (size_t)n2 * (sizeof(uint64_t) + sizeof(uint32_t));
   const size_t lds = embed_bytes > sort_bytes ? embed_bytes : sort_bytes;
   // The dynamic LDS limit is a per-device function attribute; set it once per device.
@@ -832,11 +854,12 @@ hipError_t launch_reorder(const int32_t* row_ptr, const int32_t* col_idx, const 
   const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
   if (use_bits) {
     hipLaunchKernelGGL(k_reorder<true>, dim3(H), dim3(kThreads), lds, s, row_ptr, col_idx, csc_ptr,
-                       csc_idx, cap, x0, MB, NB, block, head_dim, dp, perm, inv_perm, skipped,
+                       csc_idx, cap, x0, MB, NB, block, head_dim, dp, 0, perm, inv_perm, skipped,
                        angles, stats);
   } else {
     hipLaunchKernelGGL(k_reorder<false>, dim3(H), dim3(kThreads), lds, s, row_ptr, col_idx,
-                       csc_ptr, csc_idx, cap, x0, MB, NB, block, head_dim, dp, perm, inv_perm,
+                       csc_ptr, csc_idx, cap, x0, MB, NB, block, head_dim, dp, rowbits, perm,
+                       inv_perm,
                        skipped, angles, stats);
   }
   return hipGetLastError();

@@ -70,6 +70,12 @@ CASES = [
                                        skip_mode=caq.WA_SKIP_NEVER)),
     ("wan75k", {"heads": 4}, caq.ReorderParams(wave=64, n_slices=8, skip_mode=caq.WA_SKIP_NEVER)),
     ("gsrs75k", {"heads": 2}, caq.ReorderParams(wave=64, n_slices=8, skip_mode=caq.WA_SKIP_NEVER)),
+    # 929 blocks: the transposed-list form, very sparse Top-p masks, one lane per list
+    ("hunyuan119k", {"heads": 3}, caq.ReorderParams(wave=64, n_slices=8,
+                                                    skip_mode=caq.WA_SKIP_NEVER)),
+    ("hunyuan119k", {"heads": 3}, caq.ReorderParams(wave=64, n_slices=8,
+                                                    skip_mode=caq.WA_SKIP_ADAPTIVE,
+                                                    flops_min=1e10, jaccard_max=0.9)),
 ]
 
 
