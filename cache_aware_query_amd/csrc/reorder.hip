@@ -28,7 +28,7 @@ namespace {
 constexpr int kThreads = 1024;
 // Dynamic LDS the bitmask form of the reorder may use (the rest of the 160 KiB is
 // left to the kernel's static arrays).
-constexpr size_t kBitsLdsLimit = 144 * 1024;
+constexpr size_t kBitsLdsLimit = 152 * 1024;
 constexpr int kWaves = kThreads / 64;
 // Mean row length from which the CSC-form statistics walk rows per wave.
 constexpr long long kStatsWaveMin = 64;
@@ -284,16 +284,35 @@ __device__ void apply_m(const double2* y, const int32_t* __restrict__ cp,
   });
 }
 
-// The head's mask as bitmasks in LDS: row u is rm[u*NW .. +NW) (bit v%32 of word
-// v/32), column v is cm[v*MW .. +MW); cc[v] is the column count.  Four lanes share
-// a row or column, each summing every fourth word in ascending bit order, and the
-// four partial sums are combined with a fixed shuffle tree (so every sum has a
-// fixed order and the result is reproducible).
+// Z = M Y - 1 (c^T Y) / MB with the column counts c from LDS and the rows gathered
+// from the CSR in global memory (faster than walking the row bitmasks).
+template <typename F>
+__device__ void apply_m_rows(const double2* y, const int32_t* cc, const int32_t* __restrict__ rp,
+                             const int32_t* __restrict__ ci, int cap, int MB, int NB, int lanes,
+                             Reducer& red, F f) {
+  const int t = threadIdx.x;
+  double2 s = make_double2(0.0, 0.0);
+  for (int v = t; v < NB; v += kThreads) {
+    const double c = (double)cc[v];
+    s.x += c * y[v].x;
+    s.y += c * y[v].y;
+  }
+  s = block_sum2(s, red);
+  const double inv = 1.0 / (double)MB;
+  gather_any(lanes, y, rp, ci, cap, MB, [&](int u, double ax, double ay) {
+    f(u, make_double2(ax - s.x * inv, ay - s.y * inv));
+  });
+}
+
+// The head's mask as column bitmasks in LDS: column v is cm[v*MW .. +MW) (bit u%32
+// of word u/32 for row u); cc[v] is the column count.  Four lanes share a column,
+// each summing every fourth word in ascending bit order, and the four partial sums
+// are combined with a fixed shuffle tree (so every sum has a fixed order and the
+// result is reproducible).  Row products read the CSR lists instead.
 struct MaskBits {
-  const uint32_t* rm;
   const uint32_t* cm;
   const int32_t* cc;
-  int NW, MW;
+  int MW;
 };
 
 // Y = M^T X - c (1^T X) / MB from the column bitmasks.
@@ -330,39 +349,6 @@ __device__ void apply_mt_bits(const double2* x, double2* y, const MaskBits& mb, 
   __syncthreads();
 }
 
-// Z = M Y - 1 (c^T Y) / MB from the row bitmasks; calls f(u, z) on one lane per row.
-template <typename F>
-__device__ void apply_m_bits(const double2* y, const MaskBits& mb, int MB, int NB, Reducer& red,
-                             F f) {
-  const int t = threadIdx.x;
-  double2 s = make_double2(0.0, 0.0);
-  for (int v = t; v < NB; v += kThreads) {
-    const double c = (double)mb.cc[v];
-    s.x += c * y[v].x;
-    s.y += c * y[v].y;
-  }
-  s = block_sum2(s, red);
-  const double inv = 1.0 / (double)MB;
-  const int sub = t & 3;
-  for (int u = t >> 2; u < MB; u += kThreads / 4) {
-    double ax = 0.0, ay = 0.0;
-    const uint32_t* row = mb.rm + (size_t)u * mb.NW;
-    for (int i = sub; i < mb.NW; i += 4) {
-      uint32_t bits = row[i];
-      while (bits != 0u) {
-        const int v = 32 * i + __builtin_ctz(bits);
-        bits &= bits - 1u;
-        ax += y[v].x;
-        ay += y[v].y;
-      }
-    }
-    ax += __shfl_xor(ax, 1);
-    ay += __shfl_xor(ay, 1);
-    ax += __shfl_xor(ax, 2);
-    ay += __shfl_xor(ay, 2);
-    if (sub == 0) f(u, make_double2(ax - s.x * inv, ay - s.y * inv));
-  }
-}
 
 // Ascending sort of n (a power of two, at most 4 * kThreads) (key, val) pairs in
 // LDS, ordered by key and then by val; the pairs must be distinct.  Runs of 64 are
@@ -486,32 +472,37 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
   double* ang_h = angles ? angles + (size_t)h * MB : nullptr;
 
   MaskBits bits{};
+  // BITS: this thread's part of the sum over adjacent row pairs of |R_u & R_u+1|,
+  // read off the column bitmasks as pairs of neighbouring set bits.
+  long long pair_inter = 0;
   if constexpr (BITS) {
-    const int NW = (NB + 31) / 32, MW = (MB + 31) / 32;
-    uint32_t* rm = reinterpret_cast<uint32_t*>(lds + MB + NB);
-    uint32_t* cm = rm + (size_t)MB * NW;
+    const int MW = (MB + 31) / 32;
+    uint32_t* cm = reinterpret_cast<uint32_t*>(lds + MB + NB);
     int32_t* cc = reinterpret_cast<int32_t*>(cm + (size_t)NB * MW);
-    for (int i = t; i < MB * NW + NB * MW; i += kThreads) rm[i] = 0u;
+    for (int i = t; i < NB * MW; i += kThreads) cm[i] = 0u;
     __syncthreads();
     const int w = t >> 6, lane = t & 63;
     for (int u = w; u < MB; u += kWaves) {
       const int lo = min(rp[u], cap), hi = min(rp[u + 1], cap);
       for (int k = lo + lane; k < hi; k += 64) {
         const int v = col_idx[k];
-        if ((unsigned)v < (unsigned)NB) {
-          atomicOr(&rm[(size_t)u * NW + (v >> 5)], 1u << (v & 31));
-          atomicOr(&cm[(size_t)v * MW + (u >> 5)], 1u << (u & 31));
-        }
+        if ((unsigned)v < (unsigned)NB) atomicOr(&cm[(size_t)v * MW + (u >> 5)], 1u << (u & 31));
       }
     }
     __syncthreads();
     for (int v = t; v < NB; v += kThreads) {
       int c = 0;
-      for (int i = 0; i < MW; ++i) c += __popc(cm[(size_t)v * MW + i]);
+      uint32_t prev = 0u;
+      for (int i = 0; i < MW; ++i) {
+        const uint32_t x = cm[(size_t)v * MW + i];
+        c += __popc(x);
+        pair_inter += __popc(x & (x >> 1)) + (int)((prev >> 31) & x & 1u);
+        prev = x;
+      }
       cc[v] = c;
     }
     __syncthreads();
-    bits = MaskBits{rm, cm, cc, NW, MW};
+    bits = MaskBits{cm, cc, MW};
   }
 
   // ---- statistics and the skip decision (§IV-E) ----
@@ -519,8 +510,8 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
   long long inter = 0, uni = 0;
   // Without the bitmasks of the BITS form, row bitmasks alone still fit in LDS for
   // moderate sizes (rowbits): built here from the lists, they only serve the pairs.
-  const uint32_t* prm = BITS ? bits.rm : reinterpret_cast<const uint32_t*>(lds);
-  const int pnw = BITS ? bits.NW : (NB + 31) / 32;
+  const uint32_t* prm = reinterpret_cast<const uint32_t*>(lds);
+  const int pnw = (NB + 31) / 32;
   if constexpr (!BITS) {
     if (rowbits) {
       uint32_t* rmw = reinterpret_cast<uint32_t*>(lds);
@@ -535,14 +526,23 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
       __syncthreads();
     }
   }
-  if (BITS || rowbits || nnz < kStatsWaveMin * (long long)MB) {
+  if (BITS) {
+    // pooled union = sum over pairs of |R_u| + |R_u+1| minus the intersections
+    inter = pair_inter;
+    uni = -pair_inter;
+    if (t == 0) {
+      const long long n0 = min(rp[1], cap) - min(rp[0], cap);
+      const long long nl = min(rp[MB], cap) - min(rp[MB - 1], cap);
+      uni += 2 * ((long long)min(rp[MB], cap) - min(rp[0], cap)) - n0 - nl;
+    }
+  } else if (rowbits || nnz < kStatsWaveMin * (long long)MB) {
     // One thread per adjacent pair: popcounts of the row bitmasks, else a merge of
     // the two sorted lists (short lists: cheaper than walking rows per wave).
     for (int u = t; u + 1 < MB; u += kThreads) {
       const int na = min(rp[u + 1], cap) - min(rp[u], cap);
       const int nb = min(rp[u + 2], cap) - min(rp[u + 1], cap);
       int common = 0;
-      if (BITS || rowbits) {
+      if (rowbits) {
         for (int i = 0; i < pnw; ++i)
           common += __popc(prm[(size_t)u * pnw + i] & prm[(size_t)(u + 1) * pnw + i]);
       } else {
@@ -658,7 +658,8 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
     for (int it = 0; it < p.iters; ++it) {
       if constexpr (BITS) {
         apply_mt_bits(X, Y, bits, MB, NB, red);
-        apply_m_bits(Y, bits, MB, NB, red, [&](int u, double2 z) { X[u] = z; });
+        apply_m_rows(Y, bits.cc, rp, col_idx, cap, MB, NB, glists, red,
+                     [&](int u, double2 z) { X[u] = z; });
       } else {
         apply_mt(X, Y, cp, csc_idx, cap, MB, NB, glists, red);
         apply_m(Y, cp, rp, col_idx, cap, MB, NB, glists, red, [&](int u, double2 z) { X[u] = z; });
@@ -678,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
     };
     if constexpr (BITS) {
       apply_mt_bits(X, Y, bits, MB, NB, red);
-      apply_m_bits(Y, bits, MB, NB, red, ritz_acc);
+      apply_m_rows(Y, bits.cc, rp, col_idx, cap, MB, NB, glists, red, ritz_acc);
     } else {
       apply_mt(X, Y, cp, csc_idx, cap, MB, NB, glists, red);
       apply_m(Y, cp, rp, col_idx, cap, MB, NB, glists, red, ritz_acc);
@@ -810,8 +811,8 @@ __global__ __launch_bounds__(kThreads) void k_minhash_order(
 }  // namespace
 
 size_t reorder_bits_lds_bytes(int MB, int NB) {
-  const size_t NW = (NB + 31) / 32, MW = (MB + 31) / 32;
-  return (size_t)(MB + NB) * sizeof(double2) + ((size_t)MB * NW + (size_t)NB * MW + NB) * 4;
+  const size_t MW = (MB + 31) / 32;
+  return (size_t)(MB + NB) * sizeof(double2) + ((size_t)NB * MW + NB) * 4;
 }
 
 bool reorder_needs_csc(int MB, int NB) { return reorder_bits_lds_bytes(MB, NB) > kBitsLdsLimit; }

@@ -133,9 +133,9 @@ typedef struct wa_reorder_params {
  * K/V bytes NB*b*d*4 > ws_min_bytes, 4*b*b*d*nnz >= flops_min and the pooled
  * Jaccard similarity of adjacent rows < jaccard_max.
  *   row_ptr, col_idx, csc_ptr, csc_idx  from wa_build_block_index.  The CSC may be
- *             NULL when the head's mask fits in LDS as row and column bitmasks:
- *             (MB+NB)*16 + (MB*ceil(NB/32) + NB*ceil(MB/32) + NB)*4 <= 147456 bytes
- *             (about MB = NB <= 700); the reorder then reads only the CSR
+ *             NULL when the head's mask fits in LDS as column bitmasks:
+ *             (MB+NB)*16 + (NB*ceil(MB/32) + NB)*4 <= 155648 bytes (about
+ *             MB = NB <= 972); the reorder then reads only the CSR
  *   capacity  number of entries col_idx and csc_idx hold; list entries at or beyond it
  *             are ignored (a truncated index never causes an out-of-bounds read)
  *   x0        float [H][MB][2]  raw start values (the random block of Algorithm 1)

@@ -65,7 +65,7 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert lib.wa_reorder_rows(fake, fake, fake, fake, 16, fake, 1, 5000, 4, 128, 128,
                                ctypes.byref(p), fake, fake, fake, None, None, None) == -2
     # the transposed lists are required once the mask no longer fits LDS as bitmasks
-    assert lib.wa_reorder_rows(fake, fake, None, None, 16, fake, 1, 760, 760, 128, 128,
+    assert lib.wa_reorder_rows(fake, fake, None, None, 16, fake, 1, 1000, 1000, 128, 128,
                                ctypes.byref(p), fake, fake, fake, None, None, None) == -1
     assert b"csc" in lib.wa_last_error()
     # MinHash order: coefficient ranges, hash count, geometry and sizes are checked first
@@ -109,6 +109,8 @@ def test_host_validation_rejects_bad_arguments(lib):
 def test_reorder_needs_csc_threshold(lib):
     assert lib.wa_reorder_needs_csc(591, 591) == 0
     assert lib.wa_reorder_needs_csc(16, 16) == 0
-    assert lib.wa_reorder_needs_csc(760, 760) == 1
-    assert lib.wa_reorder_needs_csc(929, 929) == 1
+    assert lib.wa_reorder_needs_csc(929, 929) == 0
+    assert lib.wa_reorder_needs_csc(972, 972) == 0
+    assert lib.wa_reorder_needs_csc(973, 973) == 1
+    assert lib.wa_reorder_needs_csc(1000, 1000) == 1
     assert lib.wa_reorder_needs_csc(0, 5) < 0

@@ -70,7 +70,7 @@ CASES = [
                                        skip_mode=caq.WA_SKIP_NEVER)),
     ("wan75k", {"heads": 4}, caq.ReorderParams(wave=64, n_slices=8, skip_mode=caq.WA_SKIP_NEVER)),
     ("gsrs75k", {"heads": 2}, caq.ReorderParams(wave=64, n_slices=8, skip_mode=caq.WA_SKIP_NEVER)),
-    # 929 blocks: the transposed-list form, very sparse Top-p masks, one lane per list
+    # 929 blocks: the column-bitmask form near its limit, very sparse Top-p masks
     ("hunyuan119k", {"heads": 3}, caq.ReorderParams(wave=64, n_slices=8,
                                                     skip_mode=caq.WA_SKIP_NEVER)),
     ("hunyuan119k", {"heads": 3}, caq.ReorderParams(wave=64, n_slices=8,
@@ -87,17 +87,29 @@ def test_reorder_matches_oracle(name, over, params):
 
 
 @pytest.mark.parametrize("mb,density", [
-    (760, 0.01),   # short lists: one lane per list, pair statistics by merging lists
-    (760, 0.05),   # four lanes per list
-    (760, 0.3),    # four lanes per list, pair statistics walked row by row per wave
-    (2100, 0.05),  # 2,100 blocks, 4,096-key sorts, statistics per wave
+    (1000, 0.005),  # one lane per list, pair statistics from LDS row bitmasks
+    (1000, 0.05),   # four lanes per list, row-bitmask statistics
+    (1200, 0.005),  # row bitmasks no longer fit: pair statistics by merging the lists
+    (1200, 0.3),    # pair statistics walked row by row per wave
+    (2100, 0.05),   # 2,100 blocks, 4,096-key sorts
 ])
 def test_reorder_from_transposed_lists_matches_oracle(mb, density):
-    """A mask too large for the LDS bitmasks takes the CSR + CSC gather form."""
+    """A mask too large for the LDS column bitmasks takes the CSR + CSC gather form."""
     w = synth.random_tiny_case(5, heads=2, seq_len=mb * 64, head_dim=64, block=64,
                                density=density, empty_rows=(3,))
     assert caq.reorder_needs_csc(mb, mb)
     banner(f"reorder {mb} x {mb} (CSC form) rho={density}")
+    _compare_with_oracle(w, caq.ReorderParams(wave=64, n_slices=8,
+                                              skip_mode=caq.WA_SKIP_NEVER))
+
+
+@pytest.mark.parametrize("mb,density", [(950, 0.05), (972, 0.3)])
+def test_reorder_bitmask_form_near_its_limit(mb, density):
+    """The largest masks that still take the column-bitmask form."""
+    w = synth.random_tiny_case(9, heads=2, seq_len=mb * 64, head_dim=64, block=64,
+                               density=density, empty_rows=(3,))
+    assert not caq.reorder_needs_csc(mb, mb)
+    banner(f"reorder {mb} x {mb} (bitmask form) rho={density}")
     _compare_with_oracle(w, caq.ReorderParams(wave=64, n_slices=8,
                                               skip_mode=caq.WA_SKIP_NEVER))
 
