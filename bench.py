@@ -273,6 +273,19 @@ def gsrs_schedule_main(args, w, params):
     recall = {name: round(float(caq.mask_recall(gs.full.w, gs.full.row_ptr, gs.full.col_idx,
                                                 m).mean().item()), 4)
               for name, m in (("candidate_set_s1", gs.s1), ("final_mask", gs.mask))}
+    # Row entropy and mean attention distance along the schedule (GSRS §4, Fig. 1), from
+    # one more run in which every attention pass also writes both (untimed).
+    diag = None
+    if args.diagnostics:
+        gd = GsrsSchedule(H, L, d, b, w.q.device, reorder=params, steps=args.schedule_steps,
+                          search_steps=search, thresholds=(0.95, 0.9, 0.85, 0.8),
+                          diagnostics=True)
+        gd.run(inputs)
+        diag = {str(t): {"kind": kind, "mean_entropy": round(float(e.item()), 4),
+                         "mean_distance_tokens": round(float(dist.item()), 1)}
+                for t, kind, e, dist in gd.trace
+                if kind == "search" or t in (0, search[0] - 1, args.schedule_steps - 1)}
+        del gd
     n = args.steps
     ms_per_run = total_ms / n
     flops = 4.0 * b * b * d * pairs / n
@@ -290,6 +303,7 @@ def gsrs_schedule_main(args, w, params):
                    "steps_by_kind": {k: gs.kinds.count(k) for k in per_kind},
                    "mask_density_after_search": densities,
                    "recall_at_last_step": recall,
+                   "diagnostics_by_step": diag,
                    "selected_tflop_per_run": round(flops / 1e12, 3),
                    "wall_ms_per_run": round(wall_ms, 3)},
     }
@@ -310,6 +324,9 @@ def main():
     ap.add_argument("--schedule-steps", type=int, default=0,
                     help="with --workload gsrs75k: run the whole GSRS denoising schedule of this "
                          "many steps (searches at 10, 20, 30, 40) per bench step")
+    ap.add_argument("--diagnostics", action="store_true",
+                    help="with --schedule-steps: also report the mean row entropy and mean "
+                         "attention distance of the search steps (one extra, untimed run)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--copy-calib-mb", type=int, default=0,

@@ -66,7 +66,16 @@ class HotPath:
                           if gsrs_p is not None else None)
         self.ws_bytes = sparse_attn_workspace_size(heads, seq_len, head_dim, block)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.entropy = None   # [H, L_pad] row attention entropy, when diagnostics are on
+        self.distance = None  # [H, L_pad] mean attention distance (tokens)
         self._params = (reorder or ReorderParams())._c()
+
+    def enable_diagnostics(self) -> None:
+        """Every later attention pass also writes the row entropy and mean attention
+        distance (wa_sparse_attn_fwd_diag, GSRS §4)."""
+        if self.entropy is None:
+            self.entropy = torch.empty(self.H, self.lp, dtype=torch.float32, device=self.device)
+            self.distance = torch.empty_like(self.entropy)
 
     def set_reorder_params(self, reorder: ReorderParams) -> None:
         """New reorder parameters for a path built with reordering."""
@@ -105,11 +114,16 @@ class HotPath:
         lib, s = self.lib, _stream(self.device)
         perm = self.perm if self.reorder is not None else None
         g = self.g if self.gsrs_p is not None else None
-        _check(lib.wa_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), self.H, self.L, self.d, self.b,
-                                      _ptr(self.row_ptr), _ptr(self.col_idx), self.cap, _ptr(perm),
-                                      self.schedule, self.d ** -0.5, _ptr(self.o), _ptr(self.lse),
-                                      _ptr(g), _ptr(self.workspace), self.ws_bytes, s),
-               "wa_sparse_attn_fwd")
+        args = (_ptr(q), _ptr(k), _ptr(v), self.H, self.L, self.d, self.b, _ptr(self.row_ptr),
+                _ptr(self.col_idx), self.cap, _ptr(perm), self.schedule, self.d ** -0.5,
+                _ptr(self.o), _ptr(self.lse), _ptr(g))
+        if self.entropy is not None:
+            _check(lib.wa_sparse_attn_fwd_diag(*args, _ptr(self.entropy), _ptr(self.distance),
+                                               _ptr(self.workspace), self.ws_bytes, s),
+                   "wa_sparse_attn_fwd_diag")
+        else:
+            _check(lib.wa_sparse_attn_fwd(*args, _ptr(self.workspace), self.ws_bytes, s),
+                   "wa_sparse_attn_fwd")
 
     def attention_plain(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
         """The attention pass without the block LSE, whatever ``gsrs_p`` is."""
@@ -216,7 +230,7 @@ class GsrsSchedule:
     def __init__(self, heads: int, seq_len: int, head_dim: int, block: int, device,
                  reorder: ReorderParams | None, steps: int = 50,
                  search_steps=(10, 20, 30, 40), thresholds=(0.95, 0.9, 0.85, 0.8),
-                 schedule: int = WA_SCHED_XCD_SLICED):
+                 schedule: int = WA_SCHED_XCD_SLICED, diagnostics: bool = False):
         if len(search_steps) != len(thresholds) or not search_steps:
             raise ValueError("one threshold per search step")
         if list(search_steps) != sorted(search_steps) or search_steps[-1] >= steps:
@@ -233,6 +247,13 @@ class GsrsSchedule:
         self.s1 = torch.zeros_like(self.ones)     # candidate set of the first search
         self.mask = torch.zeros_like(self.ones)   # current mask
         self.kinds: list[str] = []                # what each step ran
+        # With diagnostics, per step the mean row entropy and mean attention distance
+        # over the valid rows (device scalars; GSRS §4, Fig. 1 tracks both over steps).
+        self.diagnostics = diagnostics
+        self.trace: list[tuple] = []
+        if diagnostics:
+            for path in (self.full, self.search, self.sparse):
+                path.enable_diagnostics()
 
     def run(self, inputs, on_step=None) -> None:
         """Enqueue the whole schedule; ``on_step(t, kind)`` is called after each step."""
@@ -264,6 +285,12 @@ class GsrsSchedule:
                 kind = "reuse"
                 self.sparse.attention(q, k, v)
             self.kinds.append(kind)
+            if self.diagnostics:
+                path = (self.full if (t < self.T[0] or t == self.T[0]) else
+                        self.search if t in self.T else self.sparse)
+                L = path.L
+                self.trace.append((t, kind, path.entropy[:, :L].mean(),
+                                   path.distance[:, :L].mean()))
             if on_step is not None:
                 on_step(t, kind)
 

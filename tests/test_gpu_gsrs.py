@@ -4,6 +4,8 @@ G and W are compared with tolerances (fp32 against fp64); the Top-p kept sets
 are compared bit for bit for the same W, which both sides get from the seeded
 generator."""
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -11,6 +13,7 @@ import torch
 import cache_aware_query_amd as caq
 import oracle
 import synth
+from cache_aware_query_amd.pipeline import GsrsSchedule
 from helpers import banner, gpu, np64
 
 pytestmark = pytest.mark.gpu
@@ -235,3 +238,26 @@ def test_mask_recall_matches_oracle(case):
                              w.scale)
     np.testing.assert_allclose(rec.cpu().numpy(), ref, rtol=0, atol=2e-4)
     np.testing.assert_allclose(rec_all.cpu().numpy(), 1.0, rtol=0, atol=2e-4)
+
+
+def test_schedule_diagnostics_match_plain_schedule():
+    """A schedule with diagnostics gives the same outputs and masks as without, and its
+    per-step entropy and distance are finite and non-negative."""
+    dev = gpu()
+    w = synth.random_tiny_case(31, heads=2, seq_len=1200, head_dim=64, block=64, density=1.0,
+                               device=dev)
+    banner("GSRS schedule with diagnostics")
+    p = caq.ReorderParams(wave=8, n_slices=8, skip_mode=caq.WA_SKIP_NEVER)
+    kw = dict(steps=6, search_steps=(2, 4), thresholds=(0.9, 0.8))
+    a = GsrsSchedule(2, w.seq_len, 64, 64, dev, reorder=p, **kw)
+    b = GsrsSchedule(2, w.seq_len, 64, 64, dev, reorder=p, diagnostics=True, **kw)
+    inputs = lambda t: (w.q, w.k, w.v, w.x0)  # noqa: E731
+    a.run(inputs)
+    b.run(inputs)
+    torch.cuda.synchronize()
+    assert torch.equal(a.mask, b.mask) and torch.equal(a.s1, b.s1)
+    assert torch.equal(a.sparse.o, b.sparse.o) and torch.equal(a.sparse.lse, b.sparse.lse)
+    assert [k for _, k, _, _ in b.trace] == b.kinds
+    for _, _, e, dist in b.trace:
+        assert math.isfinite(float(e)) and float(e) >= 0.0
+        assert math.isfinite(float(dist)) and float(dist) >= 0.0
