@@ -453,6 +453,23 @@ def main():
                               out=(hp_mh.perm, hp_mh.inv_perm))
         minhash()
         t_minhash = _time_calls(minhash, reps)
+        # The explicit form of applying the permutation ([WA] §V: gather the Q blocks
+        # into execution order before the kernel, scatter O back after it), which the
+        # fused kernel avoids; both copies are HBM-bound.
+        lib = caq.load_library()
+        q_x, o_x = torch.empty_like(w.q), torch.empty_like(hp.o)
+        blk_bytes = b * d * w.q.element_size()
+
+        def explicit_permute():
+            caq._check(lib.wa_gather_blocks(caq._ptr(w.q), caq._ptr(q_x), caq._ptr(hp.perm), H,
+                                            mb, blk_bytes, caq._stream(dev)), "wa_gather_blocks")
+            caq._check(lib.wa_scatter_blocks(caq._ptr(hp.o), caq._ptr(o_x), caq._ptr(hp.perm), H,
+                                             mb, blk_bytes, caq._stream(dev)),
+                       "wa_scatter_blocks")
+        explicit_permute()
+        t_perm = _time_calls(explicit_permute, reps)
+        perm_bytes = 2 * 2 * H * mb * blk_bytes  # Q and O, each read and written once
+        del q_x, o_x
         ablation["minhash_order"] = hp_mh
 
         def with_schedule(path, sched):
@@ -487,6 +504,8 @@ def main():
                        "index_ms_without_reorder": round(t_index_id, 4)})
         detail.update({f"attn_ms_{k}": round(v, 4) for k, v in t.items()})
         detail["minhash_order_ms"] = round(t_minhash, 4)
+        detail["explicit_permute_ms"] = round(t_perm, 4)
+        detail["explicit_permute_gb_per_s"] = round(perm_bytes / (t_perm * 1e-3) / 1e9, 1)
         detail["e2e_ms_minhash"] = round(t_index + t_minhash + t["minhash_order"], 4)
         detail.update({"e2e_ms_reordered": round(e2e_reord, 4),
                        "e2e_ms_unreordered_best": round(e2e_plain, 4),
