@@ -122,3 +122,42 @@ def test_more_blocks_than_the_staged_list_cap():
         o_ref, l_ref = oracle.masked_attention_rows(qn, kn, vn, m, rows, L, b, w.scale)
         assert_attention_close(np64(o[0, rows]), lse[0, rows].cpu().numpy().astype(np.float64),
                                o_ref, l_ref, f"row block {u}")
+
+
+def test_the_largest_supported_mask():
+    """WA_MAX_BLOCKS = 4,096 query and key blocks (block 64, ragged last block): the
+    reorder's statistics, angles and permutation against the oracle, the attention's
+    global-list path on sampled rows, and the MinHash order bit for bit."""
+    dev = gpu()
+    mb, b, d = 4096, 64, 64
+    L = mb * b - 17
+    banner(f"largest mask: L={L} b={b} d={d} MB={mb}")
+    w = synth.random_tiny_case(83, heads=1, seq_len=L, head_dim=d, block=b, density=0.001,
+                               empty_rows=(7,))
+    assert w.mask.shape[1] == mb and caq.reorder_needs_csc(mb, mb)
+    q, k, v, mask, x0 = (t.to(dev) for t in (w.q, w.k, w.v, w.mask, w.x0))
+    idx = caq.build_block_index(mask)
+    params = caq.ReorderParams(wave=64, n_slices=8, iters=5, skip_mode=caq.WA_SKIP_NEVER)
+    ro = caq.reorder_rows(idx, x0, b, d, params)
+    o, lse, _ = caq.sparse_attn_fwd(q, k, v, L, b, idx.row_ptr, idx.col_idx, perm=ro.perm)
+    a_mh, b_mh = synth.minhash_params(2)
+    perm_mh, _ = caq.minhash_order(idx, a_mh, b_mh, 64, 8)
+    torch.cuda.synchronize()
+    m_all = w.mask.cpu().numpy()
+    op = oracle.ReorderParams(wave=64, n_slices=8, iters=5, skip_mode=oracle.reorder.SKIP_NEVER)
+    perm_o, _, _, ang_o, st_o = oracle.reorder_rows(m_all, w.x0.cpu().numpy().astype(np.float64),
+                                                    b, d, op)
+    np.testing.assert_array_equal(ro.stats.cpu().numpy(), st_o)
+    ang_g = ro.angles.cpu().numpy()[0]
+    both = np.isfinite(ang_o[0])
+    np.testing.assert_allclose(ang_g[both], ang_o[0][both], atol=1e-9, rtol=0)
+    assert sorted(ro.perm.cpu().numpy()[0].tolist()) == list(range(mb))
+    np.testing.assert_array_equal(perm_mh.cpu().numpy(),
+                                  oracle.minhash_order(m_all, a_mh, b_mh, 64, 8)[0])
+    qn, kn, vn = np64(w.q)[0], np64(w.k)[0], np64(w.v)[0]
+    m = m_all[0]
+    for u in (0, 7, 2048, mb - 1):
+        rows = np.arange(u * b, min((u + 1) * b, L))[::5]
+        o_ref, l_ref = oracle.masked_attention_rows(qn, kn, vn, m, rows, L, b, w.scale)
+        assert_attention_close(np64(o[0, rows]), lse[0, rows].cpu().numpy().astype(np.float64),
+                               o_ref, l_ref, f"row block {u}")
