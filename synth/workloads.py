@@ -8,7 +8,7 @@ a fixed seed with the same shapes: video token grids (t, y, x) flattened to one
 sequence, head dimension 128, block size 128, and block masks whose density and
 row-length spread resemble dynamic sparse attention.
 
-Five workloads are defined (``CONFIGS``):
+Seven workloads are defined (``CONFIGS``):
 
 ``tiny``         1 head, d=64, grid 4x16x16 (L=1,024), block 64.  Q/K/V are
                  fp32 N(0,1) rounded to bf16.  Mask: diagonal plus Bernoulli(0.5),
@@ -29,6 +29,10 @@ Five workloads are defined (``CONFIGS``):
 ``random20``     The Wan shape with structureless masks: every block Bernoulli(0.2)
                  plus the diagonal, the random-mask locality floor of WaveAlign
                  Table I.
+``wan364k``      The ``wan75k`` recipe at the length WaveAlign profiles its locality
+                 and stage ablation on (§VI-D Fig. 11, §VI-E Fig. 12: 401 frames at
+                 720x1280): grid 101x45x80 (L=363,600, 2,841 blocks per side), 40
+                 heads.
 
 Any field can be overridden (``make_workload("wan75k", grid=(9, 45, 80),
 heads=16, density=0.1)``): ``density`` fixes the Top-k budget of every head,
@@ -94,6 +98,7 @@ CONFIGS = {
     "gsrs75k": WorkloadConfig("gsrs75k", 4, 40, 128, (21, 45, 80), 128, "smooth", "dense"),
     "random20": WorkloadConfig("random20", 5, 40, 128, (21, 45, 80), 128, "smooth", "random",
                                density=0.2),
+    "wan364k": WorkloadConfig("wan364k", 6, 40, 128, (101, 45, 80), 128, "smooth", "topk"),
 }
 
 

@@ -68,3 +68,11 @@ def test_random_mask_density_and_diagonal():
     assert torch.all(torch.diagonal(m, dim1=1, dim2=2) == 1)
     dens = m.float().mean().item()
     assert abs(dens - (0.2 + 0.8 / nb)) < 0.03, dens
+
+
+def test_long_wan_geometry():
+    # 401 frames at 720x1280: (401 - 1) / 4 + 1 = 101 latent frames, and 720 / 16 by
+    # 1280 / 16 = 45 x 80 tokens per frame (8x spatial compression, 2x2 patches)
+    cfg = synth.get_config("wan364k")
+    assert cfg.seq_len == 363600 and cfg.num_blocks == 2841 and cfg.padded_len == 363648
+    assert cfg.heads == 40 and cfg.head_dim == 128 and cfg.mask == "topk"
