@@ -63,38 +63,185 @@ __global__ __launch_bounds__(256) void k_block_importance(const float* __restric
   }
 }
 
-// One wavefront per query-block row: sort the candidates by (W descending, block
-// id ascending) with a bitonic sort of 64-bit keys in LDS (n2 = the candidate count
-// rounded up to a power of two), then walk them in that order with a wave-uniform
-// fp64 running total (the order of the additions fixes the rounding of the total,
-// and the kept set depends on it) and keep blocks while the total before them is
-// at most p.
-__global__ __launch_bounds__(64) void k_topp(const float* __restrict__ W,
-                                             const int32_t* __restrict__ row_ptr,
-                                             const int32_t* __restrict__ col_idx, int cap,
-                                             int NB, double p, uint8_t* __restrict__ mask_out) {
+// Top-p key of a candidate: (W descending, block id ascending) as one unsigned
+// 64-bit key, so that ascending key order is the selection order.  NaN and
+// negative weights rank as zero; a real key is below 2^63, the padding key ~0.
+__device__ inline uint64_t topp_key(float w, int32_t v) {
+  if (!(w > 0.0f)) w = 0.0f;
+  return ((uint64_t)(0x7FFFFFFFu - __float_as_uint(w)) << 32) | (uint32_t)v;
+}
+
+__device__ inline float topp_weight(uint64_t key) {
+  return __uint_as_float(0x7FFFFFFFu - (uint32_t)(key >> 32));
+}
+
+// Rows up to kToppRegMax candidates are sorted in registers; longer rows (possible
+// only when NB > kToppRegMax) take the LDS kernel below.
+constexpr int kToppRegMax = 1024;
+
+__device__ inline uint64_t shfl_xor_u64(uint64_t x, int m) {
+  const int lo = __shfl_xor((int)(uint32_t)x, m), hi = __shfl_xor((int)(uint32_t)(x >> 32), m);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// One chunk of the walk: lane j holds the weight of the chunk's element j (m
+// elements, zero beyond).  Adds them in lane order to the wave-uniform running
+// total acc and returns false when every element is kept (acc then includes them
+// all); otherwise returns true with j_kept = the elements kept before the first
+// whose preceding total exceeds p (the cut; acc is then no longer needed).  A whole
+// chunk is kept when the total before its last element is at most p, since a total
+// of non-negative terms never decreases; only the chunk holding the cut, and a
+// partial last chunk, are walked element by element.
+__device__ __forceinline__ bool walk_chunk(double wd, int m, double p, double& acc, int& j_kept) {
+  const int lo = __double2loint(wd), hi = __double2hiint(wd);
+  auto lane_w = [&](int j) {
+    return __hiloint2double(__builtin_amdgcn_readlane(hi, j), __builtin_amdgcn_readlane(lo, j));
+  };
+  if (m == 64) {
+    double a = acc;
+#pragma unroll 3
+    for (int j = 0; j < 63; ++j) a += lane_w(j);
+    const bool whole = !(a > p);
+    a += lane_w(63);
+    if (whole) {
+      acc = a;
+      return false;
+    }
+  }
+  int j = 0;
+  double a = acc;
+  for (; j < m && !(a > p); ++j) a += lane_w(j);
+  acc = a;
+  j_kept = j;
+  return j < m;
+}
+
+// Cross-lane stages of the register bitonic sort for one `size`: pairs `stride`
+// lanes apart in the same register, stride = first, first/2, .., 1 (first <= 32).
+// The direction of a pair follows bit `size` of its element index 64*r + lane,
+// which comes from the lane when size < 64 and from r otherwise.
+template <int R>
+__device__ __forceinline__ void bitonic_across_lanes(uint64_t (&k)[R], int lane, int size,
+                                                     int first) {
+  const bool lane_asc = (lane & size) == 0;
+#pragma unroll 1
+  for (int stride = first; stride > 0; stride >>= 1) {
+    const bool lower = (lane & stride) == 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool asc = lane_asc && ((64 * r) & size) == 0;
+      const uint64_t o = shfl_xor_u64(k[r], stride);
+      // the lower element of an ascending pair keeps the smaller key
+      const bool take_other = (k[r] < o) != (lower == asc);
+      k[r] = take_other ? o : k[r];
+    }
+  }
+}
+
+// Bitonic sort, ascending, of the 64*R keys held as element i = 64*r + lane in
+// register r of each lane: pairs 64 or more elements apart (rs = stride/64
+// registers) exchange within a lane, closer pairs across lanes.
+template <int R>
+__device__ __forceinline__ void bitonic_sort_reg(uint64_t (&k)[R], int lane) {
+#pragma unroll 1
+  for (int size = 2; size <= 64; size <<= 1) bitonic_across_lanes<R>(k, lane, size, size >> 1);
+#pragma unroll
+  for (int size = 128; size <= 64 * R; size <<= 1) {
+#pragma unroll
+    for (int rs = size / 128; rs >= 1; rs >>= 1) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (r & rs) continue;
+        const bool asc = ((64 * r) & size) == 0;
+        const uint64_t a = k[r], b = k[r | rs];
+        const bool sw = (b < a) == asc;  // equal keys may swap: nothing changes
+        k[r] = sw ? b : a;
+        k[r | rs] = sw ? a : b;
+      }
+    }
+    bitonic_across_lanes<R>(k, lane, size, 32);
+  }
+}
+
+// One row of n <= 64*R candidates on one wavefront: the keys are sorted in
+// registers, then walked in sorted order chunk by chunk (chunk r is register r).
+template <int R>
+__device__ __forceinline__ void topp_row_reg(const float* __restrict__ W,
+                                             const int32_t* __restrict__ col_idx, int e0, int n,
+                                             int NB, double p, uint8_t* flags, int lane) {
+  uint64_t k[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = 64 * r + lane;
+    k[r] = i < n ? topp_key(W[e0 + i], col_idx[e0 + i]) : ~0ull;
+  }
+  bitonic_sort_reg<R>(k, lane);
+  double acc = 0.0;
+  int kept = n;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (64 * r >= n) break;
+    const int m = min(64, n - 64 * r);
+    const double wd = 64 * r + lane < n ? (double)topp_weight(k[r]) : 0.0;
+    int j;
+    if (walk_chunk(wd, m, p, acc, j)) {
+      kept = 64 * r + j;
+      break;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int v = (int)(uint32_t)k[r];
+    if (64 * r + lane < kept && v >= 0 && v < NB) flags[v] = 1;
+  }
+}
+
+// One wavefront per query-block row with at most kToppRegMax candidates (rows with
+// more are left to k_topp_lds): the row's NB mask bytes are built in LDS and
+// written once.
+__global__ __launch_bounds__(64) void k_topp_reg(const float* __restrict__ W,
+                                                 const int32_t* __restrict__ row_ptr,
+                                                 const int32_t* __restrict__ col_idx, int cap,
+                                                 int NB, double p, uint8_t* __restrict__ mask_out) {
+  extern __shared__ uint8_t flags[];
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int e0 = min(row_ptr[row], cap), e1 = min(row_ptr[row + 1], cap);
+  int n2max = 1;
+  while (n2max < NB) n2max <<= 1;
+  const int n = max(0, min(e1 - e0, n2max));  // a well-formed row has at most NB entries
+  if (n > kToppRegMax) return;
+  for (int v = lane; v < NB; v += 64) flags[v] = 0;
+  __syncthreads();
+  if (n > 512) topp_row_reg<16>(W, col_idx, e0, n, NB, p, flags, lane);
+  else if (n > 256) topp_row_reg<8>(W, col_idx, e0, n, NB, p, flags, lane);
+  else if (n > 128) topp_row_reg<4>(W, col_idx, e0, n, NB, p, flags, lane);
+  else if (n > 64) topp_row_reg<2>(W, col_idx, e0, n, NB, p, flags, lane);
+  else if (n > 0) topp_row_reg<1>(W, col_idx, e0, n, NB, p, flags, lane);
+  __syncthreads();
+  uint8_t* out = mask_out + (size_t)row * NB;
+  for (int v = lane; v < NB; v += 64) out[v] = flags[v];
+}
+
+// Rows with more than kToppRegMax candidates: a bitonic sort of the 64-bit keys in
+// LDS (n2 = the candidate count rounded up to a power of two), then the same walk
+// one element at a time.
+__global__ __launch_bounds__(64) void k_topp_lds(const float* __restrict__ W,
+                                                 const int32_t* __restrict__ row_ptr,
+                                                 const int32_t* __restrict__ col_idx, int cap,
+                                                 int NB, double p, uint8_t* __restrict__ mask_out) {
   extern __shared__ uint64_t key[];
   const int row = blockIdx.x;
   const int lane = threadIdx.x;
   const int e0 = min(row_ptr[row], cap), e1 = min(row_ptr[row + 1], cap);
   int n2max = 1;  // LDS keys allocated by the launcher
   while (n2max < NB) n2max <<= 1;
-  const int n = max(0, min(e1 - e0, n2max));  // a well-formed row has at most NB entries
+  const int n = max(0, min(e1 - e0, n2max));
+  if (n <= kToppRegMax) return;  // k_topp_reg's row
   uint8_t* out = mask_out + (size_t)row * NB;
-  for (int v = lane; v < NB; v += 64) out[v] = 0;
-  if (n <= 0) return;
   int n2 = 1;
   while (n2 < n) n2 <<= 1;
-  for (int i = lane; i < n2; i += 64) {
-    if (i < n) {
-      float w = W[e0 + i];
-      if (!(w >= 0.0f)) w = 0.0f;  // NaN or negative weights rank last
-      const uint32_t wb = __float_as_uint(w);
-      key[i] = ((uint64_t)(0x7FFFFFFFu - wb) << 32) | (uint32_t)col_idx[e0 + i];
-    } else {
-      key[i] = ~0ull;
-    }
-  }
+  for (int i = lane; i < n2; i += 64) key[i] = i < n ? topp_key(W[e0 + i], col_idx[e0 + i]) : ~0ull;
   for (int size = 2; size <= n2; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       __syncthreads();
@@ -112,18 +259,25 @@ __global__ __launch_bounds__(64) void k_topp(const float* __restrict__ W,
   }
   __syncthreads();
   double acc = 0.0;
-  for (int c = 0; c < n && !(acc > p); c += 64) {
-    const uint64_t mine = c + lane < n ? key[c + lane] : ~0ull;
-    const uint32_t klo = (uint32_t)mine, khi = (uint32_t)(mine >> 32);
+  int kept = n;
+  for (int c = 0; c < n; c += 64) {
     const int m = min(64, n - c);
-    for (int j = 0; j < m; ++j) {
-      if (acc > p) break;
-      const uint32_t wv = 0x7FFFFFFFu - __builtin_amdgcn_readlane(khi, j);
-      const int v = (int)__builtin_amdgcn_readlane(klo, j);
-      if (lane == 0 && v >= 0 && v < NB) out[v] = 1;
-      acc += (double)__uint_as_float(wv);
+    const double wd = c + lane < n ? (double)topp_weight(key[c + lane]) : 0.0;
+    int j;
+    if (walk_chunk(wd, m, p, acc, j)) {
+      kept = c + j;
+      break;
     }
   }
+  uint8_t* flags = reinterpret_cast<uint8_t*>(key + n2max);
+  for (int v = lane; v < NB; v += 64) flags[v] = 0;
+  __syncthreads();
+  for (int i = lane; i < kept; i += 64) {
+    const int v = (int)(uint32_t)key[i];
+    if (v >= 0 && v < NB) flags[v] = 1;
+  }
+  __syncthreads();
+  for (int v = lane; v < NB; v += 64) out[v] = flags[v];
 }
 
 // Attention recall of a mask per query block: one wavefront per CSR row; lanes
@@ -181,8 +335,12 @@ hipError_t launch_topp(const float* w, const int32_t* row_ptr, const int32_t* co
   const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
   int n2 = 1;
   while (n2 < NB) n2 <<= 1;  // a row has at most NB candidates
-  hipLaunchKernelGGL(k_topp, dim3(H * MB), dim3(64), (size_t)n2 * sizeof(uint64_t), s, w,
-                     row_ptr, col_idx, cap, NB, p, mask_out);
+  hipLaunchKernelGGL(k_topp_reg, dim3(H * MB), dim3(64), (size_t)((NB + 3) & ~3), s, w, row_ptr,
+                     col_idx, cap, NB, p, mask_out);
+  if (n2 > kToppRegMax)  // keys, then the row's mask bytes
+    hipLaunchKernelGGL(k_topp_lds, dim3(H * MB), dim3(64),
+                       (size_t)n2 * sizeof(uint64_t) + (size_t)((NB + 3) & ~3), s, w, row_ptr,
+                       col_idx, cap, NB, p, mask_out);
   return hipGetLastError();
 }
 

@@ -111,6 +111,30 @@ def test_topp_is_bit_exact_for_a_given_w(p):
         assert int(ref[0, 9].sum()) == 91
 
 
+@pytest.mark.parametrize("p", [0.5, 0.9, 1.0])
+def test_topp_rows_of_every_length_class(p):
+    # Rows of 0..1,500 candidates: each side of every register-sort size (64, 128, 256,
+    # 512 and 1,024 keys) and rows longer than 1,024, which take the LDS sort.
+    dev = gpu()
+    rng = np.random.default_rng(37)
+    lengths = [0, 1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513, 700, 1023,
+               1024, 1025, 1200, 1500]
+    H, nb = 2, 1500
+    mb = len(lengths)
+    mask = np.zeros((H, mb, nb), dtype=np.uint8)
+    for h in range(H):
+        for u, n in enumerate(lengths):
+            mask[h, u, rng.choice(nb, size=n, replace=False)] = 1
+    rp, ci, _, _, _ = oracle.block_index(mask)
+    w = _random_weights(rng, rp)
+    banner(f"topp length classes p={p}")
+    sel = caq.topp_select(torch.from_numpy(w).to(dev), torch.from_numpy(rp.astype(np.int32)).to(dev),
+                          torch.from_numpy(ci.astype(np.int32)).to(dev), H, mb, nb, p)
+    torch.cuda.synchronize()
+    ref = oracle.topp_select(w, rp, ci, H, mb, nb, p)
+    np.testing.assert_array_equal(sel.cpu().numpy(), ref)
+
+
 def test_gsrs_search_pipeline_growing_sparsity():
     """Dense pass -> W -> Top-p(0.9) = S1; pass over S1 -> W over S1 -> Top-p(0.8) = S2."""
     dev = gpu()
