@@ -161,3 +161,50 @@ def test_the_largest_supported_mask():
         o_ref, l_ref = oracle.masked_attention_rows(qn, kn, vn, m, rows, L, b, w.scale)
         assert_attention_close(np64(o[0, rows]), lse[0, rows].cpu().numpy().astype(np.float64),
                                o_ref, l_ref, f"row block {u}")
+
+
+def test_long_sequence_sampled():
+    # The 363,600-token shape (2,841 blocks per side) on 4 of its 40 heads: the reorder
+    # takes the transposed-list form, the attention reads its lists from global memory
+    # (more than 2,048 blocks), and Top-p sorts rows of hundreds of keys in registers.
+    dev = gpu()
+    banner("long sequence: generating wan364k, 4 heads")
+    w = synth.make_workload("wan364k", device=dev, heads=4)
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    nnz = int(w.mask.sum())
+    _, _, wave = caq.schedule_info(0, w.head_dim)
+    params = caq.ReorderParams(wave=wave, n_slices=8, skip_mode=caq.WA_SKIP_NEVER)
+    hp = HotPath(H, w.seq_len, w.head_dim, w.block, dev, capacity=nnz, reorder=params, gsrs_p=0.9)
+    assert hp.with_csc
+    banner(f"long sequence: H={H} MB={mb} nnz={nnz}")
+    hp.step(w.q, w.k, w.v, w.mask, w.x0)
+    torch.cuda.synchronize()
+    perm = hp.perm.cpu().numpy()
+    for h in range(H):
+        assert sorted(perm[h].tolist()) == list(range(mb))
+    assert not torch.isnan(hp.o[:, : w.seq_len]).any()
+    rp = hp.row_ptr.cpu().numpy()
+    ci = hp.col_idx.cpu().numpy()
+    wts = hp.w.cpu().numpy()
+    sel = hp.next_mask.cpu().numpy()
+    mask = w.mask.cpu().numpy()
+    rng = np.random.default_rng(11)
+    samples = _sample_rows(w, rng, n_heads=2, n_blocks=3)
+    cached = {}
+    for h, u, rows in samples:
+        if h not in cached:
+            cached.clear()
+            cached[h] = tuple(np64(t[h]) for t in (w.q, w.k, w.v))
+        qh, kh, vh = cached[h]
+        o_ref, l_ref = oracle.masked_attention_rows(qh, kh, vh, mask[h], rows, w.seq_len,
+                                                    w.block, w.scale)
+        assert_attention_close(np64(hp.o[h])[rows],
+                               hp.lse[h].cpu().numpy().astype(np.float64)[rows], o_ref, l_ref,
+                               f"wan364k h={h} u={u}")
+        # Top-p of this row from the same W, bit for bit
+        lo, hi = int(rp[h * mb + u]), int(rp[h * mb + u + 1])
+        assert abs(float(wts[lo:hi].astype(np.float64).sum()) - 1.0) < 1e-4
+        ref = oracle.topp_select(wts[lo:hi], np.array([0, hi - lo]), ci[lo:hi], 1, 1, mb, 0.9)
+        np.testing.assert_array_equal(sel[h, u], ref[0, 0], err_msg=f"top-p h={h} u={u}")
+    lengths = np.diff(rp)
+    print(f"wan364k: longest row {lengths.max()} blocks, mean {lengths.mean():.1f}")
