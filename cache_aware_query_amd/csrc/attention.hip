@@ -110,6 +110,10 @@ constexpr float kTau = 8.0f;
 // A quarter whose maximum lies more than kLow below the reference takes its
 // own maximum as reference, so that its block log-sum-exp keeps full precision.
 constexpr float kLow = 64.0f;
+// Bounds on a lane's sum of one quarter's probabilities (16 keys) under which the
+// quarter keeps the current reference without taking its maximum.
+constexpr float kSumMax = 256.0f;                 // 2^kTau
+constexpr float kSumMin = 1.2621774483536189e-29f;  // 2^-96
 
 template <int N>
 __device__ inline void wait_vmcnt() {
@@ -371,7 +375,7 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   int e_pending = -1;
 
   // Row maximum of a masked quarter and the reference decisions that follow from it.
-  auto decide = [&](const f32x16& acc) {
+  auto decide = [&](const f32x16& acc) __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
@@ -391,42 +395,35 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     return d;
   };
 
-  // Probabilities of quarter q (in acc, decided by d), packed to bf16 for P.V;
-  // updates the running reference and sum and, at the tile's last quarter, the
-  // pending block LSE of the tile.
-  auto softmax = [&](const f32x16& acc, const QuarterDecision& d, int v, int q, bf16x8(&pb)[2]) {
+  // Probabilities of a quarter against exponent offset c, packed to bf16 for P.V;
+  // returns this lane's sum of the packed values.
+  auto exps = [&](const f32x16& acc, float c, bf16x8(&pb)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        pb[ps][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc[8 * ps + j], scale_log2, -d.c));
-    const float psum = sum8(pb[1], sum8(pb[0], 0.0f));
-    float lsum = psum;
+        pb[ps][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc[8 * ps + j], scale_log2, -c));
+    return sum8(pb[1], sum8(pb[0], 0.0f));
+  };
+
+  // Bookkeeping of quarter q once its probabilities are fixed: pb against the
+  // running reference (lane sum lsum), and the lane sum psum of the same keys
+  // against the block-statistic offset c_g.  Adds to the running sum and, at the
+  // tile's last quarter, sets the pending block LSE of the tile.
+  auto account = [&](const f32x16& acc, float c_g, float psum, float lsum, int v, int q,
+                     const bf16x8(&pb)[2]) __attribute__((always_inline)) {
     if constexpr (WITH_G) {
       const int qi = q % kQ;
-      if (d.any_low) {
-        // Lanes whose quarter sits far below the reference: their output share uses
-        // the common reference (a value 2^-64 below it or smaller).
-        if (d.m_h < d.m_ref - kLow) {
-          const float cr = d.m_ref == -INFINITY ? 0.0f : d.m_ref;
-#pragma unroll
-          for (int ps = 0; ps < 2; ++ps)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              pb[ps][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc[8 * ps + j], scale_log2, -cr));
-          lsum = sum8(pb[1], sum8(pb[0], 0.0f));
-        }
-      }
       if (qi == 0) {
-        blk_m = d.c_g;
+        blk_m = c_g;
         blk_s = psum;
-      } else if (__builtin_amdgcn_ballot_w64(d.c_g != blk_m) == 0) {
+      } else if (__builtin_amdgcn_ballot_w64(c_g != blk_m) == 0) {
         blk_s += psum;  // the usual case: the tile keeps one offset
       } else {
-        const float nm = fmaxf(blk_m, d.c_g);
+        const float nm = fmaxf(blk_m, c_g);
         if (nm != -INFINITY)
           blk_s = blk_s * __builtin_amdgcn_exp2f(blk_m - nm) +
-                  psum * __builtin_amdgcn_exp2f(d.c_g - nm);
+                  psum * __builtin_amdgcn_exp2f(c_g - nm);
         blk_m = nm;
       }
       if (qi == kQ - 1) {
@@ -453,11 +450,53 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
           es = fmaf(p, fmaxf(acc[8 * ps + j], -3.0e38f), es);
           ds = fmaf(p, fabsf(d0 - (float)(16 * ps + j)), ds);
         }
-      es_run = es_run * d.alpha + es;
-      ds_run = ds_run * d.alpha + ds;
+      es_run += es;
+      ds_run += ds;
     }
-    l_run = l_run * d.alpha + lsum;
-    m_run = d.m_ref;
+    l_run += lsum;
+  };
+
+  // Softmax of quarter q (S in acc, masked).  The probabilities are first taken
+  // against the current reference, without the row maximum: if every lane's sum
+  // of them lies in [kSumMin, 2^kTau], no probability exceeds 2^kTau (so the
+  // reference would not move) and, with G, each lane's largest probability is at
+  // least kSumMin / 16, a normal number whose block sum keeps full precision.  That
+  // is the usual case after the first quarter.  Otherwise (the first quarter, a
+  // rising maximum, a quarter far below the reference, masked keys) the wave takes
+  // the row maximum and decides as above, recomputing the probabilities if the
+  // offset changed, and rescales O^T if the reference moved.
+  auto quarter = [&](const f32x16& acc, int v, int q, bf16x8(&pb)[2]) __attribute__((always_inline)) {
+    const float c0 = m_run == -INFINITY ? 0.0f : m_run;
+    float psum = exps(acc, c0, pb);
+    float lsum = psum;
+    float c_g = m_run;
+    const bool bad = m_run == -INFINITY || !(psum <= kSumMax) || (WITH_G && psum < kSumMin);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+      const QuarterDecision d = decide(acc);
+      if (d.any_grow) {  // the reference moved on some lane: rescale what it weighs
+#pragma unroll
+        for (int dt = 0; dt < T::kDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[dt][r] *= d.alpha;
+        l_run *= d.alpha;
+        if constexpr (DIAG) {
+          es_run *= d.alpha;
+          ds_run *= d.alpha;
+        }
+      }
+      m_run = d.m_ref;
+      c_g = d.c_g;
+      if (__builtin_amdgcn_ballot_w64(d.c != c0) != 0) psum = exps(acc, d.c, pb);
+      lsum = psum;
+      if constexpr (WITH_G) {
+        if (d.any_low) {
+          // Lanes whose quarter sits far below the reference: their output share uses
+          // the common reference (a value 2^-64 below it or smaller).
+          if (d.m_h < d.m_ref - kLow) lsum = exps(acc, d.m_ref == -INFINITY ? 0.0f : d.m_ref, pb);
+        }
+      }
+    }
+    account(acc, c_g, psum, lsum, v, q, pb);
   };
 
   // O^T += V^T P^T over one quarter (key tile mt of the half in a V buffer).  The V
@@ -493,12 +532,11 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
   };
 
-  // One quarter step.  On entry S of quarter q is in acc[MT] with its decision dec.
+  // One quarter step.  On entry S of quarter q is in acc[MT], masked.
   // Copies: K of half hh+2 is issued at the middle of half hh (once K of half hh is
   // consumed) and V of half hh+1 at its start; each is awaited one half later, with
   // only the younger copies (loads retire in order) left in flight.
   f32x16 acc[2];
-  QuarterDecision dec;
   bf16x8 pb[2];
   // ids[i] is the list entry of tile t0 + i, t0 the tile of the step's first half.
   auto step = [&](auto mt_c, auto buf_c, int q, int t0, const int (&ids)[4]) {
@@ -520,16 +558,9 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     // is unused) while this quarter's softmax runs.
     if constexpr (MT == 0) compute_s(acc[1], P ? sk1 : sk0, 1);
     else compute_s(acc[0], P ? sk0 : sk1, 0);
-    softmax(acc[MT], dec, id_of_half(hh), q, pb);
-    if (dec.any_grow) {
-#pragma unroll
-      for (int dt = 0; dt < T::kDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[dt][r] *= dec.alpha;
-    }
+    quarter(acc[MT], id_of_half(hh), q, pb);
     if (q + 1 < NQ) mask_s(acc[1 - MT], id_of_half((q + 1) >> 1), q + 1);
     pv(pb, P ? sv1 : sv0, MT);
-    dec = decide(acc[1 - MT]);
   };
 
   // Prologue: K of halves 0 and 1 and V of half 0; S of quarter 0.
@@ -547,7 +578,6 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   __syncthreads();
   compute_s(acc[0], sk0, 0);
   mask_s(acc[0], ids[0], 0);
-  dec = decide(acc[0]);
 
   // Each iteration runs two halves (four quarters); the list entries it needs
   // (tiles t0 .. t0+3 at most) are read one iteration ahead.
