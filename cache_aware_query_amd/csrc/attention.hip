@@ -201,12 +201,13 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    float* __restrict__ ENT, float* __restrict__ DIST,
                    const int* __restrict__ sched_ws) {
   using T = Tile<BLOCK, D>;
-  // Two K and two V^T half-tile buffers, separate LDS objects so that the compiler
-  // can tell the asynchronous copies into one from the reads of another.
-  __shared__ __attribute__((aligned(1024))) char sk0[T::kSubBytes];
-  __shared__ __attribute__((aligned(1024))) char sk1[T::kSubBytes];
-  __shared__ __attribute__((aligned(1024))) char sv0[T::kSubBytes];
-  __shared__ __attribute__((aligned(1024))) char sv1[T::kSubBytes];
+  // Two K and two V half-tile buffers in one LDS array, so that every operand read
+  // is a loop-invariant per-lane address plus a constant offset.
+  __shared__ __attribute__((aligned(1024))) char kvbuf[4 * T::kSubBytes];
+  char* const sk0 = kvbuf;
+  char* const sk1 = kvbuf + T::kSubBytes;
+  char* const sv0 = kvbuf + 2 * T::kSubBytes;
+  char* const sv1 = kvbuf + 3 * T::kSubBytes;
   __shared__ int32_t blist[STAGED ? kListCap + 4 : 4];
 
   const int Lp = MB * BLOCK;
