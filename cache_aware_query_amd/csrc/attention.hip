@@ -105,14 +105,15 @@ constexpr int kListCap = 2048;
 // Lazy softmax reference: the running maximum used as the exponent reference
 // only moves when a new block maximum exceeds it by more than kTau (log2
 // units), so most tiles need no rescale of the output accumulator; the
-// probabilities stay below 2^kTau, far inside bf16 and fp32 range.
-constexpr float kTau = 8.0f;
+// probabilities stay below 2^kTau, far inside bf16 and fp32 range (a row's sum of
+// them, and its products with V, stay below 2^60 for any list length here).
+constexpr float kTau = 32.0f;
 // A quarter whose maximum lies more than kLow below the reference takes its
 // own maximum as reference, so that its block log-sum-exp keeps full precision.
 constexpr float kLow = 64.0f;
 // Bounds on a lane's sum of one quarter's probabilities (16 keys) under which the
 // quarter keeps the current reference without taking its maximum.
-constexpr float kSumMax = 256.0f;                 // 2^kTau
+constexpr float kSumMax = 4294967296.0f;            // 2^kTau
 constexpr float kSumMin = 1.2621774483536189e-29f;  // 2^-96
 
 template <int N>
@@ -472,6 +473,16 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     float lsum = psum;
     float c_g = m_run;
     const bool bad = m_run == -INFINITY || !(psum <= kSumMax) || (WITH_G && psum < kSumMin);
+    // Order of the region that also holds the next quarter's S^T product: its K
+    // operand reads first, then a few of these VALU instructions before the first
+    // MFMA waits on its read, then one MFMA per six VALU instructions.
+    __builtin_amdgcn_sched_group_barrier(0x100, T::kKS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+#pragma unroll
+    for (int i = 0; i < T::kKS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
     if (__builtin_amdgcn_ballot_w64(bad) != 0) {
       const QuarterDecision d = decide(acc);
       if (d.any_grow) {  // the reference moved on some lane: rescale what it weighs
@@ -513,6 +524,7 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                  8 * (tr_s & 1);
   }
   auto pv = [&](const bf16x8(&pb)[2], const char* sv, int mt) {
+    bf16x8 a[2][T::kDT];
 #pragma unroll
     for (int p2 = 0; p2 < 2; ++p2) {
       const int ps = 2 * mt + p2;
@@ -521,10 +533,18 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         const char* base = sv + tr_off[dt] + 16 * ps * (D * 2);
         const i16x4 lo = lds_read_tr16(base);
         const i16x4 hi = lds_read_tr16(base + 4 * (D * 2));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[p2], acc_o[dt], 0, 0, 0);
+        a[p2][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2)
+#pragma unroll
+      for (int dt = 0; dt < T::kDT; ++dt)
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[p2][dt], pb[p2], acc_o[dt], 0, 0, 0);
+    // Every V operand read is issued before the first MFMA, so that each MFMA waits
+    // only for its own pair of reads, not for reads issued just before it.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * T::kDT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * T::kDT, 0);
   };
   auto store_pending_g = [&]() {
     if constexpr (WITH_G) {
