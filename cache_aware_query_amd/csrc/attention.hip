@@ -331,20 +331,29 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       dma16_group<kGroup>(base + gq * 4096, voff, lv[buf] + (uint32_t)(gq * 4096));
   };
 
-  // S^T of one 32-key tile (key tile mt of the half in a K buffer).
-  auto compute_s = [&](f32x16& acc, const char* sk, int mt) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  // K operands of the S^T product of one 32-key tile (key tile mt of the half in a
+  // K buffer), then the product itself.
+  auto load_k = [&](bf16x8(&ka)[T::kKS], const char* sk, int mt) {
     const int krow = mt * 32 + pi_row(i32);
     const char* base = sk + krow * (D * 2);
     const int sw = swz_k<T::kKChunks>(krow);
 #pragma unroll
-    for (int ks = 0; ks < T::kKS; ++ks) {
-      const int c = 2 * ks + g;
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(base + 16 * (c ^ sw)));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], acc, 0, 0, 0);
-    }
+    for (int ks = 0; ks < T::kKS; ++ks)
+      ka[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(base + 16 * ((2 * ks + g) ^ sw)));
   };
+  auto mfma_s = [&](f32x16& acc, const bf16x8(&ka)[T::kKS]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < T::kKS; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], acc, 0, 0, 0);
+  };
+  auto compute_s = [&](f32x16& acc, const char* sk, int mt) {
+    bf16x8 ka[T::kKS];
+    load_k(ka, sk, mt);
+    mfma_s(acc, ka);
+  };
+
   // Keys past L (last tile) and every key of an invalid list entry leave the softmax.
   auto mask_s = [&](f32x16& acc, int v, int q) {
     const int hh = q >> 1;
@@ -473,11 +482,10 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     float lsum = psum;
     float c_g = m_run;
     const bool bad = m_run == -INFINITY || !(psum <= kSumMax) || (WITH_G && psum < kSumMin);
-    // Order of the region that also holds the next quarter's S^T product: its K
-    // operand reads first, then a few of these VALU instructions before the first
-    // MFMA waits on its read, then one MFMA per six VALU instructions.
-    __builtin_amdgcn_sched_group_barrier(0x100, T::kKS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    // Order of the region that also holds the next quarter's S^T product (its K
+    // operands were read before the copies were issued): two of these VALU
+    // instructions, then one MFMA per six VALU instructions.
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
 #pragma unroll
     for (int i = 0; i < T::kKS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -569,6 +577,11 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     else wait_vmcnt<0>();
     __syncthreads();
     auto id_of_half = [&](int x) { return ids[x / T::kHalves - t0]; };
+    // K operands of the S product of quarter q+1 (after the last quarter they come
+    // from a stale buffer and are unused), read before the copies are issued.
+    bf16x8 ka[T::kKS];
+    if constexpr (MT == 0) load_k(ka, P ? sk1 : sk0, 1);
+    else load_k(ka, P ? sk0 : sk1, 0);
     if constexpr (MT == 0) {
       store_pending_g();
       if (hh + 1 < NH) issue_v(id_of_half(hh + 1), hh + 1, 1 - P);
@@ -577,8 +590,8 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
     // S of quarter q+1 (after the last quarter the product reads a stale buffer and
     // is unused) while this quarter's softmax runs.
-    if constexpr (MT == 0) compute_s(acc[1], P ? sk1 : sk0, 1);
-    else compute_s(acc[0], P ? sk0 : sk1, 0);
+    if constexpr (MT == 0) mfma_s(acc[1], ka);
+    else mfma_s(acc[0], ka);
     quarter(acc[MT], id_of_half(hh), q, pb);
     if (q + 1 < NQ) mask_s(acc[1 - MT], id_of_half((q + 1) >> 1), q + 1);
     pv(pb, P ? sv1 : sv0, MT);
