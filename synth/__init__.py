@@ -16,5 +16,6 @@ from .workloads import (  # noqa: F401
     make_workload,
     minhash_params,
     random_tiny_case,
+    wide_range_case,
 )
 from .hilbert import gilbert2d, video_hilbert_order  # noqa: F401

@@ -342,6 +342,26 @@ def random_tiny_case(seed: int, heads: int = 2, seq_len: int = 300, head_dim: in
     return Workload(cfg, q, k, v, mask, x0, seq_len, block)
 
 
+def wide_range_case(seed: int, heads: int = 2, seq_len: int = 1000, head_dim: int = 128,
+                    block: int = 128, density: float = 0.6, device="cpu") -> Workload:
+    """random_tiny_case with scores spread over hundreds of log2 units: Q is scaled by
+    8 and each K block by a factor drawn from {0, 1, 8} (powers of two, exact in
+    bf16).  Along a query block's list the block maxima then rise by far more than
+    any lazy reference bound, blocks lie far below the row maximum (a zero block has
+    all scores 0) and the kept probabilities span the whole fp32 range."""
+    w = random_tiny_case(seed, heads=heads, seq_len=seq_len, head_dim=head_dim, block=block,
+                         density=density, device=device)
+    nb = w.mask.shape[1]
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed(BASE_SEED, 2000 + seed))
+    choice = torch.randint(0, 3, (heads, nb), generator=g, device=device)
+    factor = torch.tensor([0.0, 1.0, 8.0], device=device)[choice]
+    k = (w.k.float().view(heads, nb, block, head_dim) * factor[:, :, None, None])
+    w.k = k.view(heads, nb * block, head_dim).to(torch.bfloat16)
+    w.q = (w.q.float() * 8.0).to(torch.bfloat16)
+    return w
+
+
 def drift_states(w: Workload, n_states: int, sigma: float = 0.3, seed: int = BASE_SEED):
     """Q, K, V that drift across denoising steps: state s (0 <= s < n_states) is
     x + (s / (n_states - 1)) * delta_x for x in Q, K, V, with delta_x ~ N(0, sigma^2)

@@ -76,3 +76,33 @@ def test_long_wan_geometry():
     cfg = synth.get_config("wan364k")
     assert cfg.seq_len == 363600 and cfg.num_blocks == 2841 and cfg.padded_len == 363648
     assert cfg.heads == 40 and cfg.head_dim == 128 and cfg.mask == "topk"
+
+
+def test_wide_range_case_spans_the_softmax_bounds():
+    """The wide-range inputs do what their GPU test needs: some query row's block
+    maximum rises by more than 2^32 (32 log2 units) over an earlier block of its list,
+    and some kept block lies more than 96 log2 units below its row's final maximum."""
+    import math
+
+    import numpy as np
+
+    w = synth.wide_range_case(7, heads=2, seq_len=1000, head_dim=128, block=128)
+    q = w.q.float().numpy().astype(np.float64)
+    k = w.k.float().numpy().astype(np.float64)
+    m = w.mask.numpy()
+    H, mb, b, L = m.shape[0], m.shape[1], w.block, w.seq_len
+    l2 = w.scale / math.log(2.0)
+    rise = below = 0.0
+    for h in range(H):
+        s = q[h, :L] @ k[h, :L].T * l2
+        for u in range(mb):
+            rows = s[u * b:min(L, (u + 1) * b)]
+            cols = np.nonzero(m[h, u])[0]
+            if len(cols) < 2:
+                continue
+            bmax = np.stack([rows[:, v * b:min(L, (v + 1) * b)].max(axis=1) for v in cols], 1)
+            run = np.maximum.accumulate(bmax, axis=1)
+            rise = max(rise, float((bmax[:, 1:] - run[:, :-1]).max()))
+            below = max(below, float((run[:, -1:] - bmax).max()))
+    assert rise > 32.0
+    assert below > 96.0
