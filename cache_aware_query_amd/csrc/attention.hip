@@ -25,8 +25,10 @@
 //    P.V product: no data moves between the two products.  Row sums are taken from
 //    the bf16 probabilities with dot products against 1.
 //  * The list is walked in 32-key quarters, software-pipelined: the S^T product of
-//    quarter q+1 is issued while the softmax of quarter q runs, and the P.V product
-//    of quarter q while the row maximum of quarter q+1 is taken.
+//    quarter q+1 is issued while the softmax of quarter q runs, then the P.V product
+//    of quarter q.  The softmax first takes the probabilities against the running
+//    (lazy) reference and takes the row maximum only when their sums show that the
+//    reference must move or that a block sum would lose precision.
 //  * K and V are copied HBM/L2 -> LDS with global_load_lds_dwordx4 (no VGPR
 //    staging) in 64-key halves, double-buffered, in 16-byte chunks whose position
 //    inside a row is XOR-swizzled so that the lanes of an LDS read phase hit
