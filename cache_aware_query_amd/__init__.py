@@ -34,7 +34,7 @@ EXPORTED = (
     "wa_reorder_rows", "wa_reorder_needs_csc", "wa_minhash_order", "wa_sparse_attn_workspace_size",
     "wa_sparse_attn_fwd", "wa_sparse_attn_fwd_diag", "wa_attn_schedule_select",
     "wa_block_importance", "wa_topp_select", "wa_mask_recall", "wa_gather_blocks",
-    "wa_scatter_blocks",
+    "wa_scatter_blocks", "wa_xcd_placement",
 )
 
 
@@ -117,11 +117,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                          ctypes.POINTER(ctypes.c_size_t)]),
         "wa_attn_schedule_select": (ctypes.c_int, [_P, _I32, _P, ctypes.c_size_t, _P]),
         "wa_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _I64, _P,
-                                              _I32, ctypes.c_float, _P, _P, _P, _P,
+                                              _I32, _I32, ctypes.c_float, _P, _P, _P, _P,
                                               ctypes.c_size_t, _P]),
         "wa_sparse_attn_fwd_diag": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P,
-                                                   _I64, _P, _I32, ctypes.c_float, _P, _P, _P,
-                                                   _P, _P, _P, ctypes.c_size_t, _P]),
+                                                   _I64, _P, _I32, _I32, ctypes.c_float, _P, _P,
+                                                   _P, _P, _P, _P, ctypes.c_size_t, _P]),
+        "wa_xcd_placement": (ctypes.c_int, [_I32, _I32, _P, _P]),
         "wa_block_importance": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P,
                                                _P]),
         "wa_topp_select": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, ctypes.c_double,
@@ -218,6 +219,7 @@ class Reorder:
     skipped: torch.Tensor   # uint8 [H]
     angles: torch.Tensor    # float64 [H, MB]
     stats: torch.Tensor     # float64 [H, 5]
+    n_slices: int = 1       # slices the wave buckets were cut into (params.n_slices)
 
 
 def reorder_rows(index: BlockIndex, x0: torch.Tensor, block: int, head_dim: int,
@@ -245,7 +247,7 @@ def reorder_rows(index: BlockIndex, x0: torch.Tensor, block: int, head_dim: int,
                                _ptr(index.csc_idx), cap, _ptr(x0), H, MB, NB, block, head_dim,
                                ctypes.byref(cp), _ptr(perm), _ptr(inv), _ptr(skipped),
                                _ptr(angles), _ptr(stats), _stream(dev)), "wa_reorder_rows")
-    return Reorder(perm, inv, skipped, angles, stats)
+    return Reorder(perm, inv, skipped, angles, stats, int(params.n_slices))
 
 
 def minhash_order(index: BlockIndex, hash_a, hash_b, wave: int, n_slices: int,
@@ -297,9 +299,20 @@ def attn_schedule_select(skipped: torch.Tensor, workspace: torch.Tensor) -> None
            "wa_attn_schedule_select")
 
 
+def xcd_placement(n_wg: int, block: int = 128, device=0) -> torch.Tensor:
+    """XCD each of n_wg workgroups of the attention kernel's size ran on
+    (wa_xcd_placement): the dispatch the XCD-sliced schedule relies on."""
+    lib = load_library()
+    dev = torch.device("cuda", device) if isinstance(device, int) else torch.device(device)
+    out = torch.full((n_wg,), -1, dtype=torch.int32, device=dev)
+    _check(lib.wa_xcd_placement(n_wg, block, _ptr(out), _stream(dev)), "wa_xcd_placement")
+    return out
+
+
 def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len: int,
                     block: int, row_ptr: torch.Tensor, col_idx: torch.Tensor,
                     perm: torch.Tensor | None = None, schedule: int = WA_SCHED_XCD_SLICED,
+                    perm_slices: int | None = None,
                     scale: float | None = None, with_g: bool = False,
                     out: tuple | None = None, workspace: torch.Tensor | None = None,
                     entropy_out: torch.Tensor | None = None,
@@ -310,7 +323,9 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len: 
     buffer of sparse_attn_workspace_size bytes, so that repeated calls allocate
     nothing.  With ``entropy_out`` and/or ``distance_out`` (float [H, L_pad]) the same
     pass also writes each row's attention entropy and mean attention distance in
-    tokens (wa_sparse_attn_fwd_diag).
+    tokens (wa_sparse_attn_fwd_diag).  ``perm_slices`` is the n_slices ``perm`` was
+    built with (``Reorder.n_slices``); the XCD-sliced and AUTO schedules need it and
+    the library rejects a count other than the device's XCD count.
     """
     lib = load_library()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -329,6 +344,10 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len: 
         _need(perm, torch.int32, "perm")
         if perm.numel() != H * mb:
             raise ValueError("perm must have H*MB entries")
+        if perm_slices is None and schedule in (WA_SCHED_XCD_SLICED, WA_SCHED_AUTO):
+            raise ValueError("perm_slices (the n_slices perm was built with) is required with "
+                             "the XCD-sliced and AUTO schedules")
+    slices = 0 if perm is None or perm_slices is None else int(perm_slices)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dev = q.device
     if out is None:
@@ -357,12 +376,13 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len: 
                     raise ValueError(f"{n} must be [H, L_pad]")
         _check(lib.wa_sparse_attn_fwd_diag(
             _ptr(q), _ptr(k), _ptr(v), H, seq_len, d, block, _ptr(row_ptr), _ptr(col_idx), cap,
-            _ptr(perm), schedule, scale, _ptr(o), _ptr(lse), _ptr(g), _ptr(entropy_out),
+            _ptr(perm), slices, schedule, scale, _ptr(o), _ptr(lse), _ptr(g), _ptr(entropy_out),
             _ptr(distance_out), _ptr(workspace), workspace.numel(), _stream(dev)),
             "wa_sparse_attn_fwd_diag")
         return o, lse, g
     _check(lib.wa_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), H, seq_len, d, block,
-                                  _ptr(row_ptr), _ptr(col_idx), cap, _ptr(perm), schedule, scale,
+                                  _ptr(row_ptr), _ptr(col_idx), cap, _ptr(perm), slices,
+                                  schedule, scale,
                                   _ptr(o), _ptr(lse), _ptr(g), _ptr(workspace),
                                   workspace.numel(), _stream(dev)), "wa_sparse_attn_fwd")
     return o, lse, g

@@ -32,11 +32,23 @@ bool supported_shape(int head_dim, int block) {
   return (head_dim == 64 || head_dim == 128) && (block == 64 || block == 128);
 }
 
+// XCD (L2 domain) count of the device that runs `stream` (the current device for
+// the null stream); 1 if the runtime does not report it.
+hipError_t stream_xcds(hipStream_t stream, int* n_xcd) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int x = 0;
+  e = hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev);
+  *n_xcd = (e == hipSuccess && x >= 1) ? x : 1;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
 
-int wa_abi_version(void) { return 2; }
+int wa_abi_version(void) { return 3; }
 
 const char* wa_last_error(void) { return g_err; }
 
@@ -149,7 +161,8 @@ int wa_sparse_attn_workspace_size(int32_t H, int32_t L, int32_t head_dim, int32_
 static int sparse_attn_common(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
                               int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
                               const int32_t* col_idx, int64_t capacity, const int32_t* perm,
-                              int32_t schedule, float scale, wa_bf16* o, float* lse, float* g,
+                              int32_t perm_slices, int32_t schedule, float scale, wa_bf16* o,
+                              float* lse, float* g,
                               float* entropy, float* distance, void* workspace,
                               size_t workspace_bytes, void* stream, const char* name) {
   if (!q || !k || !v || !row_ptr || !col_idx || !o || !lse)
@@ -173,12 +186,32 @@ static int sparse_attn_common(const wa_bf16* q, const wa_bf16* k, const wa_bf16*
   const size_t need = wa::attn_workspace_bytes(H, (int)(MB * block), head_dim);
   if (workspace_bytes < need || (need > 0 && !workspace))
     return fail(WA_ERR_CAPACITY, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (perm_slices < 0 || perm_slices > 64)
+    return fail(WA_ERR_INVALID_ARG, "perm_slices must be in 0..64");
+  int n_xcd = 1;
+  const hipError_t e = stream_xcds(static_cast<hipStream_t>(stream), &n_xcd);
+  if (e != hipSuccess) return hip_status(e, "device of the stream");
+  // The XCD-sliced schedule runs slice x of each head's order on XCD x, so a
+  // permutation whose wave buckets were cut into another number of slices would
+  // put its buckets across L2 domains.
+  if (perm != nullptr && (schedule == WA_SCHED_XCD_SLICED || schedule == WA_SCHED_AUTO) &&
+      perm_slices != n_xcd)
+    return fail(WA_ERR_INVALID_ARG,
+                "perm was built for %d slices but the XCD-sliced schedule runs %d (the device's "
+                "XCD count)", perm_slices, n_xcd);
   return hip_status(wa::launch_sparse_attn(q, k, v, H, L, head_dim, block, row_ptr, col_idx,
-                                           capacity, perm,
-                                           schedule, scale, o, lse, g, entropy, distance,
-                                           workspace,
+                                           capacity, perm, schedule, n_xcd, scale, o, lse, g,
+                                           entropy, distance, workspace,
                                            static_cast<hipStream_t>(stream)),
                     name);
+}
+
+int wa_xcd_placement(int32_t n_wg, int32_t block, int32_t* xcd_out, void* stream) {
+  if (!xcd_out) return fail(WA_ERR_INVALID_ARG, "null pointer argument");
+  if (n_wg < 1) return fail(WA_ERR_INVALID_ARG, "n_wg must be >= 1");
+  if (block != 64 && block != 128) return fail(WA_ERR_UNSUPPORTED, "block %d not in {64, 128}", block);
+  return hip_status(wa::launch_xcd_placement(n_wg, block, xcd_out, static_cast<hipStream_t>(stream)),
+                    "wa_xcd_placement");
 }
 
 int wa_attn_schedule_select(const uint8_t* skipped, int32_t H, void* workspace,
@@ -195,23 +228,23 @@ int wa_attn_schedule_select(const uint8_t* skipped, int32_t H, void* workspace,
 int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
                        int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
                        const int32_t* col_idx, int64_t capacity, const int32_t* perm,
-                       int32_t schedule, float scale, wa_bf16* o, float* lse, float* g,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       int32_t perm_slices, int32_t schedule, float scale, wa_bf16* o, float* lse,
+                       float* g, void* workspace, size_t workspace_bytes, void* stream) {
   return sparse_attn_common(q, k, v, H, L, head_dim, block, row_ptr, col_idx, capacity, perm,
-                            schedule, scale, o, lse, g, nullptr, nullptr, workspace,
+                            perm_slices, schedule, scale, o, lse, g, nullptr, nullptr, workspace,
                             workspace_bytes, stream, "wa_sparse_attn_fwd");
 }
 
 int wa_sparse_attn_fwd_diag(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
                             int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
                             const int32_t* col_idx, int64_t capacity, const int32_t* perm,
-                            int32_t schedule, float scale, wa_bf16* o, float* lse, float* g,
-                            float* entropy, float* distance, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            int32_t perm_slices, int32_t schedule, float scale, wa_bf16* o,
+                            float* lse, float* g, float* entropy, float* distance,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   if (!entropy && !distance)
     return fail(WA_ERR_INVALID_ARG, "entropy and distance are both null");
   return sparse_attn_common(q, k, v, H, L, head_dim, block, row_ptr, col_idx, capacity, perm,
-                            schedule, scale, o, lse, g, entropy, distance, workspace,
+                            perm_slices, schedule, scale, o, lse, g, entropy, distance, workspace,
                             workspace_bytes, stream, "wa_sparse_attn_fwd_diag");
 }
 

@@ -37,7 +37,9 @@
 //    transposed copy of V is ever written.  The query block's K/V list is staged
 //    in LDS so that block ids never wait on scalar memory inside the loop.
 //  * Workgroup -> query block: natural head-major order, or XCD-sliced: workgroup
-//    w runs on XCD w % 8 (round-robin dispatch), and XCD x takes the x-th
+//    w runs on XCD w % n_xcd (round-robin dispatch; n_xcd is the device's XCD
+//    count, 8 on MI355X, and wa_xcd_placement records the placement), and XCD x
+//    takes the x-th
 //    contiguous slice of each head's execution order, so each XCD's L2 sees one
 //    contiguous run of the (reordered) schedule and all XCDs stay on one head.  The
 //    head-interleaved order (position w / H of head w % H) runs all heads at once,
@@ -199,7 +201,8 @@ __global__ __launch_bounds__(BLOCK * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, int H, int L, int MB,
                    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-                   int cap, const int32_t* __restrict__ perm, int schedule, float scale_log2,
+                   int cap, const int32_t* __restrict__ perm, int schedule, int n_xcd,
+                   float scale_log2,
                    uint16_t* __restrict__ O, float* __restrict__ lse, float* __restrict__ G,
                    float* __restrict__ ENT, float* __restrict__ DIST,
                    const int* __restrict__ sched_ws) {
@@ -219,9 +222,9 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     schedule = sched_ws[0] == WA_SCHED_HEADS_INTERLEAVED ? WA_SCHED_HEADS_INTERLEAVED
                                                          : WA_SCHED_XCD_SLICED;
   if (schedule == WA_SCHED_XCD_SLICED) {
-    const int s = (MB + kXcds - 1) / kXcds;
-    const int x = blockIdx.x % kXcds;
-    const int j = blockIdx.x / kXcds;
+    const int s = (MB + n_xcd - 1) / n_xcd;
+    const int x = blockIdx.x % n_xcd;
+    const int j = blockIdx.x / n_xcd;
     h = j / s;
     pos = x * s + j % s;
     if (pos >= MB) return;
@@ -263,7 +266,9 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // for every K/V copy in flight as well.
   const int ntiles = e1 - e0;
   if constexpr (STAGED) {
-    for (int i = threadIdx.x; i < ntiles; i += BLOCK * 2) blist[i] = col_idx[e0 + i];
+    // A well-formed row holds at most NB <= kListCap entries; entries past kListCap
+    // (a malformed, longer row) are read from global memory instead.
+    for (int i = threadIdx.x; i < min(ntiles, kListCap); i += BLOCK * 2) blist[i] = col_idx[e0 + i];
   }
   // Q rows (the B operand of S^T): lane holds q[qrow][16*ks + 8*g .. +7].  Their
   // loads complete here, before any copy is in flight, for the same reason.
@@ -280,8 +285,10 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // List entry of tile t (wave-uniform; t is clamped into the list).
   auto list_entry = [&](int t) {
     t = min(t, ntiles - 1);
-    if constexpr (STAGED) return __builtin_amdgcn_readfirstlane(blist[t]);
-    else return __builtin_amdgcn_readfirstlane(col_idx[e0 + t]);
+    if constexpr (STAGED) {
+      if (t < kListCap) return __builtin_amdgcn_readfirstlane(blist[t]);
+    }
+    return __builtin_amdgcn_readfirstlane(col_idx[e0 + t]);
   };
 
   // Copies of a K or V half (64 keys x D, 1 KiB chunks of whole rows): wave w copies
@@ -440,12 +447,13 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         blk_m = nm;
       }
       if (qi == kQ - 1) {
-        const int e = e0 + q / kQ;
-        if ((unsigned)v < (unsigned)MB) {
-          g_pending = blk_m == -INFINITY ? -INFINITY
-                                         : (blk_m + __log2f(pair_sum(blk_s))) * kLn2;
-          e_pending = e;
-        }
+        // An entry outside [0, MB) evaluates no key: its G is -inf, so that its block
+        // weight is 0.
+        const float bs = pair_sum(blk_s);
+        g_pending = ((unsigned)v < (unsigned)MB && blk_m != -INFINITY)
+                        ? (blk_m + __log2f(bs)) * kLn2
+                        : -INFINITY;
+        e_pending = e0 + q / kQ;
       }
     }
     if constexpr (DIAG) {
@@ -635,8 +643,10 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   store_pending_g();
 
   // Normalise and store.  Register r of d tile dt holds d = 32*dt + 8*(r/4) + 4*g + r%4.
+  // A row that evaluated no key (every list entry outside [0, MB)) has l_tot = 0:
+  // it gets O = 0 and LSE = -inf, like an empty list.
   const float l_tot = pair_sum(l_run);
-  const float inv_l = 1.0f / l_tot;
+  const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   uint16_t* op = O + head_off + (size_t)qrow * D;
 #pragma unroll
   for (int dt = 0; dt < T::kDT; ++dt)
@@ -653,14 +663,14 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                  ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
       *reinterpret_cast<uint2*>(op + dt * 32 + 8 * rb + 4 * g) = packed;
     }
-  const float lse_row = (m_run + __log2f(l_tot)) * kLn2;
+  const float lse_row = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   if (g == 0) lse[(size_t)h * Lp + qrow] = lse_row;
   if constexpr (DIAG) {
     // Entropy of the row's attention: LSE - E[z] with z = scale * q.k (natural log);
     // mean attention distance: E[|i - j|] in tokens.
     const float ez = pair_sum(es_run) * inv_l * (scale_log2 * kLn2);
     const float ed = pair_sum(ds_run) * inv_l;
-    if (ENT != nullptr && g == 0) ENT[(size_t)h * Lp + qrow] = lse_row - ez;
+    if (ENT != nullptr && g == 0) ENT[(size_t)h * Lp + qrow] = l_tot > 0.0f ? lse_row - ez : 0.0f;
     if (DIST != nullptr && g == 0) DIST[(size_t)h * Lp + qrow] = ed;
   }
 }
@@ -668,16 +678,17 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 template <int BLOCK, int D>
 hipError_t launch_typed(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H, int L,
                         const int32_t* row_ptr, const int32_t* col_idx, int cap,
-                        const int32_t* perm, int schedule, float scale, uint16_t* o, float* lse,
-                        float* g, float* ent, float* dist, const int* sched_ws, hipStream_t s) {
+                        const int32_t* perm, int schedule, int n_xcd, float scale, uint16_t* o,
+                        float* lse, float* g, float* ent, float* dist, const int* sched_ws,
+                        hipStream_t s) {
   const int MB = (L + BLOCK - 1) / BLOCK;
   int grid = H * MB;
   if (schedule == WA_SCHED_XCD_SLICED || schedule == WA_SCHED_AUTO)
-    grid = H * kXcds * ((MB + kXcds - 1) / kXcds);  // >= H * MB, the other schedules' grid
+    grid = H * n_xcd * ((MB + n_xcd - 1) / n_xcd);  // >= H * MB, the other schedules' grid
   const float sl2 = scale * kLog2e;
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(BLOCK * 2), 0, s, q, k, v, H, L, MB, row_ptr,
-                       col_idx, cap, perm, schedule, sl2, o, lse, g, ent, dist, sched_ws);
+                       col_idx, cap, perm, schedule, n_xcd, sl2, o, lse, g, ent, dist, sched_ws);
   };
   const bool staged = MB <= kListCap;  // NB = MB: every list fits in LDS
   auto pick = [&](auto diag) {
@@ -731,21 +742,38 @@ int attn_resident_wgs_per_cu(int head_dim, int block) {
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H,
                               int L, int head_dim, int block, const int32_t* row_ptr,
                               const int32_t* col_idx, int64_t cap64, const int32_t* perm,
-                              int schedule, float scale, uint16_t* o, float* lse, float* g,
-                              float* ent, float* dist, void* workspace, hipStream_t s) {
+                              int schedule, int n_xcd, float scale, uint16_t* o, float* lse,
+                              float* g, float* ent, float* dist, void* workspace, hipStream_t s) {
   const int* sched_ws = static_cast<const int*>(workspace);
   const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
   if (block == 128 && head_dim == 128)
-    return launch_typed<128, 128>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o,
-                                  lse, g, ent, dist, sched_ws, s);
+    return launch_typed<128, 128>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, n_xcd,
+                                  scale, o, lse, g, ent, dist, sched_ws, s);
   if (block == 128 && head_dim == 64)
-    return launch_typed<128, 64>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o,
-                                 lse, g, ent, dist, sched_ws, s);
+    return launch_typed<128, 64>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, n_xcd,
+                                 scale, o, lse, g, ent, dist, sched_ws, s);
   if (block == 64 && head_dim == 128)
-    return launch_typed<64, 128>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o,
-                                 lse, g, ent, dist, sched_ws, s);
-  return launch_typed<64, 64>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, scale, o, lse,
-                              g, ent, dist, sched_ws, s);
+    return launch_typed<64, 128>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, n_xcd,
+                                 scale, o, lse, g, ent, dist, sched_ws, s);
+  return launch_typed<64, 64>(q, k, v, H, L, row_ptr, col_idx, cap, perm, schedule, n_xcd, scale,
+                              o, lse, g, ent, dist, sched_ws, s);
+}
+
+namespace {
+// Each workgroup (of the attention kernel's size for this block) records the XCD it
+// runs on: bits [3:0] of the XCC_ID hardware register.
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void k_xcd_placement(int32_t* __restrict__ out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15;
+}
+}  // namespace
+
+hipError_t launch_xcd_placement(int n_wg, int block, int32_t* out, hipStream_t s) {
+  if (block == 128)
+    hipLaunchKernelGGL(k_xcd_placement<256>, dim3(n_wg), dim3(256), 0, s, out);
+  else
+    hipLaunchKernelGGL(k_xcd_placement<128>, dim3(n_wg), dim3(128), 0, s, out);
+  return hipGetLastError();
 }
 
 }  // namespace wa

@@ -34,10 +34,9 @@ hipError_t launch_sched_select(const uint8_t* skipped, int H, void* workspace, h
 hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int H,
                               int L, int head_dim, int block, const int32_t* row_ptr,
                               const int32_t* col_idx, int64_t cap, const int32_t* perm,
-                              int schedule,
-                              float scale, uint16_t* o, float* lse, float* g, float* ent,
-                              float* dist,
-                              void* workspace, hipStream_t s);
+                              int schedule, int n_xcd, float scale, uint16_t* o, float* lse,
+                              float* g, float* ent, float* dist, void* workspace, hipStream_t s);
+hipError_t launch_xcd_placement(int n_wg, int block, int32_t* out, hipStream_t s);
 int attn_resident_wgs_per_cu(int head_dim, int block);
 
 hipError_t launch_block_importance(const float* g, const float* lse, const int32_t* row_ptr,
@@ -52,7 +51,5 @@ hipError_t launch_topp(const float* w, const int32_t* row_ptr, const int32_t* co
 hipError_t launch_permute_blocks(const void* src, void* dst, const int32_t* perm, int H, int MB,
                                  int64_t block_bytes, bool scatter, hipStream_t s);
 
-// Number of XCDs the attention schedule slices over.
-constexpr int kXcds = 8;
 
 }  // namespace wa

@@ -114,8 +114,9 @@ class HotPath:
         lib, s = self.lib, _stream(self.device)
         perm = self.perm if self.reorder is not None else None
         g = self.g if self.gsrs_p is not None else None
+        slices = self.reorder.n_slices if perm is not None else 0
         args = (_ptr(q), _ptr(k), _ptr(v), self.H, self.L, self.d, self.b, _ptr(self.row_ptr),
-                _ptr(self.col_idx), self.cap, _ptr(perm), self.schedule, self.d ** -0.5,
+                _ptr(self.col_idx), self.cap, _ptr(perm), slices, self.schedule, self.d ** -0.5,
                 _ptr(self.o), _ptr(self.lse), _ptr(g))
         if self.entropy is not None:
             _check(lib.wa_sparse_attn_fwd_diag(*args, _ptr(self.entropy), _ptr(self.distance),

@@ -107,7 +107,9 @@ int wa_build_block_index(const uint8_t* mask, int32_t H, int32_t MB, int32_t NB,
 typedef struct wa_reorder_params {
   int32_t wave;        /* W, rows per wave bucket (>= 1)                                */
   int32_t n_slices;    /* contiguous slices of the order, one per L2 domain (1..64);
-                          1 reproduces [WA Algorithm 2] exactly                          */
+                          1 reproduces [WA Algorithm 2] exactly; the XCD-sliced
+                          attention schedule needs the device's XCD count here and
+                          checks it (wa_sparse_attn_fwd perm_slices)                     */
   int32_t iters;       /* T of [WA Algorithm 1] (0..1000)                                */
   int32_t stage1;      /* 1: spectral polar order, 0: keep the row order                 */
   int32_t stage2;      /* 1: NNZ-descending order inside buckets, 0: off                  */
@@ -200,27 +202,49 @@ int wa_sparse_attn_workspace_size(int32_t H, int32_t L, int32_t head_dim, int32_
  * the probabilities are rounded to bf16 before the P*V product.
  *   q, k, v   bf16 [H][L_pad][head_dim]; head_dim 64 or 128; block 64 or 128
  *   capacity  entries col_idx holds (and rows g holds); entries at or beyond it are
- *             skipped, as are block ids outside [0, MB)
+ *             skipped, as are block ids outside [0, MB): such an entry evaluates no
+ *             key and its G row is -inf; a query block whose entries are all skipped
+ *             gets O = 0 and LSE = -inf, like an empty one
  *   perm      int32 [H][MB] or NULL  execution order [WA §V]: position p of head h runs
  *             query block perm[h][p]; O, LSE and G stay in the original order (the
  *             permutation is applied by indexing, the inverse reorder is implicit)
+ *   perm_slices  the n_slices the permutation's wave buckets were cut into (the
+ *             reorder's parameter), 0 if unknown.  With perm != NULL and the
+ *             XCD-sliced (or AUTO) schedule it must equal the device's XCD count
+ *             (wa_schedule_info): slice x of each head's order runs on XCD x.
+ *             Ignored when perm is NULL.
  *   schedule  WA_SCHED_NATURAL, WA_SCHED_XCD_SLICED, WA_SCHED_HEADS_INTERLEAVED or
- *             WA_SCHED_AUTO (reads the choice of wa_attn_schedule_select from workspace)
+ *             WA_SCHED_AUTO (reads the choice of wa_attn_schedule_select from workspace).
+ *             XCD-sliced: workgroup w runs on XCD w mod n_xcd (round-robin dispatch,
+ *             n_xcd = the device's XCD count, checked by wa_xcd_placement) and takes
+ *             position floor(w / n_xcd) of slice (w mod n_xcd) of its head's order
  *   o         bf16 [H][L_pad][head_dim] out
  *   lse       float [H][L_pad] out, natural log
  *   g         float [row_ptr[H*MB]][block] out or NULL  [GSRS §5.3 Phase 1] for CSR
  *             entry e = (u, v) and row r of u, the block log-sum-exp
  *             G = m + ln sum_{j in v, j < L} exp(z_rj - m), m the block maximum
  *   workspace device buffer of at least wa_sparse_attn_workspace_size bytes
- * Errors: WA_ERR_INVALID_ARG, WA_ERR_UNSUPPORTED (head_dim/block), WA_ERR_CAPACITY
+ * Errors: WA_ERR_INVALID_ARG (including perm_slices != the XCD count under the
+ * XCD-sliced schedule), WA_ERR_UNSUPPORTED (head_dim/block), WA_ERR_CAPACITY
  * (workspace too small), WA_ERR_HIP.
  */
 int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
                        int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
                        const int32_t* col_idx, int64_t capacity, const int32_t* perm,
-                       int32_t schedule,
-                       float scale, wa_bf16* o, float* lse, float* g, void* workspace,
-                       size_t workspace_bytes, void* stream);
+                       int32_t perm_slices, int32_t schedule, float scale, wa_bf16* o,
+                       float* lse, float* g, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * wa_xcd_placement - [WA §II-C: a wave is the set of row tasks resident at once on
+ * processors that share one L2] checks the dispatch the XCD-sliced schedule relies
+ * on: launches n_wg workgroups of the attention kernel's size for `block` and writes,
+ * for each, the XCD (L2 domain) it ran on, read from the XCC_ID hardware register.
+ *   xcd_out  int32 [n_wg] out
+ * Errors: WA_ERR_INVALID_ARG (null pointer, n_wg < 1), WA_ERR_UNSUPPORTED (block not
+ * 64/128), WA_ERR_HIP.
+ */
+int wa_xcd_placement(int32_t n_wg, int32_t block, int32_t* xcd_out, void* stream);
 
 /*
  * wa_attn_schedule_select - [WA §VI-F, Fig. 13: when the adaptive skip leaves every
@@ -255,9 +279,9 @@ int wa_attn_schedule_select(const uint8_t* skipped, int32_t H, void* workspace,
 int wa_sparse_attn_fwd_diag(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
                             int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
                             const int32_t* col_idx, int64_t capacity, const int32_t* perm,
-                            int32_t schedule, float scale, wa_bf16* o, float* lse, float* g,
-                            float* entropy, float* distance, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            int32_t perm_slices, int32_t schedule, float scale, wa_bf16* o,
+                            float* lse, float* g, float* entropy, float* distance,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * wa_block_importance - [GSRS §5.3 Phase 2, Appendix A.2] block weights.

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.wa_abi_version() == 2
+    assert lib.wa_abi_version() == 3
 
 
 def test_host_validation_rejects_bad_arguments(lib):
@@ -86,21 +86,31 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert lib.wa_minhash_order(None, fake, 16, 1, 4, 4, ga, gb, 2, 4, 1, 1, fake, fake,
                                 None) == -1
     # negative capacity, bad schedule and non-positive scale are refused on the host
-    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, -1, None, 1,
+    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, -1, None, 0, 1,
                                   0.1, fake, fake, None, None, 0, None) == -1
-    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 7,
+    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 0, 7,
                                   0.1, fake, fake, None, None, 0, None) == -1
-    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 1,
+    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 0, 1,
                                   -0.1, fake, fake, None, None, 0, None) == -1
     # the workspace is required (it carries the WA_SCHED_AUTO choice)
-    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 3,
+    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 0, 3,
                                   0.1, fake, fake, None, None, 0, None) == -3
     assert lib.wa_attn_schedule_select(fake, 4, fake, 16, None) == -3
     assert lib.wa_attn_schedule_select(None, 4, fake, 256, None) == -1
     assert lib.wa_attn_schedule_select(fake, 0, fake, 256, None) == -1
+    # the slice count of a permutation is checked against the range before the device
+    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, fake, -1, 1,
+                                  0.1, fake, fake, None, fake, 256, None) == -1
+    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, fake, 65, 1,
+                                  0.1, fake, fake, None, fake, 256, None) == -1
+    assert b"perm_slices" in lib.wa_last_error()
+    # the XCD placement probe checks its arguments on the host
+    assert lib.wa_xcd_placement(0, 128, fake, None) == -1
+    assert lib.wa_xcd_placement(4, 128, None, None) == -1
+    assert lib.wa_xcd_placement(4, 96, fake, None) == -2
     # unaligned pointer
     odd = ctypes.c_void_p(18)
-    assert lib.wa_sparse_attn_fwd(odd, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 1,
+    assert lib.wa_sparse_attn_fwd(odd, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 0, 1,
                                   0.1, fake, fake, None, None, 0, None) == -1
     # overlapping gather
     assert lib.wa_gather_blocks(fake, fake, fake, 1, 2, 64, None) == -1

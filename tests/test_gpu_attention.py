@@ -20,8 +20,11 @@ def _run(w, perm=None, schedule=caq.WA_SCHED_XCD_SLICED, with_g=False):
     q, k, v, mask = (t.to(dev) for t in (w.q, w.k, w.v, w.mask))
     idx = caq.build_block_index(mask)
     p = None if perm is None else perm.to(dev)
+    # a free permutation: the slice count of the schedule it runs under is the device's
+    n_xcd = caq.schedule_info(0, w.head_dim)[0]
     o, lse, g = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx,
-                                    perm=p, schedule=schedule, with_g=with_g)
+                                    perm=p, schedule=schedule, with_g=with_g,
+                                    perm_slices=None if p is None else n_xcd)
     torch.cuda.synchronize()
     return o, lse, g, idx
 
@@ -199,17 +202,106 @@ def test_auto_schedule_follows_the_skip_flags(skip_mode, expect):
     banner(f"attention AUTO schedule skip_mode={skip_mode}")
     q, k, v, mask, x0 = (t.to(dev) for t in (w.q, w.k, w.v, w.mask, w.x0))
     idx = caq.build_block_index(mask)
+    n_xcd = caq.schedule_info(0, w.head_dim)[0]
     ro = caq.reorder_rows(idx, x0, w.block, w.head_dim,
-                          caq.ReorderParams(wave=8, n_slices=8, skip_mode=skip_mode))
+                          caq.ReorderParams(wave=8, n_slices=n_xcd, skip_mode=skip_mode))
     ws = torch.empty(caq.sparse_attn_workspace_size(3, w.seq_len, 128, 128), dtype=torch.uint8,
                      device=dev)
     caq.attn_schedule_select(ro.skipped, ws)
     o, lse, g = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx,
                                     perm=ro.perm, schedule=caq.WA_SCHED_AUTO, with_g=True,
-                                    workspace=ws)
+                                    workspace=ws, perm_slices=ro.n_slices)
     o2, lse2, g2 = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, idx.row_ptr, idx.col_idx,
-                                       perm=ro.perm, schedule=expect, with_g=True)
+                                       perm=ro.perm, schedule=expect, with_g=True,
+                                       perm_slices=ro.n_slices)
     torch.cuda.synchronize()
     assert int(ws[:4].view(torch.int32).item()) == expect
     assert torch.equal(o, o2) and torch.equal(lse, lse2) and torch.equal(g, g2)
     _compare(w, o, lse, f"AUTO skip_mode={skip_mode}")
+
+
+def _csr_from_lists(lists):
+    """row_ptr, col_idx (int32) of per-row id lists, in row order."""
+    row_ptr = np.zeros(len(lists) + 1, dtype=np.int32)
+    row_ptr[1:] = np.cumsum([len(x) for x in lists])
+    col_idx = np.array([v for x in lists for v in x] or [0], dtype=np.int32)
+    return row_ptr, col_idx
+
+
+@pytest.mark.parametrize("with_g", [False, True])
+def test_list_entries_outside_the_key_blocks(with_g):
+    """CSR entries outside [0, MB) evaluate no key: a row holding only such ids gets
+    O = 0 and LSE = -inf (no NaN), a row mixing them with real ids equals the row
+    of the real ids alone, their G is -inf and their block weight 0."""
+    dev = gpu()
+    w = synth.random_tiny_case(31, heads=1, seq_len=1000, head_dim=128, block=128, density=0.5,
+                               empty_rows=())
+    mb = w.mask.shape[1]
+    banner(f"attention with list entries outside [0, {mb}) with_g={with_g}")
+    m = w.mask.cpu().numpy()[0].astype(bool)
+    bad = [-1, mb, mb + 5, -(2 ** 31)]
+    lists = []
+    for u in range(mb):
+        real = np.flatnonzero(m[u]).tolist()
+        if u == 2:
+            lists.append(bad[:3])                   # only ids that name no block
+        elif u == 5:
+            lists.append([bad[0]] + real + [bad[1], bad[3]])  # mixed
+        else:
+            lists.append(real)
+    rp, ci = _csr_from_lists(lists)
+    q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+    row_ptr, col_idx = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+    o, lse, g = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, row_ptr, col_idx,
+                                    schedule=caq.WA_SCHED_NATURAL, with_g=with_g)
+    torch.cuda.synchronize()
+    m_ref = m.copy()
+    m_ref[2] = False
+    L, b = w.seq_len, w.block
+    o_ref, lse_ref = oracle.masked_attention(np64(w.q), np64(w.k), np64(w.v), m_ref[None], L, b,
+                                             w.scale)
+    assert_attention_close(np64(o)[:, :L], lse.cpu().numpy().astype(np.float64)[:, :L],
+                           o_ref[:, :L], lse_ref[:, :L], "entries outside [0, MB)")
+    assert torch.all(o[0, 2 * b:3 * b] == 0)
+    if with_g:
+        gn = g.cpu().numpy()
+        ids = ci[: rp[-1]]
+        outside = (ids < 0) | (ids >= mb)
+        assert np.all(np.isneginf(gn[outside]))
+        wts = caq.block_importance(g, lse, row_ptr, L, b).cpu().numpy()
+        assert np.all(wts[outside] == 0)
+        # each row with real keys still sums to 1 over its real entries
+        for u in range(mb):
+            if u != 2:
+                assert abs(wts[rp[u]:rp[u + 1]].sum() - 1.0) < 1e-3
+
+
+def test_row_longer_than_the_staged_list():
+    """A (malformed) row listing one block 2,100 times: past the 2,048 entries staged
+    in LDS the kernel reads the list from global memory.  Every key of the block then
+    counts 2,100 times: O equals the single-block row and LSE rises by ln 2,100."""
+    dev = gpu()
+    w = synth.random_tiny_case(37, heads=1, seq_len=16 * 128, head_dim=128, block=128,
+                               density=0.3, empty_rows=())
+    mb = w.mask.shape[1]
+    banner("attention row of 2,100 entries (staged list cap 2,048)")
+    reps, u_long, v_long = 2100, 6, 3
+    m = w.mask.cpu().numpy()[0].astype(bool)
+    lists = [np.flatnonzero(m[u]).tolist() for u in range(mb)]
+    lists[u_long] = [v_long] * reps
+    rp, ci = _csr_from_lists(lists)
+    q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+    row_ptr, col_idx = torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev)
+    o, lse, _ = caq.sparse_attn_fwd(q, k, v, w.seq_len, w.block, row_ptr, col_idx,
+                                    schedule=caq.WA_SCHED_NATURAL)
+    torch.cuda.synchronize()
+    m_ref = m.copy()
+    m_ref[u_long] = False
+    m_ref[u_long, v_long] = True
+    L, b = w.seq_len, w.block
+    o_ref, lse_ref = oracle.masked_attention(np64(w.q), np64(w.k), np64(w.v), m_ref[None], L, b,
+                                             w.scale)
+    lse_ref = lse_ref.copy()
+    lse_ref[0, u_long * b:(u_long + 1) * b] += np.log(reps)
+    assert_attention_close(np64(o)[:, :L], lse.cpu().numpy().astype(np.float64)[:, :L],
+                           o_ref[:, :L], lse_ref[:, :L], "row of 2,100 entries")

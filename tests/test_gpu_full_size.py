@@ -107,7 +107,8 @@ def test_more_blocks_than_the_staged_list_cap():
     idx = caq.build_block_index(mask)
     params = caq.ReorderParams(wave=64, n_slices=8, iters=5, skip_mode=caq.WA_SKIP_NEVER)
     ro = caq.reorder_rows(idx, x0, b, d, params)
-    o, lse, _ = caq.sparse_attn_fwd(q, k, v, L, b, idx.row_ptr, idx.col_idx, perm=ro.perm)
+    o, lse, _ = caq.sparse_attn_fwd(q, k, v, L, b, idx.row_ptr, idx.col_idx, perm=ro.perm,
+                                    perm_slices=ro.n_slices)
     o_id, lse_id, _ = caq.sparse_attn_fwd(q, k, v, L, b, idx.row_ptr, idx.col_idx)
     torch.cuda.synchronize()
     perm = ro.perm.cpu().numpy()[0]
@@ -139,7 +140,8 @@ def test_the_largest_supported_mask():
     idx = caq.build_block_index(mask)
     params = caq.ReorderParams(wave=64, n_slices=8, iters=5, skip_mode=caq.WA_SKIP_NEVER)
     ro = caq.reorder_rows(idx, x0, b, d, params)
-    o, lse, _ = caq.sparse_attn_fwd(q, k, v, L, b, idx.row_ptr, idx.col_idx, perm=ro.perm)
+    o, lse, _ = caq.sparse_attn_fwd(q, k, v, L, b, idx.row_ptr, idx.col_idx, perm=ro.perm,
+                                    perm_slices=ro.n_slices)
     a_mh, b_mh = synth.minhash_params(2)
     perm_mh, _ = caq.minhash_order(idx, a_mh, b_mh, 64, 8)
     torch.cuda.synchronize()

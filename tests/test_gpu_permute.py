@@ -42,7 +42,7 @@ def test_explicit_path_equals_fused_path():
     idx = caq.build_block_index(mask)
     ro = caq.reorder_rows(idx, x0, b, w.head_dim, caq.ReorderParams(skip_mode=caq.WA_SKIP_NEVER))
     o_f, lse_f, _ = caq.sparse_attn_fwd(q, k, v, w.seq_len, b, idx.row_ptr, idx.col_idx,
-                                        perm=ro.perm)
+                                        perm=ro.perm, perm_slices=ro.n_slices)
     qg = caq.gather_blocks(q, ro.perm, b)
     mg = caq.gather_blocks(mask, ro.perm, 1)
     idx_g = caq.build_block_index(mg)
