@@ -11,9 +11,9 @@ open:
   second column vanishes after orthogonalisation (norm <= 1e-12 times the norm
   of the first column, i.e. the centered mask has rank one) the second basis
   vector is set to zero; if the first column is exactly zero both are zero.
-* The optional singular-value ordering of Algorithm 1 is applied: B = X^T Z is
-  symmetrised, its eigenvectors are taken in descending eigenvalue order
-  (a library eigensolver here), and X <- X R.
+* The optional singular-value ordering of Algorithm 1 is applied: the projected
+  2 x 2 matrix X^T M~ M~^T X is symmetrised and X is rotated onto its
+  eigenvectors in descending eigenvalue order (a library eigensolver here).
 * Sign of each basis vector: flipped so that sum_i X[i, k]^3 > 0; when
   |sum| < 1e-6 the first entry with magnitude > 1e-6 is made positive instead.
   (The page calls the angular order invariant to sign flips; a flip in fact
@@ -101,35 +101,32 @@ def canonical_signs(x: np.ndarray) -> np.ndarray:
 
 
 def mfcsi(mask_h: np.ndarray, x0: np.ndarray, iters: int, ritz: bool = True):
-    """WaveAlign Algorithm 1 (matrix-free centered subspace iteration).
+    """Rank-2 spectral embedding of the mask rows (WaveAlign §IV-C-2, Algorithm 1).
 
-    Returns the MB x 2 basis (u1, u2) after ``iters`` iterations, the optional
-    Ritz rotation and the sign convention, or None if all mask rows are equal
-    (zero centered mask).  The products with M and M^T are written with the
-    explicit 0/1 matrix; centering enters only through the rank-1 corrections
-    of lines 6-7 of the algorithm, exactly as there.
+    The embedding of row i is row i of the two leading left singular vectors of the
+    centered mask M~ (eq. (2)), which are the two leading eigenvectors of the row
+    Gram matrix M~ M~^T.  They are approximated by subspace iteration from the start
+    block x0: X <- qr(M~ (M~^T X)), ``iters`` times, with M~ formed explicitly in
+    fp64.  With ``ritz`` the two basis vectors are then rotated onto the eigenvectors
+    of the projected 2 x 2 matrix X^T M~ M~^T X, in descending eigenvalue order.  The
+    sign convention of ``canonical_signs`` fixes the result.  Returns None when every
+    row of the mask is the same (M~ = 0: there is no subspace to embed into).
     """
-    m = np.asarray(mask_h, dtype=np.float64)
-    mb = m.shape[0]
-    c = m.sum(axis=0)  # c = M^T 1
-    if np.all((c == 0) | (c == mb)):
+    mt = centered_mask(mask_h)                 # M~, MB x NB
+    if not np.any(mt):
         return None
-    ones = np.ones(mb)
+
+    def gram_times(xx):                        # M~ M~^T X, never forming the MB x MB Gram
+        return mt @ (mt.T @ xx)
+
     x = _qr2(np.asarray(x0, dtype=np.float64))
-
-    def apply(xx):
-        y = m.T @ xx - np.outer(c, ones @ xx) / mb      # Y = M^T X - c (1^T X) / m
-        z = m @ y - np.outer(ones, c @ y) / mb          # Z = M Y - 1 (c^T Y) / m
-        return z
-
     for _ in range(iters):
-        x = _qr2(apply(x))
+        x = _qr2(gram_times(x))
     if ritz:
-        z = apply(x)
-        b = x.T @ z
-        b = 0.5 * (b + b.T)
-        _, vecs = np.linalg.eigh(b)     # ascending eigenvalues
-        x = x @ vecs[:, ::-1]           # descending
+        proj = x.T @ gram_times(x)
+        proj = 0.5 * (proj + proj.T)
+        _, vecs = np.linalg.eigh(proj)         # ascending eigenvalues
+        x = x @ vecs[:, ::-1]
     return canonical_signs(x)
 
 

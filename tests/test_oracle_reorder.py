@@ -46,10 +46,11 @@ def test_centering_preserves_distances_and_zeroes_column_sums():
 
 
 def _principal_sin(a, b):
+    # sine of the largest principal angle as the norm of b's part outside span(a):
+    # ||(I - Qa Qa^T) Qb||_2 resolves angles down to rounding, unlike sqrt(1 - cos^2)
     qa, _ = np.linalg.qr(a)
     qb, _ = np.linalg.qr(b)
-    s = np.linalg.svd(qa.T @ qb, compute_uv=False)
-    return np.sqrt(max(0.0, 1.0 - s.min() ** 2))
+    return float(np.linalg.norm(qb - qa @ (qa.T @ qb), 2))
 
 
 def test_mfcsi_matches_library_svd():
@@ -149,16 +150,21 @@ def test_rank_one_centered_mask_splits_by_sign():
     assert int(np.sum(seq[1:] != seq[:-1])) == 1
 
 
-def test_matrix_free_iteration_equals_explicit_centered_iteration():
-    # Algorithm 1 never forms M~; iterating with the explicit eq. (2) matrix and a
-    # library QR must give the same basis (up to the sign convention).
+def test_explicit_iteration_equals_the_matrix_free_form():
+    # The oracle forms M~ = M - 1 c^T / MB explicitly.  The same products can be taken
+    # with the 0/1 mask and rank-1 corrections (c = M^T 1):
+    #   M~^T X = M^T X - c (1^T X) / MB,   M~ Y = M Y - 1 (c^T Y) / MB,
+    # which never forms M~; with a library QR both give the same basis.
     rng = np.random.default_rng(10)
-    m = _structured_mask(rng, 60, 50)
+    m = _structured_mask(rng, 60, 50).astype(np.float64)
     x0 = rng.uniform(-1, 1, (60, 2))
-    mt = oracle.centered_mask(m)
+    c = m.sum(axis=0)
+    ones = np.ones(60)
     x, _ = np.linalg.qr(x0)
     for _ in range(3):
-        x, r = np.linalg.qr(mt @ (mt.T @ x))
+        y = m.T @ x - np.outer(c, ones @ x) / 60
+        z = m @ y - np.outer(ones, c @ y) / 60
+        x, r = np.linalg.qr(z)
         x = x * np.sign(np.diag(r))[None, :]
     want = oracle.canonical_signs(x)
     got = oracle.mfcsi(m, x0, iters=3, ritz=False)
