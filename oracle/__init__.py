@@ -16,8 +16,9 @@ Every function restates a computation from the two source pages:
 * "Sparse Attention for Video Generation Acceleration via Growing Sparsity and
   Reduced Search" (cited as *GSRS*): block-sparse attention with a row-wise
   log-sum-exp (§3 preliminaries), the two-phase block importance (§5.3,
-  Appendix A.2), fully masked rows (note to Algorithm 2) and Top-p selection
-  (Algorithm 3).
+  Appendix A.2), fully masked rows (note to Algorithm 2), Top-p selection
+  (Algorithm 3) and the multi-step schedule of growing sparsity and reduced
+  search (§4-5, Algorithm 4).
 * The MinHash row order that WaveAlign's Table II compares against
   (``comparators``), from the published min-wise hashing it names.
 
@@ -51,6 +52,7 @@ from .gsrs import (  # noqa: F401
     mask_recall,
     block_lse,
     cached_lse_scores,
+    gsrs_schedule,
     topp_select,
 )
 from .permute import gather_blocks, scatter_blocks  # noqa: F401

@@ -188,3 +188,67 @@ def mask_recall(q: np.ndarray, k: np.ndarray, mask: np.ndarray, seq_len: int, bl
             keys = np.concatenate([_valid_keys(v, seq_len, block) for v in kept])
             out[h, u] = a[r0:r1][:, keys].sum() / (r1 - r0)
     return out
+
+
+def gsrs_schedule(steps: int, search_steps, thresholds, qk_at, seq_len: int, block: int,
+                  scale: float, w_select=None):
+    """The GSRS inference schedule over denoising steps (GSRS §4-5: warmup, growing
+    sparsity, reduced search, mask reuse; Algorithm 4 is named there and its
+    control flow described in the prose), as a plain loop.
+
+    Reading of the schedule (T = search_steps, p = thresholds):
+
+    * t < T[0]: warmup, dense attention (every block kept);
+    * t = T[0]: first search over all blocks: Phase-1 G and row LSE of the dense
+      pass, W (Phase 2), Top-p at p[0]; the kept set is the candidate set S1 and
+      the current mask;
+    * t = T[k], k >= 1: reduced search inside S1: G and LSE of the pass over S1,
+      W normalised over S1, Top-p at p[k]; the kept set (inside S1) is the current
+      mask;
+    * any other t > T[0]: the current mask is reused.
+
+    ``qk_at(t)`` gives the (q, k) arrays [H, L_pad, d] of step t.  ``w_select`` maps a
+    search step to the block weights (CSR order of that search's candidate set) that
+    its Top-p runs on; by default the oracle's own W.  Returns (kinds, masks, weights):
+    the kind of every step, the mask [H, MB, NB] every step runs with, and the
+    oracle's W at every search step.
+    """
+    T, p = tuple(search_steps), tuple(thresholds)
+    if len(T) != len(p) or list(T) != sorted(T) or T[-1] >= steps:
+        raise ValueError("one threshold per increasing search step below the step count")
+    w_select = w_select or {}
+    kinds, masks, weights = [], [], {}
+    s1 = mask = dense = None
+    for t in range(steps):
+        q, k = qk_at(t)
+        if dense is None:
+            H, lp, _ = q.shape
+            mb = lp // block
+            dense = np.ones((H, mb, mb), dtype=np.uint8)
+        if t < T[0]:
+            kinds.append("warmup")
+            masks.append(dense)
+            continue
+        if t in T:
+            cand = dense if t == T[0] else s1
+            rp, ci, _, _, _ = block_index_of(cand)
+            g, lse = block_lse(q, k, rp, ci, seq_len, block, scale)
+            w = block_importance(g, lse, rp, seq_len, block)
+            weights[t] = w
+            w_used = w_select.get(t, w)
+            kept = topp_select(w_used, rp, ci, cand.shape[0], cand.shape[1], cand.shape[2],
+                               p[T.index(t)])
+            if t == T[0]:
+                s1 = kept
+            mask = kept
+            kinds.append("search")
+        else:
+            kinds.append("reuse")
+        masks.append(mask)
+    return kinds, masks, weights
+
+
+def block_index_of(mask: np.ndarray):
+    """The CSR of a block mask (the oracle's block_index, imported lazily)."""
+    from .block_index import block_index
+    return block_index(mask)

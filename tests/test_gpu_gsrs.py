@@ -165,6 +165,31 @@ def test_gsrs_search_pipeline_growing_sparsity():
     s1_ref = oracle.topp_select(w_ref, rp, ci, H, mb, mb, 0.9)
     diff = np.sum(s1_ref != s1n)
     assert diff <= max(2, 0.002 * s1_ref.sum()), diff
+    # Step 5 (the pass restricted to S1, GSRS reduced search): the index of S1 is the
+    # oracle's, G1 and W1 over S1 match the oracle's block LSE and block importance
+    # over the same candidate set, and S2 is exactly the oracle's Top-p(0.8) of the
+    # GPU's W1.
+    rp1, ci1, _, _, _ = oracle.block_index(s1n)
+    nnz1 = int(rp1[-1])
+    np.testing.assert_array_equal(idx1.row_ptr.cpu().numpy(), rp1)
+    np.testing.assert_array_equal(idx1.col_idx.cpu().numpy()[:nnz1], ci1)
+    g1_ref, lse1_ref = oracle.block_lse(q, k, rp1, ci1, w.seq_len, w.block, w.scale)
+    w1_ref = oracle.block_importance(g1_ref, lse1_ref, rp1, w.seq_len, w.block)
+    g1n = g1.cpu().numpy()[:nnz1].astype(np.float64)
+    L, b = w.seq_len, w.block
+    for r in range(H * mb):
+        u = r % mb
+        nrows = min(b, L - u * b)
+        lo, hi = rp1[r], rp1[r + 1]
+        if hi > lo:
+            np.testing.assert_allclose(g1n[lo:hi, :nrows], g1_ref[lo:hi, :nrows], atol=5e-3,
+                                       rtol=0)
+    fin = np.isfinite(lse1_ref[:, :L])
+    np.testing.assert_allclose(lse1.cpu().numpy()[:, :L][fin], lse1_ref[:, :L][fin], atol=5e-3,
+                               rtol=0)
+    np.testing.assert_allclose(wn[:nnz1], w1_ref, atol=2e-4, rtol=1e-3)
+    s2_ref = oracle.topp_select(w1.cpu().numpy()[:nnz1], rp1, ci1, H, mb, mb, 0.8)
+    np.testing.assert_array_equal(s2n, s2_ref)
 
 
 def test_gsrs_search_class_matches_the_explicit_chain():
@@ -285,3 +310,62 @@ def test_schedule_diagnostics_match_plain_schedule():
     for _, _, e, dist in b.trace:
         assert math.isfinite(float(e)) and float(e) >= 0.0
         assert math.isfinite(float(dist)) and float(dist) >= 0.0
+
+
+def test_gsrs_schedule_matches_the_oracle_step_by_step():
+    """GsrsSchedule against oracle.gsrs_schedule on drifting inputs: the same kind of
+    step, the same mask at every step (Top-p of each search decided on the GPU's W, so
+    the sets compare bit for bit), W at every search within the dense-pass tolerance
+    of the oracle's W over the same candidates, and the last step's O and LSE against
+    the oracle's attention under the last mask."""
+    dev = gpu()
+    w = synth.make_workload("gsrs75k", device="cuda", heads=2, grid=(2, 45, 80))
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    search, thresholds, steps = (2, 4, 6), (0.95, 0.9, 0.8), 8
+    banner(f"gsrs schedule vs oracle H={H} MB={mb} searches={search}")
+    states = synth.drift_states(w, len(search) + 1)
+    n_xcd = caq.schedule_info(0, w.head_dim)[0]
+    params = caq.ReorderParams(wave=64, n_slices=n_xcd, iters=5, skip_mode=caq.WA_SKIP_NEVER)
+    gs = GsrsSchedule(H, w.seq_len, w.head_dim, w.block, dev, reorder=params, steps=steps,
+                      search_steps=search, thresholds=thresholds)
+
+    def state(t):
+        return states[sum(1 for s_ in search if t >= s_)]
+
+    masks, w_gpu = [], {}
+
+    def on_step(t, kind):
+        masks.append(gs.mask.clone())
+        if kind == "search":
+            path = gs.full if t == search[0] else gs.search
+            nnz = int(path.row_ptr[-1].item())
+            w_gpu[t] = path.w[:nnz].clone()
+
+    gs.run(lambda t: (*state(t)[:3], w.x0), on_step)
+    torch.cuda.synchronize()
+    qk = {}
+
+    def qk_at(t):
+        i = sum(1 for s_ in search if t >= s_)
+        if i not in qk:
+            qk[i] = (np64(states[i][0]), np64(states[i][1]))
+        return qk[i]
+
+    wsel = {t: v.cpu().numpy() for t, v in w_gpu.items()}
+    kinds, masks_ref, w_ref = oracle.gsrs_schedule(steps, search, thresholds, qk_at,
+                                                   w.seq_len, w.block, w.scale, w_select=wsel)
+    assert gs.kinds == kinds
+    for t in range(steps):
+        if kinds[t] == "warmup":
+            continue  # the warmup runs the dense pass; the schedule keeps no mask then
+        np.testing.assert_array_equal(masks[t].cpu().numpy(), masks_ref[t], err_msg=f"step {t}")
+    for t in search:
+        np.testing.assert_allclose(wsel[t].astype(np.float64), w_ref[t], atol=2e-4, rtol=1e-3,
+                                   err_msg=f"W at step {t}")
+    # the last step: attention under the last mask with that step's inputs
+    q, k, v = (np64(x) for x in state(steps - 1)[:3])
+    L = w.seq_len
+    o_ref, lse_ref = oracle.masked_attention(q, k, v, masks_ref[-1], L, w.block, w.scale)
+    from helpers import assert_attention_close
+    assert_attention_close(np64(gs.sparse.o)[:, :L], gs.sparse.lse.cpu().numpy().astype(np.float64)[:, :L],
+                           o_ref[:, :L], lse_ref[:, :L], "last schedule step")

@@ -84,3 +84,22 @@ def test_stage2_inside_buckets():
         for lo, hi in oracle.wave_buckets(30, 2, 4):
             assert sorted(perm[h][lo:hi].tolist()) == sorted(base[lo:hi].tolist())
             assert list(-nnz[perm[h][lo:hi]]) == sorted(-nnz[perm[h][lo:hi]])
+
+
+def test_signature_priority_hand_worked():
+    """Hand-worked order with h1(v) = v and h2(v) = (P - 1) v + 5 mod P = 5 - v (for
+    v <= 5), so sig1 = smallest id and sig2 = 5 - largest id <= 5:
+
+        row 0 {3, 4}: (3, 1)    row 1 {1, 7}: (1, 4)
+        row 2 {3, 5}: (3, 0)    row 3 {2}:    (2, 3)
+
+    Sorted by sig1, then sig2, then row: 1, 3, 2, 0.  With sig2 primary the order
+    would be 2, 0, 3, 1; with the row index before sig2 it would be 1, 3, 0, 2."""
+    m = np.zeros((4, 8), dtype=np.uint8)
+    for r, ids in enumerate(([3, 4], [1, 7], [3, 5], [2])):
+        m[r, ids] = 1
+    a, b = [1, P - 1], [0, 5]
+    sig = oracle.minhash_signatures(m, a, b)
+    assert sig.tolist() == [[3, 1], [1, 4], [3, 0], [2, 3]]
+    order = oracle.minhash_order_head(m, a, b, wave=4, n_slices=1, stage2=False)
+    assert order.tolist() == [1, 3, 2, 0]

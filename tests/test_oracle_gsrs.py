@@ -189,3 +189,75 @@ def test_mask_recall_definition_and_identities():
             lo = rp[h * nb + u]
             kept = sum(wfull[lo + v] for v in range(nb) if mask[h, u, v])
             assert abs(kept - rec[h, u]) < 1e-12
+
+
+def _static_qk(seed=5, H=2, L=600, d=32, b=64):
+    rng = np.random.default_rng(seed)
+    mb = -(-L // b)
+    q = np.zeros((H, mb * b, d))
+    k = np.zeros((H, mb * b, d))
+    q[:, :L] = rng.standard_normal((H, L, d)) * 2.0
+    k[:, :L] = rng.standard_normal((H, L, d)) * 2.0
+    return q, k, L, b, d ** -0.5
+
+
+def test_schedule_steps_follow_warmup_search_and_reuse():
+    """The control flow of the schedule: dense warmup, searches at T, reuse of the
+    latest search's mask in between (GSRS §4-5)."""
+    q, k, L, b, scale = _static_qk()
+    kinds, masks, weights = oracle.gsrs_schedule(9, (2, 5, 7), (0.9, 0.5, 0.6),
+                                                 lambda t: (q, k), L, b, scale)
+    assert kinds == ["warmup", "warmup", "search", "reuse", "reuse", "search", "reuse",
+                     "search", "reuse"]
+    assert sorted(weights) == [2, 5, 7]
+    assert np.all(masks[0] == 1) and np.all(masks[1] == 1)
+    # reuse steps run the latest search's mask, not the candidate set
+    assert np.array_equal(masks[3], masks[2]) and np.array_equal(masks[4], masks[2])
+    assert np.array_equal(masks[6], masks[5]) and np.array_equal(masks[8], masks[7])
+    assert not np.array_equal(masks[6], masks[2])
+
+
+def test_reduced_search_stays_inside_the_candidate_set():
+    """Later searches select among S1 only: with a small first threshold and a large
+    later one, a search over all blocks would keep blocks outside S1."""
+    q, k, L, b, scale = _static_qk(seed=6)
+    kinds, masks, weights = oracle.gsrs_schedule(4, (1, 2), (0.3, 0.99),
+                                                 lambda t: (q, k), L, b, scale)
+    s1 = masks[1]
+    assert np.all(masks[2] <= s1) and np.all(masks[3] <= s1)
+    # W at the second search is normalised over S1: each row's weights sum to one
+    rp, _, _, _, _ = oracle.block_index(s1)
+    w = weights[2]
+    for r in range(len(rp) - 1):
+        if rp[r + 1] > rp[r]:
+            assert abs(w[rp[r]:rp[r + 1]].sum() - 1.0) < 1e-12
+    # and a dense search at 0.99 keeps strictly more than S1 holds
+    dense = np.ones_like(s1)
+    rpd, cid, _, _, _ = oracle.block_index(dense)
+    g, lse = oracle.block_lse(q, k, rpd, cid, L, b, scale)
+    wd = oracle.block_importance(g, lse, rpd, L, b)
+    kept = oracle.topp_select(wd, rpd, cid, *dense.shape, 0.99)
+    assert kept.sum() > s1.sum()
+
+
+def test_schedule_selects_on_the_given_weights():
+    """With weights supplied for a search step, its Top-p runs on them: one-hot rows
+    keep exactly their one block; p = 1 keeps every candidate."""
+    q, k, L, b, scale = _static_qk(seed=7)
+    H, lp, _ = q.shape
+    mb = lp // b
+    rp, ci, _, _, _ = oracle.block_index(np.ones((H, mb, mb), dtype=np.uint8))
+    onehot = np.zeros(int(rp[-1]), dtype=np.float32)
+    hot = {}
+    for r in range(H * mb):
+        j = (7 * r + 3) % mb
+        onehot[rp[r] + j] = 1.0
+        hot[r] = j
+    _, masks, _ = oracle.gsrs_schedule(3, (1, 2), (0.5, 1.0), lambda t: (q, k), L, b, scale,
+                                       w_select={1: onehot})
+    m1 = masks[1]
+    for r in range(H * mb):
+        h, u = divmod(r, mb)
+        assert m1[h, u].sum() == 1 and m1[h, u, hot[r]] == 1
+    # p = 1 over S1 keeps all of S1
+    assert np.array_equal(masks[2], m1)
