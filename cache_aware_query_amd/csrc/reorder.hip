@@ -835,21 +835,12 @@ hipError_t launch_reorder(const int32_t* row_ptr, const int32_t* col_idx, const 
   if (rowbits && rowbits_bytes > embed_bytes) embed_bytes = rowbits_bytes;
   const size_t sort_bytes = (size_t)n2 * (sizeof(uint64_t) + sizeof(uint32_t));
   const size_t lds = embed_bytes > sort_bytes ? embed_bytes : sort_bytes;
-  // The dynamic LDS limit is a per-device function attribute; set it once per device.
-  static bool attr_set[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  // The dynamic LDS limit is a function attribute of the current device; setting it
+  // is idempotent and cheap, so every launch sets it (no state kept between calls).
+  hipError_t e = hipFuncSetAttribute((const void*)(use_bits ? k_reorder<true> : k_reorder<false>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     160 * 1024 - 4096);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (!attr_set[dev]) {
-    e = hipFuncSetAttribute((const void*)k_reorder<false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 4096);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)k_reorder<true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 4096);
-    if (e != hipSuccess) return e;
-    attr_set[dev] = true;
-  }
   DevParams dp{p.wave, p.n_slices, p.iters, p.stage1, p.stage2, p.skip_mode,
                p.ws_min_bytes, p.flops_min, p.jaccard_max};
   const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
