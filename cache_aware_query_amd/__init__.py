@@ -34,7 +34,7 @@ EXPORTED = (
     "wa_reorder_rows", "wa_reorder_needs_csc", "wa_minhash_order", "wa_sparse_attn_workspace_size",
     "wa_sparse_attn_fwd", "wa_sparse_attn_fwd_diag", "wa_attn_schedule_select",
     "wa_block_importance", "wa_topp_select", "wa_mask_recall", "wa_gather_blocks",
-    "wa_scatter_blocks", "wa_xcd_placement",
+    "wa_scatter_blocks", "wa_xcd_placement", "wa_sparse_attn_fwd_noalloc",
 )
 
 
@@ -123,6 +123,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                    _I64, _P, _I32, _I32, ctypes.c_float, _P, _P,
                                                    _P, _P, _P, _P, ctypes.c_size_t, _P]),
         "wa_xcd_placement": (ctypes.c_int, [_I32, _I32, _P, _P]),
+        "wa_sparse_attn_fwd_noalloc": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P,
+                                                      _I64, _P, _I32, _I32, _P, ctypes.c_float,
+                                                      _P, _P, _P, _P]),
         "wa_block_importance": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P,
                                                _P]),
         "wa_topp_select": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, ctypes.c_double,

@@ -158,13 +158,14 @@ int wa_sparse_attn_workspace_size(int32_t H, int32_t L, int32_t head_dim, int32_
   return ok();
 }
 
-static int sparse_attn_common(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
-                              int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
-                              const int32_t* col_idx, int64_t capacity, const int32_t* perm,
-                              int32_t perm_slices, int32_t schedule, float scale, wa_bf16* o,
-                              float* lse, float* g,
-                              float* entropy, float* distance, void* workspace,
-                              size_t workspace_bytes, void* stream, const char* name) {
+// Host-side validation of an attention call; on success *n_xcd is the XCD count of
+// the stream's device and nothing has been enqueued.
+static int sparse_attn_check(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
+                             int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
+                             const int32_t* col_idx, int64_t capacity, const int32_t* perm,
+                             int32_t perm_slices, int32_t schedule, float scale, wa_bf16* o,
+                             float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                             int* n_xcd_out) {
   if (!q || !k || !v || !row_ptr || !col_idx || !o || !lse)
     return fail(WA_ERR_INVALID_ARG, "null pointer argument");
   if (H < 1 || L < 1) return fail(WA_ERR_INVALID_ARG, "H and L must be >= 1");
@@ -199,11 +200,68 @@ static int sparse_attn_common(const wa_bf16* q, const wa_bf16* k, const wa_bf16*
     return fail(WA_ERR_INVALID_ARG,
                 "perm was built for %d slices but the XCD-sliced schedule runs %d (the device's "
                 "XCD count)", perm_slices, n_xcd);
+  *n_xcd_out = n_xcd;
+  return WA_OK;
+}
+
+static int sparse_attn_common(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
+                              int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
+                              const int32_t* col_idx, int64_t capacity, const int32_t* perm,
+                              int32_t perm_slices, int32_t schedule, float scale, wa_bf16* o,
+                              float* lse, float* g, float* entropy, float* distance,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              const char* name) {
+  int n_xcd = 1;
+  const int rc = sparse_attn_check(q, k, v, H, L, head_dim, block, row_ptr, col_idx, capacity,
+                                   perm, perm_slices, schedule, scale, o, lse, workspace,
+                                   workspace_bytes, stream, &n_xcd);
+  if (rc != WA_OK) return rc;
   return hip_status(wa::launch_sparse_attn(q, k, v, H, L, head_dim, block, row_ptr, col_idx,
                                            capacity, perm, schedule, n_xcd, scale, o, lse, g,
                                            entropy, distance, workspace,
                                            static_cast<hipStream_t>(stream)),
                     name);
+}
+
+int wa_sparse_attn_fwd_noalloc(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
+                               int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
+                               const int32_t* col_idx, int64_t capacity, const int32_t* perm,
+                               int32_t perm_slices, int32_t schedule, const uint8_t* skipped,
+                               float scale, wa_bf16* o, float* lse, float* g, void* stream) {
+  if (schedule == WA_SCHED_AUTO && !skipped)
+    return fail(WA_ERR_INVALID_ARG, "WA_SCHED_AUTO needs the skip flags");
+  if (H < 1 || L < 1) return fail(WA_ERR_INVALID_ARG, "H and L must be >= 1");
+  if (!supported_shape(head_dim, block))
+    return fail(WA_ERR_UNSUPPORTED, "head_dim %d / block %d not in {64, 128}", head_dim, block);
+  const int64_t MB = ((int64_t)L + block - 1) / block;
+  if ((int64_t)H * MB * 8 >= ((int64_t)1 << 31))
+    return fail(WA_ERR_UNSUPPORTED, "too many query blocks");
+  const size_t need = wa::attn_workspace_bytes(H, (int)(MB * block), head_dim);
+  if (need > wa::kStaticScratchBytes)
+    return fail(WA_ERR_CAPACITY, "these sizes need %zu bytes of scratch; the static scratch "
+                "holds %zu", need, wa::kStaticScratchBytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "device of the stream");
+  void* scratch = nullptr;
+  e = wa::static_scratch(dev, &scratch);
+  if (e != hipSuccess) return hip_status(e, "static scratch address");
+  int n_xcd = 1;
+  const int rc = sparse_attn_check(q, k, v, H, L, head_dim, block, row_ptr, col_idx, capacity,
+                                   perm, perm_slices, schedule, scale, o, lse, scratch,
+                                   wa::kStaticScratchBytes, stream, &n_xcd);
+  if (rc != WA_OK) return rc;
+  if (schedule == WA_SCHED_AUTO) {
+    // The schedule word is written whole by the selection kernel, so nothing has to
+    // be cleared first.
+    e = wa::launch_sched_select(skipped, H, scratch, s);
+    if (e != hipSuccess) return hip_status(e, "wa_sparse_attn_fwd_noalloc (schedule)");
+  }
+  return hip_status(wa::launch_sparse_attn(q, k, v, H, L, head_dim, block, row_ptr, col_idx,
+                                           capacity, perm, schedule, n_xcd, scale, o, lse, g,
+                                           nullptr, nullptr, scratch, s),
+                    "wa_sparse_attn_fwd_noalloc");
 }
 
 int wa_xcd_placement(int32_t n_wg, int32_t block, int32_t* xcd_out, void* stream) {

@@ -46,9 +46,17 @@
 //    the concurrent-head execution WaveAlign compares sequential heads with.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "wa_internal.h"
+
+// Scratch of the allocation-free entry point (wa_sparse_attn_fwd_noalloc): the
+// schedule word WA_SCHED_AUTO reads, written on the device by k_sched_select.  Each
+// GPU the library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, not the device array: kernels get the device
+// address that static_scratch() looks up.
+static __device__ __align__(256) int scratch[wa::kStaticScratchBytes / sizeof(int)];
 
 namespace wa {
 namespace {
@@ -726,6 +734,34 @@ __global__ __launch_bounds__(64) void k_sched_select(const uint8_t* __restrict__
   if (threadIdx.x == 0) out[0] = some_reordered ? WA_SCHED_XCD_SLICED : WA_SCHED_HEADS_INTERLEAVED;
 }
 }  // namespace
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // Once per device, with that device current: the device address of its copy.
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_sched_select(const uint8_t* skipped, int H, void* workspace, hipStream_t s) {
   hipLaunchKernelGGL(k_sched_select, dim3(1), dim3(64), 0, s, skipped, H,

@@ -37,6 +37,12 @@ hipError_t launch_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16
                               int schedule, int n_xcd, float scale, uint16_t* o, float* lse,
                               float* g, float* ent, float* dist, void* workspace, hipStream_t s);
 hipError_t launch_xcd_placement(int n_wg, int block, int32_t* out, hipStream_t s);
+
+// The static device scratch of wa_sparse_attn_fwd_noalloc: its size, and the device
+// address of device `dev`'s copy (looked up once per device).
+constexpr size_t kStaticScratchBytes = 256;
+constexpr int kMaxDevices = 64;
+hipError_t static_scratch(int dev, void** out);
 int attn_resident_wgs_per_cu(int head_dim, int block);
 
 hipError_t launch_block_importance(const float* g, const float* lse, const int32_t* row_ptr,

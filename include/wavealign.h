@@ -236,6 +236,27 @@ int wa_sparse_attn_fwd(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int
                        void* stream);
 
 /*
+ * wa_sparse_attn_fwd_noalloc - wa_sparse_attn_fwd for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It allocates nothing: the 256-byte
+ * schedule word that WA_SCHED_AUTO reads lives in a static device array of the
+ * library (one copy per GPU, held until the process ends, its address looked up once
+ * per device on the first call there).
+ *   skipped   uint8 [H] (wa_reorder_rows) with WA_SCHED_AUTO: the call then enqueues
+ *             the schedule choice of wa_attn_schedule_select into the static array
+ *             before the attention; ignored (may be NULL) for the other schedules
+ * Every other argument, the results and the errors are those of wa_sparse_attn_fwd,
+ * plus WA_ERR_CAPACITY if these sizes needed more scratch than the static 256 bytes
+ * (none does at present).  Calls that overlap on one GPU share its array and race:
+ * enqueue them on one stream, or let one finish before the next starts.
+ */
+int wa_sparse_attn_fwd_noalloc(const wa_bf16* q, const wa_bf16* k, const wa_bf16* v, int32_t H,
+                               int32_t L, int32_t head_dim, int32_t block, const int32_t* row_ptr,
+                               const int32_t* col_idx, int64_t capacity, const int32_t* perm,
+                               int32_t perm_slices, int32_t schedule, const uint8_t* skipped,
+                               float scale, wa_bf16* o, float* lse, float* g, void* stream);
+
+/*
  * wa_xcd_placement - [WA §II-C: a wave is the set of row tasks resident at once on
  * processors that share one L2] checks the dispatch the XCD-sliced schedule relies
  * on: launches n_wg workgroups of the attention kernel's size for `block` and writes,
