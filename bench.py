@@ -468,6 +468,20 @@ def main():
                               out=(hp_mh.perm, hp_mh.inv_perm))
         minhash()
         t_minhash = _time_calls(minhash, reps)
+        # The banded LSH comparator of the same table (four bands of two MinHash
+        # values; each row joins the lowest row it shares a bucket with), every head.
+        hp_lsh = share_g(HotPath(H, L, d, b, dev, capacity=nnz,
+                                 reorder=caq.ReorderParams(wave=wave, n_slices=n_xcd,
+                                                           skip_mode=caq.WA_SKIP_NEVER),
+                                 schedule=caq.WA_SCHED_XCD_SLICED, gsrs_p=0.9))
+        hp_lsh.build_index(w.mask)
+        lsh_a, lsh_b = synth.minhash_params(8, seed=synth.workloads.BASE_SEED + 100)
+
+        def lsh():
+            caq.lsh_order(hp_lsh.index(), lsh_a, lsh_b, wave, n_xcd, True,
+                          out=(hp_lsh.perm, hp_lsh.inv_perm))
+        lsh()
+        t_lsh = _time_calls(lsh, reps)
         # The explicit form of applying the permutation ([WA] §V: gather the Q blocks
         # into execution order before the kernel, scatter O back after it), which the
         # fused kernel avoids; both copies are HBM-bound.
@@ -486,6 +500,7 @@ def main():
         perm_bytes = 2 * 2 * H * mb * blk_bytes  # Q and O, each read and written once
         del q_x, o_x
         ablation["minhash_order"] = hp_mh
+        ablation["lsh_order"] = hp_lsh
 
         def with_schedule(path, sched):
             def run():
@@ -519,6 +534,8 @@ def main():
                        "index_ms_without_reorder": round(t_index_id, 4)})
         detail.update({f"attn_ms_{k}": round(v, 4) for k, v in t.items()})
         detail["minhash_order_ms"] = round(t_minhash, 4)
+        detail["lsh_order_ms"] = round(t_lsh, 4)
+        detail["e2e_ms_lsh"] = round(t_index + t_lsh + t["lsh_order"], 4)
         detail["explicit_permute_ms"] = round(t_perm, 4)
         detail["explicit_permute_gb_per_s"] = round(perm_bytes / (t_perm * 1e-3) / 1e9, 1)
         detail["e2e_ms_minhash"] = round(t_index + t_minhash + t["minhash_order"], 4)

@@ -34,7 +34,7 @@ EXPORTED = (
     "wa_reorder_rows", "wa_reorder_needs_csc", "wa_minhash_order", "wa_sparse_attn_workspace_size",
     "wa_sparse_attn_fwd", "wa_sparse_attn_fwd_diag", "wa_attn_schedule_select",
     "wa_block_importance", "wa_topp_select", "wa_mask_recall", "wa_gather_blocks",
-    "wa_scatter_blocks", "wa_xcd_placement", "wa_sparse_attn_fwd_noalloc",
+    "wa_scatter_blocks", "wa_xcd_placement", "wa_sparse_attn_fwd_noalloc", "wa_lsh_order",
 )
 
 
@@ -111,6 +111,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                            ctypes.POINTER(_ReorderParams), _P, _P, _P, _P, _P,
                                            _P]),
         "wa_reorder_needs_csc": (ctypes.c_int, [_I32, _I32]),
+        "wa_lsh_order": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _P, _P, _I32, _I32,
+                                        _I32, _I32, _P, _P, _P]),
         "wa_minhash_order": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _P, _P, _I32, _I32,
                                             _I32, _I32, _P, _P, _P]),
         "wa_sparse_attn_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32,
@@ -272,6 +274,29 @@ def minhash_order(index: BlockIndex, hash_a, hash_b, wave: int, n_slices: int,
     _check(lib.wa_minhash_order(_ptr(index.row_ptr), _ptr(index.col_idx), index.col_idx.numel(),
                                 H, MB, NB, a, b, n, wave, n_slices, 1 if stage2 else 0, _ptr(perm),
                                 _ptr(inv), _stream(dev)), "wa_minhash_order")
+    return perm, inv
+
+
+def lsh_order(index: BlockIndex, hash_a, hash_b, wave: int, n_slices: int,
+              stage2: bool = True, out: tuple | None = None):
+    """The banded LSH comparator order (wa_lsh_order): len(hash_a) / 2 bands of two
+    MinHash values each; returns (perm, inv_perm)."""
+    lib = load_library()
+    H, MB, NB = index.heads, index.mb, index.nb
+    n = len(hash_a)
+    if n != len(hash_b) or n % 2 or not 2 <= n <= 8:
+        raise ValueError("hash_a and hash_b must both hold 2, 4, 6 or 8 coefficients")
+    dev = index.row_ptr.device
+    if out is None:
+        perm = torch.empty(H, MB, dtype=torch.int32, device=dev)
+        inv = torch.empty(H, MB, dtype=torch.int32, device=dev)
+    else:
+        perm, inv = out
+    a = (ctypes.c_uint32 * n)(*[int(x) for x in hash_a])
+    b = (ctypes.c_uint32 * n)(*[int(x) for x in hash_b])
+    _check(lib.wa_lsh_order(_ptr(index.row_ptr), _ptr(index.col_idx), index.col_idx.numel(),
+                            H, MB, NB, a, b, n // 2, wave, n_slices, 1 if stage2 else 0,
+                            _ptr(perm), _ptr(inv), _stream(dev)), "wa_lsh_order")
     return perm, inv
 
 

@@ -139,6 +139,30 @@ int wa_minhash_order(const int32_t* row_ptr, const int32_t* col_idx, int64_t cap
                     "wa_minhash_order");
 }
 
+int wa_lsh_order(const int32_t* row_ptr, const int32_t* col_idx, int64_t capacity, int32_t H,
+                 int32_t MB, int32_t NB, const uint32_t* hash_a, const uint32_t* hash_b,
+                 int32_t n_bands, int32_t wave, int32_t n_slices, int32_t stage2,
+                 int32_t* perm, int32_t* inv_perm, void* stream) {
+  if (!row_ptr || !col_idx || !hash_a || !hash_b || !perm || !inv_perm)
+    return fail(WA_ERR_INVALID_ARG, "null pointer argument");
+  if (H < 1 || MB < 1 || NB < 1) return fail(WA_ERR_INVALID_ARG, "H, MB, NB must be >= 1");
+  if (MB > WA_MAX_BLOCKS || NB > WA_MAX_BLOCKS)
+    return fail(WA_ERR_UNSUPPORTED, "MB and NB must be <= %d", WA_MAX_BLOCKS);
+  if (capacity < 0) return fail(WA_ERR_INVALID_ARG, "negative capacity");
+  if (n_bands < 1 || n_bands > wa::kLshMaxBands)
+    return fail(WA_ERR_INVALID_ARG, "n_bands must be in 1..%d", wa::kLshMaxBands);
+  for (int i = 0; i < 2 * n_bands; ++i)
+    if (hash_a[i] < 1 || hash_a[i] >= 0x7fffffffu || hash_b[i] >= 0x7fffffffu)
+      return fail(WA_ERR_INVALID_ARG, "hash coefficients must satisfy 1 <= a < 2^31-1, b < 2^31-1");
+  if (wave < 1) return fail(WA_ERR_INVALID_ARG, "wave must be >= 1");
+  if (n_slices < 1 || n_slices > 64) return fail(WA_ERR_INVALID_ARG, "n_slices must be in 1..64");
+  if (stage2 != 0 && stage2 != 1) return fail(WA_ERR_INVALID_ARG, "stage2 must be 0 or 1");
+  return hip_status(wa::launch_lsh_order(row_ptr, col_idx, capacity, H, MB, NB, hash_a, hash_b,
+                                         n_bands, wave, n_slices, stage2, perm, inv_perm,
+                                         static_cast<hipStream_t>(stream)),
+                    "wa_lsh_order");
+}
+
 int wa_reorder_needs_csc(int32_t MB, int32_t NB) {
   if (MB < 1 || NB < 1) return fail(WA_ERR_INVALID_ARG, "MB and NB must be >= 1");
   if (MB > WA_MAX_BLOCKS || NB > WA_MAX_BLOCKS)

@@ -808,7 +808,102 @@ __global__ __launch_bounds__(kThreads) void k_minhash_order(
                    perm + (size_t)h * MB, inv_perm + (size_t)h * MB);
 }
 
+// ---- The banded LSH comparator order (WaveAlign Table II) ----
+// One workgroup per head.  Band b's bucket of a row is the pair of its MinHash values
+// under hash functions 2b and 2b+1, as one 62-bit key.  Rows sorted by (key, row) put
+// each bucket in one run whose first element is its lowest row; every row takes the
+// lowest such row over the bands as its label (one owner per row and band, so no two
+// threads update a label in the same band).  Rows are then ordered by (label, row)
+// and the same Stage 2 follows.
+__global__ __launch_bounds__(kThreads) void k_lsh_order(
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int cap, int MB,
+    int NB, LshHashes hs, int n_bands, int wave, int n_slices, int stage2,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  extern __shared__ double2 lds[];
+  const int h = blockIdx.x, t = threadIdx.x;
+  const int w = t >> 6, lane = t & 63;
+  const int32_t* rp = row_ptr + (size_t)h * MB;
+  int n2 = 1;
+  while (n2 < MB) n2 <<= 1;
+  uint64_t* key = reinterpret_cast<uint64_t*>(lds);
+  uint32_t* val = reinterpret_cast<uint32_t*>(key + n2);
+  int* label = reinterpret_cast<int*>(val + n2);
+  for (int u = t; u < MB; u += kThreads) label[u] = u;
+  for (int b = 0; b < n_bands; ++b) {
+    const uint32_t a0 = hs.a[2 * b], b0 = hs.b[2 * b], a1 = hs.a[2 * b + 1], b1 = hs.b[2 * b + 1];
+    for (int u = w; u < MB; u += kWaves) {
+      uint32_t m0 = kMinhashP, m1 = kMinhashP;
+      const int lo = min(rp[u], cap), hi = min(rp[u + 1], cap);
+      for (int k = lo + lane; k < hi; k += 64) {
+        const int v = col_idx[k];
+        if ((unsigned)v < (unsigned)NB) {
+          m0 = min(m0, minhash(a0, b0, v));
+          m1 = min(m1, minhash(a1, b1, v));
+        }
+      }
+      m0 = wave_min_u32(m0);
+      m1 = wave_min_u32(m1);
+      if (lane == 0) {
+        key[u] = ((uint64_t)m0 << 31) | m1;
+        val[u] = (uint32_t)u;
+      }
+    }
+    for (int u = MB + t; u < n2; u += kThreads) {
+      key[u] = ~0ull;
+      val[u] = (uint32_t)u;
+    }
+    sort_pairs(key, val, n2);  // ends with a barrier
+    for (int p = t; p < MB; p += kThreads) {
+      // first position of the run of key[p]: the lowest row of its bucket
+      const uint64_t k = key[p];
+      int lo = 0, hi = p;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (key[mid] < k) lo = mid + 1;
+        else hi = mid;
+      }
+      const int row = (int)val[p], first = (int)val[lo];
+      if (first < label[row]) label[row] = first;
+    }
+    __syncthreads();  // the next band's keys overwrite the sorted ones
+  }
+  for (int u = t; u < n2; u += kThreads) {
+    key[u] = u < MB ? ((uint64_t)label[u] << 32) | (uint32_t)u : ~0ull;
+    val[u] = (uint32_t)u;
+  }
+  sort_pairs(key, val, n2);
+  stage2_and_write(key, val, n2, rp, cap, MB, NB, wave, n_slices, stage2 != 0,
+                   perm + (size_t)h * MB, inv_perm + (size_t)h * MB);
+}
+
 }  // namespace
+
+size_t lsh_lds_bytes(int MB, int n_bands) {
+  (void)n_bands;
+  int n2 = 1;
+  while (n2 < MB) n2 <<= 1;
+  return (size_t)n2 * (sizeof(uint64_t) + sizeof(uint32_t)) + (size_t)MB * sizeof(int);
+}
+
+hipError_t launch_lsh_order(const int32_t* row_ptr, const int32_t* col_idx, int64_t cap64, int H,
+                            int MB, int NB, const uint32_t* hash_a, const uint32_t* hash_b,
+                            int n_bands, int wave, int n_slices, int stage2, int32_t* perm,
+                            int32_t* inv_perm, hipStream_t s) {
+  LshHashes hs{};
+  for (int i = 0; i < 2 * n_bands; ++i) {
+    hs.a[i] = hash_a[i];
+    hs.b[i] = hash_b[i];
+  }
+  const size_t lds = lsh_lds_bytes(MB, n_bands);
+  hipError_t e = hipFuncSetAttribute((const void*)k_lsh_order,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     160 * 1024 - 4096);
+  if (e != hipSuccess) return e;
+  const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
+  hipLaunchKernelGGL(k_lsh_order, dim3(H), dim3(kThreads), lds, s, row_ptr, col_idx, cap, MB, NB,
+                     hs, n_bands, wave, n_slices, stage2, perm, inv_perm);
+  return hipGetLastError();
+}
 
 size_t reorder_bits_lds_bytes(int MB, int NB) {
   const size_t MW = (MB + 31) / 32;

@@ -25,6 +25,17 @@ hipError_t launch_minhash_order(const int32_t* row_ptr, const int32_t* col_idx, 
                                 const uint32_t* hash_b, int n_hash, int wave, int n_slices,
                                 int stage2, int32_t* perm, int32_t* inv_perm, hipStream_t s);
 
+// Hash coefficients of the LSH comparator: two MinHash functions per band.
+constexpr int kLshMaxBands = 4;
+struct LshHashes {
+  uint32_t a[2 * kLshMaxBands], b[2 * kLshMaxBands];
+};
+hipError_t launch_lsh_order(const int32_t* row_ptr, const int32_t* col_idx, int64_t cap, int H,
+                            int MB, int NB, const uint32_t* hash_a, const uint32_t* hash_b,
+                            int n_bands, int wave, int n_slices, int stage2, int32_t* perm,
+                            int32_t* inv_perm, hipStream_t s);
+size_t lsh_lds_bytes(int MB, int n_bands);
+
 // True if the reorder of an MB x NB mask cannot hold the mask as bitmasks in LDS
 // and must read the transposed lists (CSC) instead.
 bool reorder_needs_csc(int MB, int NB);

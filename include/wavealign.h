@@ -182,6 +182,28 @@ int wa_minhash_order(const int32_t* row_ptr, const int32_t* col_idx, int64_t cap
                      int32_t n_hash, int32_t wave, int32_t n_slices, int32_t stage2,
                      int32_t* perm, int32_t* inv_perm, void* stream);
 
+/*
+ * wa_lsh_order - the banded locality-sensitive-hashing comparator row order of
+ * [WA §VI, Table II (comparison with other reordering algorithms)]: per head, band b
+ * (b < n_bands <= 4) puts row u in the bucket (sig_2b(u), sig_2b+1(u)) of its MinHash
+ * values (as in wa_minhash_order, hash functions 2b and 2b+1); each row is labelled
+ * with the lowest row it shares a bucket with in any band (itself if none is lower,
+ * no transitive closure) and rows are ordered by (label, row): a row and the higher
+ * rows directly similar to it run together, groups in the order of their first row,
+ * and a row that shares no bucket keeps its place relative to the others.  With
+ * stage2 = 1 the same wave buckets and NNZ-descending Stage 2 follow [WA §IV-D].  No
+ * skip rule.  Integer work, bit-exact.
+ *   hash_a, hash_b  host arrays of 2 * n_bands coefficients, 1 <= a < 2^31 - 1,
+ *                   0 <= b < 2^31 - 1 (drawn by the caller)
+ *   other arguments as wa_minhash_order
+ * Errors: WA_ERR_INVALID_ARG (null pointer, sizes, coefficients, n_bands, wave,
+ * n_slices, stage2), WA_ERR_UNSUPPORTED (MB or NB > WA_MAX_BLOCKS), WA_ERR_HIP.
+ */
+int wa_lsh_order(const int32_t* row_ptr, const int32_t* col_idx, int64_t capacity, int32_t H,
+                 int32_t MB, int32_t NB, const uint32_t* hash_a, const uint32_t* hash_b,
+                 int32_t n_bands, int32_t wave, int32_t n_slices, int32_t stage2,
+                 int32_t* perm, int32_t* inv_perm, void* stream);
+
 /* 1 if wa_reorder_rows needs the CSC (csc_ptr, csc_idx) for an MB x NB mask,
  * 0 if it reads only the CSR (see wa_reorder_rows), negative on bad sizes. */
 int wa_reorder_needs_csc(int32_t MB, int32_t NB);

@@ -19,8 +19,9 @@ Every function restates a computation from the two source pages:
   Appendix A.2), fully masked rows (note to Algorithm 2), Top-p selection
   (Algorithm 3) and the multi-step schedule of growing sparsity and reduced
   search (§4-5, Algorithm 4).
-* The MinHash row order that WaveAlign's Table II compares against
-  (``comparators``), from the published min-wise hashing it names.
+* The MinHash and banded-LSH row orders that WaveAlign's Table II compares
+  against (``comparators``), from the published min-wise hashing and the banded
+  locality-sensitive hashing of its signatures.
 
 Floating point is fp64 throughout; bf16 inputs are widened exactly.  Where the
 pages leave a step open the reading taken is stated in the function's
@@ -56,5 +57,6 @@ from .gsrs import (  # noqa: F401
     topp_select,
 )
 from .permute import gather_blocks, scatter_blocks  # noqa: F401
-from .comparators import (MINHASH_P, minhash_order, minhash_order_head,  # noqa: F401
+from .comparators import (LSH_ROWS_PER_BAND, MINHASH_P, lsh_components,  # noqa: F401
+                          lsh_order, lsh_order_head, minhash_order, minhash_order_head,
                           minhash_signatures)

@@ -41,3 +41,39 @@ def test_minhash_order_full_size(name, over):
     n_xcd, _, wave = caq.schedule_info(0, w.head_dim)
     banner(f"minhash order {name} {over}")
     _check(w.mask, 2, wave=wave, n_slices=n_xcd, stage2=True)
+
+
+def _check_lsh(mask, n_bands, wave, n_slices, stage2, seed=0):
+    dev = gpu()
+    a, b = synth.minhash_params(2 * n_bands, seed=synth.workloads.BASE_SEED + 100 + seed)
+    idx = caq.build_block_index(mask.to(dev))
+    perm, inv = caq.lsh_order(idx, a, b, wave, n_slices, stage2)
+    torch.cuda.synchronize()
+    perm_o, inv_o = oracle.lsh_order(mask.cpu().numpy(), a, b, n_bands, wave, n_slices, stage2)
+    np.testing.assert_array_equal(perm.cpu().numpy(), perm_o)
+    np.testing.assert_array_equal(inv.cpu().numpy(), inv_o)
+
+
+@pytest.mark.parametrize("n_bands", [1, 4])
+@pytest.mark.parametrize("stage2", [False, True])
+@pytest.mark.parametrize("mb,density", [(16, 0.4), (100, 0.05), (591, 0.02), (760, 0.3)])
+def test_lsh_order_matches_oracle(mb, density, stage2, n_bands):
+    """Low densities make many rows share buckets (few blocks per row), so the groups
+    are large and joined across bands."""
+    w = synth.random_tiny_case(mb + 7 * n_bands, heads=2, seq_len=mb * 64, head_dim=64, block=64,
+                               density=density, empty_rows=(1, mb - 1))
+    banner(f"lsh order MB={mb} rho={density} stage2={stage2} n_bands={n_bands}")
+    _check_lsh(w.mask, n_bands, wave=8, n_slices=4, stage2=stage2, seed=n_bands)
+
+
+def test_lsh_order_structured_and_largest():
+    """Wan-shaped masks (similar neighbouring rows), and the largest supported mask
+    (4,096 blocks per side) whose LDS holds four bands of edges."""
+    w = synth.make_workload("wan75k", device="cuda", heads=4)
+    n_xcd, _, wave = caq.schedule_info(0, w.head_dim)
+    banner("lsh order wan75k heads=4")
+    _check_lsh(w.mask, 4, wave=wave, n_slices=n_xcd, stage2=True)
+    big = synth.random_tiny_case(91, heads=1, seq_len=4096 * 64 - 5, head_dim=64, block=64,
+                                 density=0.001, empty_rows=(3,))
+    banner("lsh order MB=4096")
+    _check_lsh(big.mask, 4, wave=64, n_slices=8, stage2=True, seed=9)

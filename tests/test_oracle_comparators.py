@@ -103,3 +103,65 @@ def test_signature_priority_hand_worked():
     assert sig.tolist() == [[3, 1], [1, 4], [3, 0], [2, 3]]
     order = oracle.minhash_order_head(m, a, b, wave=4, n_slices=1, stage2=False)
     assert order.tolist() == [1, 3, 2, 0]
+
+
+def test_lsh_groups_hand_worked():
+    """Two bands of two hashes.  Band 0: h(v) = v and h(v) = (P - 1) v + 9 (= 9 - v for
+    v <= 9), i.e. (smallest id, 9 - largest id); band 1 uses the same two hashes in the
+    other order, so it groups the same rows.
+
+        row 0 {2, 5}: band 0 (2, 4)      row 1 {2, 5}: (2, 4)   (identical to row 0)
+        row 2 {1, 3}: (1, 6)             row 3 {6}:    (6, 3)
+        row 4 {1, 3, 8}: (1, 1)          row 5 {1, 3}: (1, 6)   (identical to row 2)
+
+    Buckets shared: {0, 1} and {2, 5}; rows 3 and 4 alone.  Groups in order of their
+    first row: [0, 1], [2, 5], [3], [4]."""
+    m = np.zeros((6, 10), dtype=np.uint8)
+    for r, ids in enumerate(([2, 5], [2, 5], [1, 3], [6], [1, 3, 8], [1, 3])):
+        m[r, ids] = 1
+    a = [1, P - 1, P - 1, 1]
+    b = [0, 9, 9, 0]
+    sig = oracle.minhash_signatures(m, a, b)
+    assert sig[:, :2].tolist() == [[2, 4], [2, 4], [1, 6], [6, 3], [1, 1], [1, 6]]
+    label = oracle.lsh_components(m, a, b, n_bands=2)
+    assert label.tolist() == [0, 0, 2, 3, 4, 2]
+    order = oracle.lsh_order_head(m, a, b, 2, wave=8, n_slices=1, stage2=False)
+    assert order.tolist() == [0, 1, 2, 5, 3, 4]
+
+
+def test_lsh_joins_directly_similar_rows_only():
+    """Row 0 shares band 0 with row 1, row 1 shares band 1 with row 2, rows 0 and 2
+    share nothing: row 1 joins row 0, row 2 joins row 1 (its lowest direct neighbour),
+    not row 0 (no transitive closure)."""
+    # band 0: (min id, min id); band 1: (9 - max id, 9 - max id) with h(v) = 9 - v
+    a = [1, 1, P - 1, P - 1]
+    b = [0, 0, 9, 9]
+    m = np.zeros((4, 10), dtype=np.uint8)
+    m[0, [0, 4]] = 1      # band 0 key (0, 0), band 1 key (5, 5)
+    m[1, [0, 7]] = 1      # band 0 (0, 0) with row 0;  band 1 (2, 2)
+    m[2, [3, 7]] = 1      # band 0 (3, 3);  band 1 (2, 2) with row 1
+    m[3, [1, 2]] = 1      # band 0 (1, 1), band 1 (7, 7): alone
+    label = oracle.lsh_components(m, a, b, n_bands=2)
+    assert label.tolist() == [0, 0, 1, 3]
+    # with band 0 alone row 2 joins nobody
+    assert oracle.lsh_components(m, a, b, n_bands=1).tolist() == [0, 0, 2, 3]
+    # order by (label, row): 0, 1 | 2 | 3 ... and a far row joins its group: move row 1's
+    # lists to the end (row 3) and it still lands next to row 0
+    m2 = m[[0, 3, 2, 1]]
+    order = oracle.lsh_order_head(m2, a, b, 2, wave=8, n_slices=1, stage2=False)
+    assert order.tolist() == [0, 3, 1, 2]
+
+
+def test_lsh_identical_rows_share_a_group_and_empty_rows_group_together():
+    rng = np.random.default_rng(5)
+    m = (rng.random((30, 50)) < 0.2).astype(np.uint8)
+    m[17] = m[4]
+    m[9] = 0
+    m[22] = 0
+    ha = rng.integers(1, P, size=8)
+    hb = rng.integers(0, P, size=8)
+    label = oracle.lsh_components(m, ha, hb, n_bands=4)
+    assert label[17] == label[4] and label[9] == label[22]
+    assert all(label[u] <= u for u in range(30))
+    perm, inv = oracle.lsh_order(m[None], ha, hb, 4, wave=4, n_slices=2)
+    assert sorted(perm[0].tolist()) == list(range(30))
