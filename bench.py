@@ -33,6 +33,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -347,6 +348,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     import cache_aware_query_amd as caq
@@ -398,24 +400,44 @@ def main():
             ev[1].record()
         hp.select()
 
+    # Caches are flushed before every timed step: a 1 GiB buffer (four times the
+    # Infinity Cache) is read and written, so no step finds the last one's data in L2
+    # or the Infinity Cache.  Back-to-back ("warm") steps are timed after, for context.
+    flush_buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+
+    def timed_steps(cold):
+        ev_step = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+        ev_attn = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            if cold:
+                flush_buf.add_(1)
+            ev_step[i][0].record()
+            step(ev_attn[i])
+            ev_step[i][1].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / args.steps
+        step_ms = [a.elapsed_time(b_) for a, b_ in ev_step]
+        attn_ms_ = [a.elapsed_time(b_) for a, b_ in ev_attn]
+        return statistics.median(step_ms), statistics.median(attn_ms_), wall
+
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    attn_ms = sum(a.elapsed_time(b_) for a, b_ in evs) / args.steps
+    ms_per_step, attn_ms, wall_ms = timed_steps(cold=True)
+    warm_step_ms, warm_attn_ms, _ = timed_steps(cold=False)
+    del flush_buf
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (attn_ms * 1e-3) / 1e12
     prof = _counter_profile(args.workload)
 
     detail = {"attn_ms": round(attn_ms, 4), "nnz_pairs": nnz,
+              "timing": "median of the timed steps, caches flushed (1 GiB streamed) before "
+                        "each; warm = back to back",
+              "wall_ms_per_step_incl_flush": round(wall_ms, 4),
+              "warm_ms_per_step": round(warm_step_ms, 4), "warm_attn_ms": round(warm_attn_ms, 4),
               "selected_tflop": round(flops / 1e12, 4),
               "skipped_heads": int(hp.skipped.sum().item()),
               "skip_per_head": "".join(str(int(x)) for x in hp.skipped.cpu().tolist()),
@@ -524,10 +546,68 @@ def main():
             variants[name] = with_schedule(hpa, caq.WA_SCHED_XCD_SLICED)
         t = _time_interleaved(variants, rounds=5, reps=max(2, reps // 2))
         hp.schedule = main_sched
+
+        # End to end, reorder cost included: each chain (index, order, attention) timed
+        # as one unit, the chains taking turns, medians over the rounds.
+        def chain(path, order, sched):
+            def run():
+                path.build_index(w.mask)
+                order()
+                path.schedule = sched
+                path.attention(w.q, w.k, w.v)
+            return run
+        chains = {
+            "reordered": chain(hp, lambda: hp.reorder_rows(w.x0), main_sched),
+            "minhash": chain(hp_mh, minhash, caq.WA_SCHED_XCD_SLICED),
+            "lsh": chain(hp_lsh, lsh, caq.WA_SCHED_XCD_SLICED),
+            "unreordered_identity_xcd": chain(hp_id, lambda: None, caq.WA_SCHED_XCD_SLICED),
+            "unreordered_natural": chain(hp_id, lambda: None, caq.WA_SCHED_NATURAL),
+            "unreordered_heads_interleaved": chain(hp_id, lambda: None,
+                                                   caq.WA_SCHED_HEADS_INTERLEAVED),
+        }
+        te = _time_interleaved(chains, rounds=7, reps=max(2, reps // 2))
+        hp.schedule = main_sched
+        hp.reorder_rows(w.x0)
+        # Locality proxies of the orders on the host (WaveAlign §IV-B Problem (1) per
+        # wave, distinct K/V blocks per XCD wave, an LRU model of each XCD's L2).
+        from cache_aware_query_amd import locality
+        mask_h = w.mask.cpu().numpy()
+        ident = np.tile(np.arange(mb, dtype=np.int64), (H, 1))
+        lru_heads = range(min(H, 8))
+        orders = {"wavealign": hp.perm.cpu().numpy(), "identity": ident,
+                  "minhash": hp_mh.perm.cpu().numpy(), "lsh": hp_lsh.perm.cpu().numpy()}
+        detail["locality_proxies"] = {
+            name: {"wave_objective": locality.wave_objective(mask_h, pm, n_xcd, wave),
+                   "distinct_kv_per_wave": round(locality.distinct_kv_per_wave(
+                       mask_h, pm, n_xcd, wave), 1),
+                   "lru_l2_hit_model": round(locality.lru_l2_model(
+                       mask_h, pm, n_xcd, wave, 64, heads=lru_heads), 4)}
+            for name, pm in orders.items()}
+        detail["locality_proxies"]["lru_model_heads"] = len(lru_heads)
+        del mask_h
+        # Speedup gap (WaveAlign §III-A, Fig. 2): the ideal speedup 1/rho of the sparse
+        # kernel over the same kernel on an all-ones mask, against the measured one
+        # (both without G, the sparse one in its reordered order).
+        dense_pairs = H * mb * mb
+        if 4.0 * b * b * d * dense_pairs <= 150e12:
+            hp_dense = HotPath(H, L, d, b, dev, capacity=dense_pairs, reorder=None,
+                               schedule=caq.WA_SCHED_XCD_SLICED, gsrs_p=None)
+            hp_dense.build_index(torch.ones(H, mb, mb, dtype=torch.uint8, device=dev))
+            t_dense = _time_calls(lambda: hp_dense.attention(w.q, w.k, w.v), 2)
+            t_sparse = _time_calls(lambda: hp.attention_plain(w.q, w.k, w.v), reps)
+            rho = nnz / dense_pairs
+            s_act = t_dense / t_sparse
+            detail["speedup_gap"] = {"dense_attn_ms": round(t_dense, 3),
+                                     "sparse_attn_ms_no_g": round(t_sparse, 4),
+                                     "density": round(rho, 5),
+                                     "ideal_speedup": round(1.0 / rho, 3),
+                                     "actual_speedup": round(s_act, 3),
+                                     "gap": round((1.0 / rho) / s_act, 3)}
+            del hp_dense
         del hp_id, ablation
-        e2e_reord = t_index + t_reorder + t["reordered_auto"]
-        e2e_plain = t_index_id + min(t["identity_xcd"], t["natural_order"],
-                                     t["heads_interleaved"])
+        e2e_reord = te["reordered"]
+        best_plain = min((k for k in te if k.startswith("unreordered_")), key=lambda k: te[k])
+        e2e_plain = te[best_plain]
         detail.update({"index_ms": round(t_index, 4),
                        "reorder_ms": round(t_reorder, 4),
                        "gsrs_select_ms": round(t_select, 4),
@@ -535,13 +615,16 @@ def main():
         detail.update({f"attn_ms_{k}": round(v, 4) for k, v in t.items()})
         detail["minhash_order_ms"] = round(t_minhash, 4)
         detail["lsh_order_ms"] = round(t_lsh, 4)
-        detail["e2e_ms_lsh"] = round(t_index + t_lsh + t["lsh_order"], 4)
+        detail["e2e_ms_lsh"] = round(te["lsh"], 4)
         detail["explicit_permute_ms"] = round(t_perm, 4)
         detail["explicit_permute_gb_per_s"] = round(perm_bytes / (t_perm * 1e-3) / 1e9, 1)
-        detail["e2e_ms_minhash"] = round(t_index + t_minhash + t["minhash_order"], 4)
+        detail["e2e_ms_minhash"] = round(te["minhash"], 4)
         detail.update({"e2e_ms_reordered": round(e2e_reord, 4),
                        "e2e_ms_unreordered_best": round(e2e_plain, 4),
-                       "reorder_speedup_incl_overhead": round(e2e_plain / e2e_reord, 4)})
+                       "e2e_unreordered_best_is": best_plain,
+                       "e2e_ms_by_chain": {k: round(v, 4) for k, v in te.items()},
+                       "reorder_speedup_incl_overhead": round(e2e_plain / e2e_reord, 4),
+                       "host_skipped_reorder": bool(hp.host_skip)})
 
     line = {
         "metric": "selected-block attention TFLOP/s + HBM read GB + L2 hit %, "

@@ -226,9 +226,13 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
   const int Lp = MB * BLOCK;
   int h, pos;
-  if (schedule == WA_SCHED_AUTO)  // the choice of k_sched_select (XCD-sliced unless all-skipped)
+  if (schedule == WA_SCHED_AUTO) {
+    // the choice of k_sched_select: XCD-sliced unless every head kept its order, when
+    // the permutation is the identity and is not read
     schedule = sched_ws[0] == WA_SCHED_HEADS_INTERLEAVED ? WA_SCHED_HEADS_INTERLEAVED
                                                          : WA_SCHED_XCD_SLICED;
+    if (schedule == WA_SCHED_HEADS_INTERLEAVED) perm = nullptr;
+  }
   if (schedule == WA_SCHED_XCD_SLICED) {
     const int s = (MB + n_xcd - 1) / n_xcd;
     const int x = blockIdx.x % n_xcd;

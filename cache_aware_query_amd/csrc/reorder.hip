@@ -471,6 +471,35 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
   int32_t* inv_h = inv_perm + (size_t)h * MB;
   double* ang_h = angles ? angles + (size_t)h * MB : nullptr;
 
+  // ---- statistics and the skip decision (§IV-E) ----
+  // The size and work rules need only the head's NNZ: when they (or WA_SKIP_ALWAYS)
+  // decide, the head is skipped at once and the adjacent-row similarity, which the
+  // decision did not need, is reported as NaN.
+  const long long nnz = (long long)rp[MB] - (long long)rp[0];
+  const double ws = (double)NB * (double)block * (double)head_dim * 4.0;
+  const double flops = 4.0 * (double)block * (double)block * (double)head_dim * (double)nnz;
+  auto skip_head = [&](double jac_) {
+    if (stats != nullptr && t == 0) {
+      double* s_ = stats + (size_t)h * 5;
+      s_[0] = (double)nnz;
+      s_[1] = (double)nnz / ((double)MB * (double)NB);
+      s_[2] = ws;
+      s_[3] = flops;
+      s_[4] = jac_;
+    }
+    if (t == 0) skipped[h] = 1;
+    for (int u = t; u < MB; u += kThreads) {
+      perm_h[u] = u;
+      inv_h[u] = u;
+      if (ang_h) ang_h[u] = __longlong_as_double(0x7ff8000000000000ll);
+    }
+  };
+  if (p.skip_mode == WA_SKIP_ALWAYS ||
+      (p.skip_mode == WA_SKIP_ADAPTIVE && !(ws > p.ws_min && flops >= p.flops_min))) {
+    skip_head(__longlong_as_double(0x7ff8000000000000ll));
+    return;
+  }
+
   MaskBits bits{};
   // BITS: this thread's part of the sum over adjacent row pairs of |R_u & R_u+1|,
   // read off the column bitmasks as pairs of neighbouring set bits.
@@ -505,8 +534,6 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
     bits = MaskBits{cm, cc, MW};
   }
 
-  // ---- statistics and the skip decision (§IV-E) ----
-  const long long nnz = (long long)rp[MB] - (long long)rp[0];
   long long inter = 0, uni = 0;
   // Without the bitmasks of the BITS form, row bitmasks alone still fit in LDS for
   // moderate sizes (rowbits): built here from the lists, they only serve the pairs.
@@ -608,8 +635,10 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
   uni = block_sum_i64(uni, redi);
   const int glists = gather_lanes(nnz, max(MB, NB));
   const double jac = uni == 0 ? 1.0 : (double)inter / (double)uni;
-  const double ws = (double)NB * (double)block * (double)head_dim * 4.0;
-  const double flops = 4.0 * (double)block * (double)block * (double)head_dim * (double)nnz;
+  if (p.skip_mode == WA_SKIP_ADAPTIVE && !(jac < p.jac_max)) {
+    skip_head(jac);
+    return;
+  }
   if (stats != nullptr && t == 0) {
     double* s = stats + (size_t)h * 5;
     s[0] = (double)nnz;
@@ -618,23 +647,7 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
     s[3] = flops;
     s[4] = jac;
   }
-  bool skip;
-  if (p.skip_mode == WA_SKIP_ALWAYS) {
-    skip = true;
-  } else if (p.skip_mode == WA_SKIP_NEVER) {
-    skip = false;
-  } else {
-    skip = !(ws > p.ws_min && flops >= p.flops_min && jac < p.jac_max);
-  }
-  if (t == 0) skipped[h] = skip ? 1 : 0;
-  if (skip) {
-    for (int u = t; u < MB; u += kThreads) {
-      perm_h[u] = u;
-      inv_h[u] = u;
-      if (ang_h) ang_h[u] = __longlong_as_double(0x7ff8000000000000ll);
-    }
-    return;
-  }
+  if (t == 0) skipped[h] = 0;
 
   // ---- Stage 1: spectral polar order ----
   double2* X = lds;        // [MB]

@@ -21,8 +21,9 @@ import ctypes
 
 import torch
 
-from . import (WA_SCHED_AUTO, WA_SCHED_XCD_SLICED, BlockIndex, ReorderParams, _check, _ptr, _stream,
-               load_library, reorder_needs_csc, sparse_attn_workspace_size)
+from . import (WA_SCHED_AUTO, WA_SCHED_HEADS_INTERLEAVED, WA_SCHED_XCD_SLICED, WA_SKIP_ADAPTIVE,
+               BlockIndex, ReorderParams, _check, _ptr, _stream, load_library, reorder_needs_csc,
+               sparse_attn_workspace_size)
 
 
 class HotPath:
@@ -69,6 +70,29 @@ class HotPath:
         self.entropy = None   # [H, L_pad] row attention entropy, when diagnostics are on
         self.distance = None  # [H, L_pad] mean attention distance (tokens)
         self._params = (reorder or ReorderParams())._c()
+        self.host_skip = False
+        self._decide_on_host()
+
+    def _decide_on_host(self) -> None:
+        # The adaptive skip's size and work rules (WaveAlign §IV-E) bounded on the host:
+        # when even a full mask (MB x NB selected blocks, or the capacity if smaller)
+        # could not pass them, every head keeps its order whatever the mask, so the
+        # reorder is not launched and the attention runs the default path (what
+        # WA_SCHED_AUTO would choose), at no cost over not reordering.
+        r = self.reorder
+        self.host_skip = False
+        if r is None or r.skip_mode != WA_SKIP_ADAPTIVE:
+            return
+        ws = float(self.mb * self.b * self.d * 4)
+        pairs = min(self.mb * self.mb, self.cap)
+        fmax = 4.0 * self.b * self.b * self.d * pairs
+        if not (ws > r.ws_min_bytes and fmax >= r.flops_min):
+            self.host_skip = True
+            H, mb = self.H, self.mb
+            ident = torch.arange(mb, dtype=torch.int32, device=self.device).repeat(H, 1)
+            self.perm.copy_(ident)
+            self.inv_perm.copy_(ident)
+            self.skipped.fill_(1)
 
     def enable_diagnostics(self) -> None:
         """Every later attention pass also writes the row entropy and mean attention
@@ -83,6 +107,7 @@ class HotPath:
             raise ValueError("this path was built without reordering")
         self.reorder = reorder
         self._params = reorder._c()
+        self._decide_on_host()
 
     def index(self) -> BlockIndex:
         return BlockIndex(self.row_ptr, self.col_idx, self.row_nnz, self.csc_ptr, self.csc_idx,
@@ -98,6 +123,8 @@ class HotPath:
                "wa_build_block_index")
 
     def reorder_rows(self, x0: torch.Tensor) -> None:
+        if self.host_skip:
+            return
         lib, s = self.lib, _stream(self.device)
         _check(lib.wa_reorder_rows(_ptr(self.row_ptr), _ptr(self.col_idx), _ptr(self.csc_ptr),
                                    _ptr(self.csc_idx), self.cap, _ptr(x0), self.H, self.mb, self.mb,
@@ -112,11 +139,14 @@ class HotPath:
 
     def attention(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
         lib, s = self.lib, _stream(self.device)
-        perm = self.perm if self.reorder is not None else None
+        perm = self.perm if self.reorder is not None and not self.host_skip else None
+        schedule = self.schedule
+        if self.host_skip and schedule == WA_SCHED_AUTO:
+            schedule = WA_SCHED_HEADS_INTERLEAVED
         g = self.g if self.gsrs_p is not None else None
         slices = self.reorder.n_slices if perm is not None else 0
         args = (_ptr(q), _ptr(k), _ptr(v), self.H, self.L, self.d, self.b, _ptr(self.row_ptr),
-                _ptr(self.col_idx), self.cap, _ptr(perm), slices, self.schedule, self.d ** -0.5,
+                _ptr(self.col_idx), self.cap, _ptr(perm), slices, schedule, self.d ** -0.5,
                 _ptr(self.o), _ptr(self.lse), _ptr(g))
         if self.entropy is not None:
             _check(lib.wa_sparse_attn_fwd_diag(*args, _ptr(self.entropy), _ptr(self.distance),

@@ -147,7 +147,10 @@ typedef struct wa_reorder_params {
  *   angles    double [H][MB] out or NULL  polar angle per query block (NaN where
  *                                         Stage 1 did not run)
  *   stats     double [H][5] out or NULL  nnz, density, K/V bytes, selected FLOP,
- *                                        adjacent-row Jaccard
+ *                                        adjacent-row Jaccard (NaN when the skip was
+ *                                        decided without it: WA_SKIP_ALWAYS, or the
+ *                                        adaptive rule failing on bytes or FLOP, which
+ *                                        skips the head before its mask is read)
  *   params    host pointer
  * Errors: WA_ERR_INVALID_ARG (null pointer, bad params, CSC missing where it is
  * required), WA_ERR_UNSUPPORTED (MB or NB > WA_MAX_BLOCKS, head_dim/block < 1),

@@ -305,3 +305,27 @@ def test_row_longer_than_the_staged_list():
     lse_ref[0, u_long * b:(u_long + 1) * b] += np.log(reps)
     assert_attention_close(np64(o)[:, :L], lse.cpu().numpy().astype(np.float64)[:, :L],
                            o_ref[:, :L], lse_ref[:, :L], "row of 2,100 entries")
+
+
+def test_host_skipped_path_runs_the_default_path():
+    """A HotPath whose shape cannot pass the adaptive skip's work rule launches no
+    reorder and runs the all-heads-at-once default path: bitwise the plain call."""
+    from cache_aware_query_amd.pipeline import HotPath
+
+    dev = gpu()
+    w = synth.make_workload("layer16k", device="cuda", heads=4)
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    nnz = int(w.mask.sum())
+    banner("host-skipped HotPath layer16k heads=4")
+    params = caq.ReorderParams(wave=64, n_slices=caq.schedule_info(0, 128)[0],
+                               skip_mode=caq.WA_SKIP_ADAPTIVE, flops_min=2.2e11)
+    hp = HotPath(H, w.seq_len, w.head_dim, w.block, dev, capacity=nnz, reorder=params,
+                 schedule=caq.WA_SCHED_AUTO, gsrs_p=None)
+    assert hp.host_skip
+    hp.build_index(w.mask)
+    hp.reorder_rows(w.x0)
+    hp.attention(w.q, w.k, w.v)
+    o, lse, _ = caq.sparse_attn_fwd(w.q, w.k, w.v, w.seq_len, w.block, hp.row_ptr, hp.col_idx,
+                                    schedule=caq.WA_SCHED_HEADS_INTERLEAVED)
+    torch.cuda.synchronize()
+    assert torch.equal(hp.o, o) and torch.equal(hp.lse, lse)

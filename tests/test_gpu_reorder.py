@@ -76,6 +76,12 @@ CASES = [
     ("hunyuan119k", {"heads": 3}, caq.ReorderParams(wave=64, n_slices=8,
                                                     skip_mode=caq.WA_SKIP_ADAPTIVE,
                                                     flops_min=1e10, jaccard_max=0.9)),
+    # skips decided before the mask is read (Jaccard reported as NaN): every head, and
+    # a work threshold between the heads' selected FLOP
+    ("layer16k", {}, caq.ReorderParams(wave=64, n_slices=8, skip_mode=caq.WA_SKIP_ALWAYS)),
+    ("hunyuan119k", {"heads": 6}, caq.ReorderParams(wave=64, n_slices=8,
+                                                    skip_mode=caq.WA_SKIP_ADAPTIVE,
+                                                    flops_min=2.5e10, jaccard_max=0.9)),
 ]
 
 
@@ -127,7 +133,17 @@ def _compare_with_oracle(w, params):
     perm_o, _, skip_o, ang_o, st_o = oracle.reorder_rows(m, x0.numpy().astype(np.float64),
                                                          w.block, w.head_dim,
                                                          _oracle_params(params))
-    np.testing.assert_array_equal(st_g, st_o)
+    # nnz, density, K/V bytes and FLOP bit-exact; the adjacent-row Jaccard too, except
+    # where the skip was decided without it (WA_SKIP_ALWAYS, or the size/work rule of
+    # the adaptive skip), where the library reports NaN
+    np.testing.assert_array_equal(st_g[:, :4], st_o[:, :4])
+    op = _oracle_params(params)
+    early = np.array([op.skip_mode == oracle.reorder.SKIP_ALWAYS or
+                      (op.skip_mode == oracle.reorder.SKIP_ADAPTIVE and
+                       not (st_o[h, 2] > op.ws_min_bytes and st_o[h, 3] >= op.flops_min))
+                      for h in range(st_o.shape[0])])
+    np.testing.assert_array_equal(np.isnan(st_g[:, 4]), early)
+    np.testing.assert_array_equal(st_g[~early, 4], st_o[~early, 4])
     np.testing.assert_array_equal(skip_g, skip_o)
     H, mb = perm_g.shape
     for h in range(H):
