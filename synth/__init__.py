@@ -18,4 +18,4 @@ from .workloads import (  # noqa: F401
     random_tiny_case,
     wide_range_case,
 )
-from .hilbert import gilbert2d, video_hilbert_order  # noqa: F401
+from .hilbert import gilbert2d, gilbert3d, video_hilbert_order  # noqa: F401

@@ -3,13 +3,18 @@
 The GSRS page ("Sparse Attention for Video Generation Acceleration via Growing
 Sparsity and Reduced Search", token reordering paragraph) flattens the (t, y, x)
 latent grid along a generalized Hilbert curve before blocking, so that each
-fixed-size token block holds spatially adjacent tokens.  The page names the
-curve by citation only.  The reading taken here: inside every frame the tokens
-follow a generalized Hilbert curve over the (y, x) rectangle, written below from
-the published recursive construction for arbitrary rectangles (split the long
-side in two when the rectangle is elongated, otherwise lay out the three legs of
-a Hilbert "U"); consecutive frames run the curve forwards and backwards in
-turn, so the step from one frame to the next is a unit step in t.
+fixed-size token block holds tokens that are close in space and time.  The page
+names the curve by citation only.  The construction restated here is the
+recursive generalized Hilbert curve for rectangles of arbitrary size published
+by Jakub Cerveny ("gilbert", the generalized Hilbert space-filling curve), in
+its three-dimensional form: a box is walked from its origin corner to the far
+end of its travel axis; a box much longer along the travel axis than across is
+cut into two halves along it; otherwise it is cut into the three legs of a
+Hilbert "U" in the plane of the travel axis and the longer of the other two
+axes (up the first half, across, back down), the third axis carried through
+every leg; halves are kept even where possible so that the legs join with unit
+steps.  The code below is this package's own (an explicit stack, cuboids
+throughout); the 2-D curve is the same construction on a box one cell deep.
 """
 
 from __future__ import annotations
@@ -26,72 +31,89 @@ def _half(v: int) -> int:
     return v // 2 if v >= 0 else -((-v) // 2)
 
 
-def gilbert2d(width: int, height: int) -> list[tuple[int, int]]:
-    """All cells (x, y) of a width x height rectangle, in curve order.
+def _length(v) -> int:
+    return abs(v[0]) + abs(v[1]) + abs(v[2])
 
-    Every cell appears once.  Consecutive cells are 4-neighbours except for at
-    most a few diagonal steps that odd side lengths force.
+
+def _unit(v):
+    return (_sign(v[0]), _sign(v[1]), _sign(v[2]))
+
+
+def _add(p, *vs):
+    return tuple(p[i] + sum(v[i] for v in vs) for i in range(3))
+
+
+def _scale(v, k: int):
+    return (v[0] * k, v[1] * k, v[2] * k)
+
+
+def _halve(v, even: bool):
+    """Half of the axis vector v (toward zero), made even when ``even`` and possible."""
+    h = (_half(v[0]), _half(v[1]), _half(v[2]))
+    if even and _length(h) % 2 == 1 and _length(v) > 2:
+        h = _add(h, _unit(v))
+    return h
+
+
+def gilbert3d(width: int, height: int, depth: int) -> list[tuple[int, int, int]]:
+    """All cells (x, y, z) of a width x height x depth box, in curve order.
+
+    Every cell appears once; consecutive cells are face neighbours except for a
+    few steps that odd side lengths force (checked by the tests).
     """
-    if width <= 0 or height <= 0:
+    if width <= 0 or height <= 0 or depth <= 0:
         return []
-    cells: list[tuple[int, int]] = []
-    # A region is (x, y, ax, ay, bx, by): start corner, major axis vector a
-    # (walked first) and minor axis vector b; exactly one component of each
-    # vector is non-zero.  Regions are processed depth-first, in order.
-    if width >= height:
-        stack = [(0, 0, width, 0, 0, height)]
-    else:
-        stack = [(0, 0, 0, height, width, 0)]
+    # A region is (origin, a, b, c): the curve enters at the origin corner and leaves
+    # at origin + (|a| - 1) * unit(a); a is the travel axis, b and c span the rest.
+    # Each axis vector has exactly one non-zero component.
+    axes = sorted([((width, 0, 0), width), ((0, height, 0), height), ((0, 0, depth), depth)],
+                  key=lambda t: -t[1])
+    stack = [((0, 0, 0), axes[0][0], axes[1][0], axes[2][0])]
+    cells: list[tuple[int, int, int]] = []
     while stack:
-        x, y, ax, ay, bx, by = stack.pop()
-        la = abs(ax + ay)
-        lb = abs(bx + by)
-        ux, uy = _sign(ax), _sign(ay)
-        vx, vy = _sign(bx), _sign(by)
-        if lb == 1:  # a single line along the major axis
-            for i in range(la):
-                cells.append((x + i * ux, y + i * uy))
+        o, a, b, c = stack.pop()
+        la, lb, lc = _length(a), _length(b), _length(c)
+        ua = _unit(a)
+        if lb == 1 and lc == 1:  # a line along the travel axis
+            cells.extend(_add(o, _scale(ua, i)) for i in range(la))
             continue
-        if la == 1:  # a single line along the minor axis
-            for i in range(lb):
-                cells.append((x + i * vx, y + i * vy))
+        if la == 1:  # a single slab across the travel axis: walk it as a 2-D box
+            if lb >= lc:
+                stack.append((o, b, c, a))
+            else:
+                stack.append((o, c, b, a))
             continue
-        hax, hay = _half(ax), _half(ay)
-        hbx, hby = _half(bx), _half(by)
-        if 2 * la > 3 * lb:
-            # Elongated: two halves side by side along the major axis.  Keep the
-            # first half even so that the curve can return to its side.
-            if abs(hax + hay) % 2 == 1 and la > 2:
-                hax, hay = hax + ux, hay + uy
-            parts = [
-                (x, y, hax, hay, bx, by),
-                (x + hax, y + hay, ax - hax, ay - hay, bx, by),
-            ]
+        if 2 * la > 3 * lb and 2 * la > 3 * lc:
+            # elongated along the travel axis: two halves one after the other
+            a1 = _halve(a, even=True)
+            a2 = _add(a, _scale(a1, -1))
+            parts = [(o, a1, b, c), (_add(o, a1), a2, b, c)]
         else:
-            # Hilbert "U": up the first half of the minor axis, across the full
-            # major axis, back down the other side.
-            if abs(hbx + hby) % 2 == 1 and lb > 2:
-                hbx, hby = hbx + vx, hby + vy
+            # Hilbert "U" in the plane of a and the longer of b and c (m); the other
+            # axis (n) is carried through every leg
+            m, n = (b, c) if lb >= lc else (c, b)
+            m1 = _halve(m, even=True)
+            m2 = _add(m, _scale(m1, -1))
+            a1 = _halve(a, even=False)
+            a2 = _add(a, _scale(a1, -1))
+            um = _unit(m)
             parts = [
-                (x, y, hbx, hby, hax, hay),
-                (x + hbx, y + hby, ax, ay, bx - hbx, by - hby),
-                (x + (ax - ux) + (hbx - vx), y + (ay - uy) + (hby - vy),
-                 -hbx, -hby, -(ax - hax), -(ay - hay)),
+                (o, m1, a1, n),                         # up the first half of m
+                (_add(o, m1), a, m2, n),                # across the far half of m
+                (_add(o, a, _scale(ua, -1), m1, _scale(um, -1)),
+                 _scale(m1, -1), _scale(a2, -1), n),    # back down to the end of a
             ]
         stack.extend(reversed(parts))
     return cells
 
 
-def video_hilbert_order(frames: int, height: int, width: int) -> np.ndarray:
-    """Permutation of row-major (t, y, x) token ids along the frame-wise curve.
+def gilbert2d(width: int, height: int) -> list[tuple[int, int]]:
+    """All cells (x, y) of a width x height rectangle, in curve order."""
+    return [(x, y) for (x, y, _) in gilbert3d(width, height, 1)]
 
-    ``order[n]`` is the row-major id of the n-th token on the curve.
-    """
-    plane = gilbert2d(width, height)
-    ids = np.array([y * width + x for (x, y) in plane], dtype=np.int64)
-    out = np.empty(frames * height * width, dtype=np.int64)
-    per = height * width
-    for t in range(frames):
-        seq = ids if t % 2 == 0 else ids[::-1]
-        out[t * per:(t + 1) * per] = t * per + seq
-    return out
+
+def video_hilbert_order(frames: int, height: int, width: int) -> np.ndarray:
+    """Permutation of row-major (t, y, x) token ids along the curve over the whole
+    (t, y, x) box.  ``order[n]`` is the row-major id of the n-th token on the curve."""
+    cells = gilbert3d(width, height, frames)
+    return np.array([(t * height + y) * width + x for (x, y, t) in cells], dtype=np.int64)

@@ -22,7 +22,7 @@ Seven workloads are defined (``CONFIGS``):
                  pooled block scores with k drawn from 5%..25% of the blocks, plus
                  the diagonal.
 ``hunyuan119k``  24 heads, d=128, grid 33x45x80 (L=118,800), block 128, tokens
-                 in frame-wise generalized-Hilbert order.  Mask: per-row Top-p
+                 along a generalized Hilbert curve over (t, y, x).  Mask: per-row Top-p
                  (0.9) over the softmax of pooled block scores.
 ``gsrs75k``      The ``wan75k`` tensors with an all-ones mask (the first, dense
                  search pass of the GSRS pipeline).

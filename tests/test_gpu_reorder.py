@@ -81,7 +81,7 @@ CASES = [
     ("layer16k", {}, caq.ReorderParams(wave=64, n_slices=8, skip_mode=caq.WA_SKIP_ALWAYS)),
     ("hunyuan119k", {"heads": 6}, caq.ReorderParams(wave=64, n_slices=8,
                                                     skip_mode=caq.WA_SKIP_ADAPTIVE,
-                                                    flops_min=2.5e10, jaccard_max=0.9)),
+                                                    flops_min=1.45e10, jaccard_max=0.9)),
 ]
 
 

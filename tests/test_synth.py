@@ -44,14 +44,36 @@ def test_wan_shape_padding_and_topk():
 
 
 def test_video_hilbert_order_is_a_local_bijection():
+    """The curve runs over the whole (t, y, x) box: a bijection whose steps join face
+    neighbours almost everywhere (odd side lengths force a few diagonal steps of two
+    cells), and whose 128-token blocks are compact in all three axes, not planar."""
     o = synth.video_hilbert_order(33, 45, 80)
     assert np.array_equal(np.sort(o), np.arange(33 * 45 * 80))
     t, y, x = o // 3600, (o % 3600) // 80, o % 80
-    step = np.abs(np.diff(t)) + np.abs(np.diff(y)) + np.abs(np.diff(x))
-    assert (step == 1).mean() >= 0.95
+    dt, dy, dx = np.abs(np.diff(t)), np.abs(np.diff(y)), np.abs(np.diff(x))
+    step = dt + dy + dx
+    assert step.max() <= 2 and max(dt.max(), dy.max(), dx.max()) <= 2
+    assert (step == 1).mean() >= 0.9
+    assert o[0] == 0                        # the curve enters at the origin corner
+    ext = np.array([[np.ptp(a[i:i + 128]) + 1 for a in (t, y, x)]
+                    for i in range(0, o.size - 127, 128)])
+    assert ext[:, 0].mean() > 3             # blocks span several frames ...
+    assert ext.max() <= 16                  # ... and stay compact in space and time
+    for dims in ((80, 45, 33), (7, 5, 3), (1, 9, 4), (12, 1, 1), (2, 2, 2), (16, 16, 16)):
+        cells = synth.gilbert3d(*dims)
+        assert len(set(cells)) == len(cells) == dims[0] * dims[1] * dims[2]
+        assert all(0 <= c[i] < dims[i] for c in cells for i in range(3))
+    # power-of-two cubes and flat boxes: every step is a unit step, as in Hilbert's curve
+    for dims in ((8, 8, 8), (80, 45, 1), (2, 2, 1), (4, 4, 4)):
+        c = np.array(synth.gilbert3d(*dims))
+        if dims == (8, 8, 8) or dims == (4, 4, 4):
+            assert np.abs(np.diff(c, axis=0)).sum(1).max() <= 2
+        else:
+            assert np.all(np.abs(np.diff(c, axis=0)).sum(1) == 1)
     for w_, h_ in ((80, 45), (7, 5), (1, 9), (12, 1)):
         cells = synth.gilbert2d(w_, h_)
         assert len(set(cells)) == w_ * h_
+        assert np.all(np.abs(np.diff(np.array(cells), axis=0)).sum(1) == 1)
 
 
 def test_random_tiny_case():
