@@ -11,9 +11,11 @@ L=75,600 tokens, block 128, per-head Top-k masks of pooled block scores):
 Inputs are synthetic (seeded), resident in HBM before timing.  The reported
 value is selected-block attention TFLOP/s of the whole step (4*b*b*d FLOP per
 selected block pair over the step time).  The roofline object reports the
-attention launch alone (HIP events on the launch stream) against the dense bf16
-MFMA peak; the CPU baseline is the fp64 oracle timed on a bounded sample of the
-same workload.
+attention launch alone (HIP events on the launch stream) against the roof its
+operational intensity puts it under: the dense bf16 MFMA peak when its FLOP per
+compulsory HBM byte exceed the ridge (312.5), else HBM bandwidth (8 TB/s) with
+compulsory bytes per second; the CPU baseline is the fp64 oracle timed on a
+bounded sample of the same workload.
 
 With ``--workload gsrs75k`` one step is the GSRS search step instead: a full
 pass with block LSE, block importance and Top-p(0.9) candidates, the reordered
@@ -42,6 +44,37 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e3 / PEAK_HBM_GBS  # 312.5
+
+
+def _attn_compulsory_bytes(H: int, lp: int, d: int, b: int, nnz: int, with_g: bool) -> float:
+    """Algorithmic HBM bytes of one attention launch: Q, K and V read and O written once
+    (4 * H * L_pad * d bf16), the row LSE (fp32), the block LSE G (nnz * b fp32) when it is
+    emitted, and the CSR (row_ptr and col_idx, int32)."""
+    return (4.0 * H * lp * d * 2 + 4.0 * H * lp + (4.0 * nnz * b if with_g else 0.0)
+            + 4.0 * (H * (lp // b) + 1) + 4.0 * nnz)
+
+
+def _roofline(flops: float, alg_bytes: float, attn_ms: float, traffic) -> dict:
+    """The roofline of the attention launch: its operational intensity (FLOP over
+    compulsory bytes) decides the roof.  Above the ridge (312.5 FLOP/B) the bound is the
+    bf16 MFMA peak and ``achieved`` counts selected-block FLOP per second; below it, HBM
+    bandwidth, and ``achieved`` counts compulsory bytes per second.  ``other`` gives the
+    fraction of the other roof for reference."""
+    s = attn_ms * 1e-3
+    tflops = flops / s / 1e12
+    gbs = alg_bytes / s / 1e9
+    intensity = flops / alg_bytes
+    mfma = {"achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    hbm = {"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+           "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    main, other, bound = (mfma, hbm, "mfma") if intensity >= RIDGE_FLOP_PER_BYTE else (hbm, mfma, "hbm")
+    return {"bound": bound, **main, "traffic": traffic,
+            "intensity_flop_per_byte": round(intensity, 1),
+            "compulsory_bytes": round(alg_bytes), "other": {"bound": "hbm" if bound == "mfma"
+                                                             else "mfma", **other}}
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "cache_aware_query_amd", "csrc", "attention.hip")
 
@@ -176,7 +209,6 @@ def gsrs_main(args, w, params):
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     dense_ms = sum(a.elapsed_time(b_) for a, b_ in evs) / args.steps
     value = sum(flops) / (ms_per_step * 1e-3) / 1e12
-    achieved = flops[0] / (dense_ms * 1e-3) / 1e12
     subset_violations = int((gs.mask2.to(torch.int16) > gs.mask1.to(torch.int16)).sum().item())
     reps = max(3, args.steps // 2)
     detail = {"pairs_full_pass": pairs[0], "pairs_s1_p0.9": pairs[1], "pairs_s2_p0.8": pairs[2],
@@ -201,9 +233,8 @@ def gsrs_main(args, w, params):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "heads": H, "seq_len": L, "head_dim": d,
                    "block": b, "p1": 0.9, "p2": 0.8},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+        "roofline": _roofline(flops[0], _attn_compulsory_bytes(H, mb * b, d, b, pairs[0], True),
+                              dense_ms, None),
         "detail": detail,
     }
     print(json.dumps(line), flush=True)
@@ -319,6 +350,39 @@ def gsrs_schedule_main(args, w, params):
     print(json.dumps(line), flush=True)
 
 
+def _skip_report(hp, w, params) -> dict:
+    """Per-head skip decision and the statistic that took it (outside the timed region).
+
+    The rule is run once more on the device with every head's statistics reported,
+    whatever the host-side bound decided: s = size (K/V bytes), w = work (selected
+    FLOP), j = similarity (adjacent-row Jaccard), r = reordered."""
+    import numpy as np
+
+    import cache_aware_query_amd as caq
+
+    ro = caq.reorder_rows(hp.index(), w.x0, w.block, w.head_dim, params)
+    st = ro.stats.cpu().double().numpy()
+    skipped = ro.skipped.cpu().numpy().astype(bool)
+    by = []
+    for h in range(st.shape[0]):
+        if not st[h, 2] > params.ws_min_bytes:
+            by.append("s")
+        elif not st[h, 3] >= params.flops_min:
+            by.append("w")
+        elif not st[h, 4] < params.jaccard_max:
+            by.append("j")
+        else:
+            by.append("r")
+        assert (by[-1] != "r") == skipped[h]
+    return {"thresholds": {"ws_min_bytes": params.ws_min_bytes, "flops_min": params.flops_min,
+                           "jaccard_max": params.jaccard_max},
+            "decided_by": "".join(by),
+            "legend": "s size, w work, j similarity, r reordered",
+            "per_head_gflop": [round(float(x) / 1e9, 2) for x in st[:, 3]],
+            "per_head_jaccard": [None if np.isnan(x) else round(float(x), 4) for x in st[:, 4]],
+            "host_bound_skipped_all": bool(hp.host_skip)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -372,8 +436,9 @@ def main():
     if args.workload == "gsrs75k":
         return gsrs_main(args, w, params)
     # With the adaptive skip the attention follows the skip flags on the device: the
-    # default (all heads at once) path when every head kept its order, XCD-sliced
-    # otherwise.  A forced skip rule keeps the XCD-sliced schedule, so that "always"
+    # default path (WA_SCHED_DEFAULT: all heads at once for small heads, else
+    # XCD-sliced in the original order) when every head kept its order, XCD-sliced in
+    # the reordered order otherwise.  A forced skip rule keeps the XCD-sliced schedule, so that "always"
     # measures the identity order under the same schedule as the reordered one.
     main_sched = caq.WA_SCHED_AUTO if args.skip == "adaptive" else caq.WA_SCHED_XCD_SLICED
     hp = HotPath(H, L, d, b, dev, capacity=nnz, reorder=params, schedule=main_sched, gsrs_p=0.9)
@@ -430,7 +495,6 @@ def main():
     warm_step_ms, warm_attn_ms, _ = timed_steps(cold=False)
     del flush_buf
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (attn_ms * 1e-3) / 1e12
     prof = _counter_profile(args.workload)
 
     detail = {"attn_ms": round(attn_ms, 4), "nnz_pairs": nnz,
@@ -446,6 +510,8 @@ def main():
               "hbm_read_gb_per_launch": (round(prof["hbm_read_bytes_per_launch"] / 1e9, 3)
                                          if "hbm_read_bytes_per_launch" in prof else None),
               "l2_hit_pct": prof.get("l2_hit_pct")}
+    if params.skip_mode == caq.WA_SKIP_ADAPTIVE:
+        detail["skip_decisions"] = _skip_report(hp, w, params)
     if not args.no_variants:
         reps = max(3, args.steps // 2)
         # Stage times of the reordered step.
@@ -662,9 +728,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "heads": H, "seq_len": L, "head_dim": d,
                    "block": b, "density": round(nnz / (H * mb * mb), 5)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": prof.get("hbm_bytes_per_launch")},
+        "roofline": _roofline(flops, _attn_compulsory_bytes(H, hp.lp, d, b, nnz, True), attn_ms,
+                              prof.get("hbm_bytes_per_launch")),
         "detail": detail,
     }
     if not args.no_cpu_baseline:

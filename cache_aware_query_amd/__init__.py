@@ -25,6 +25,7 @@ WA_SCHED_NATURAL = 0
 WA_SCHED_XCD_SLICED = 1
 WA_SCHED_HEADS_INTERLEAVED = 2
 WA_SCHED_AUTO = 3
+WA_SCHED_DEFAULT = 4
 WA_SKIP_ADAPTIVE = 0
 WA_SKIP_NEVER = 1
 WA_SKIP_ALWAYS = 2
@@ -35,6 +36,7 @@ EXPORTED = (
     "wa_sparse_attn_fwd", "wa_sparse_attn_fwd_diag", "wa_attn_schedule_select",
     "wa_block_importance", "wa_topp_select", "wa_mask_recall", "wa_gather_blocks",
     "wa_scatter_blocks", "wa_xcd_placement", "wa_sparse_attn_fwd_noalloc", "wa_lsh_order",
+    "wa_default_schedule",
 )
 
 
@@ -118,6 +120,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "wa_sparse_attn_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32,
                                                          ctypes.POINTER(ctypes.c_size_t)]),
         "wa_attn_schedule_select": (ctypes.c_int, [_P, _I32, _P, ctypes.c_size_t, _P]),
+        "wa_default_schedule": (ctypes.c_int, [_I32, _I32, _I32, _P]),
         "wa_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _I64, _P,
                                               _I32, _I32, ctypes.c_float, _P, _P, _P, _P,
                                               ctypes.c_size_t, _P]),
@@ -315,10 +318,21 @@ def sparse_attn_workspace_size(heads: int, seq_len: int, head_dim: int, block: i
     return n.value
 
 
+def default_schedule(seq_len: int, head_dim: int, block: int) -> int:
+    """The schedule WA_SCHED_DEFAULT runs for these sizes (wa_default_schedule): all
+    heads at once for small heads, XCD-sliced in the original order otherwise."""
+    lib = load_library()
+    out = ctypes.c_int32()
+    _check(lib.wa_default_schedule(seq_len, head_dim, block, ctypes.byref(out)),
+           "wa_default_schedule")
+    return int(out.value)
+
+
 def attn_schedule_select(skipped: torch.Tensor, workspace: torch.Tensor) -> None:
     """Write the WA_SCHED_AUTO choice for these skip flags into ``workspace``
-    (wa_attn_schedule_select): all heads at once if every head was skipped, else
-    XCD-sliced.  Pass the same workspace to sparse_attn_fwd(schedule=WA_SCHED_AUTO)."""
+    (wa_attn_schedule_select): the default path (WA_SCHED_DEFAULT) if every head was
+    skipped, else XCD-sliced.  Pass the same workspace to
+    sparse_attn_fwd(schedule=WA_SCHED_AUTO)."""
     lib = load_library()
     _need(skipped, torch.uint8, "skipped", 1)
     _need(workspace, torch.uint8, "workspace", 1)

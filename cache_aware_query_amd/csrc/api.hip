@@ -48,7 +48,7 @@ hipError_t stream_xcds(hipStream_t stream, int* n_xcd) {
 
 extern "C" {
 
-int wa_abi_version(void) { return 3; }
+int wa_abi_version(void) { return 4; }
 
 const char* wa_last_error(void) { return g_err; }
 
@@ -197,7 +197,8 @@ static int sparse_attn_check(const wa_bf16* q, const wa_bf16* k, const wa_bf16* 
     return fail(WA_ERR_UNSUPPORTED, "head_dim %d / block %d not in {64, 128}", head_dim, block);
   if (capacity < 0) return fail(WA_ERR_INVALID_ARG, "negative capacity");
   if (schedule != WA_SCHED_NATURAL && schedule != WA_SCHED_XCD_SLICED &&
-      schedule != WA_SCHED_HEADS_INTERLEAVED && schedule != WA_SCHED_AUTO)
+      schedule != WA_SCHED_HEADS_INTERLEAVED && schedule != WA_SCHED_AUTO &&
+      schedule != WA_SCHED_DEFAULT)
     return fail(WA_ERR_INVALID_ARG, "unknown schedule %d", schedule);
   if (!(scale > 0.0f) || !(scale < 1e30f)) return fail(WA_ERR_INVALID_ARG, "scale must be > 0");
   const int64_t MB = ((int64_t)L + block - 1) / block;
@@ -294,6 +295,15 @@ int wa_xcd_placement(int32_t n_wg, int32_t block, int32_t* xcd_out, void* stream
   if (block != 64 && block != 128) return fail(WA_ERR_UNSUPPORTED, "block %d not in {64, 128}", block);
   return hip_status(wa::launch_xcd_placement(n_wg, block, xcd_out, static_cast<hipStream_t>(stream)),
                     "wa_xcd_placement");
+}
+
+int wa_default_schedule(int32_t L, int32_t head_dim, int32_t block, int32_t* schedule) {
+  if (!schedule) return fail(WA_ERR_INVALID_ARG, "null pointer argument");
+  if (L < 1) return fail(WA_ERR_INVALID_ARG, "L must be >= 1");
+  if (!supported_shape(head_dim, block))
+    return fail(WA_ERR_UNSUPPORTED, "head_dim %d / block %d not in {64, 128}", head_dim, block);
+  *schedule = wa::default_schedule((int)(((int64_t)L + block - 1) / block), block, head_dim);
+  return ok();
 }
 
 int wa_attn_schedule_select(const uint8_t* skipped, int32_t H, void* workspace,

@@ -227,11 +227,14 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int Lp = MB * BLOCK;
   int h, pos;
   if (schedule == WA_SCHED_AUTO) {
-    // the choice of k_sched_select: XCD-sliced unless every head kept its order, when
-    // the permutation is the identity and is not read
-    schedule = sched_ws[0] == WA_SCHED_HEADS_INTERLEAVED ? WA_SCHED_HEADS_INTERLEAVED
-                                                         : WA_SCHED_XCD_SLICED;
-    if (schedule == WA_SCHED_HEADS_INTERLEAVED) perm = nullptr;
+    // the choice of k_sched_select: XCD-sliced in the reordered order, or the default
+    // path when every head kept its order (the permutation is the identity, not read)
+    if (sched_ws[0] == WA_SCHED_DEFAULT) {
+      schedule = default_schedule(MB, BLOCK, D);
+      perm = nullptr;
+    } else {
+      schedule = WA_SCHED_XCD_SLICED;
+    }
   }
   if (schedule == WA_SCHED_XCD_SLICED) {
     const int s = (MB + n_xcd - 1) / n_xcd;
@@ -694,6 +697,10 @@ hipError_t launch_typed(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         float* lse, float* g, float* ent, float* dist, const int* sched_ws,
                         hipStream_t s) {
   const int MB = (L + BLOCK - 1) / BLOCK;
+  if (schedule == WA_SCHED_DEFAULT) {  // known from the sizes: resolved here
+    schedule = default_schedule(MB, BLOCK, D);
+    perm = nullptr;
+  }
   int grid = H * MB;
   if (schedule == WA_SCHED_XCD_SLICED || schedule == WA_SCHED_AUTO)
     grid = H * n_xcd * ((MB + n_xcd - 1) / n_xcd);  // >= H * MB, the other schedules' grid
@@ -728,14 +735,14 @@ size_t attn_workspace_bytes(int H, int L_pad, int head_dim) {
 }
 
 namespace {
-// One wavefront: WA_SCHED_HEADS_INTERLEAVED if every head was skipped, else
+// One wavefront: WA_SCHED_DEFAULT if every head was skipped, else
 // WA_SCHED_XCD_SLICED, into out[0].
 __global__ __launch_bounds__(64) void k_sched_select(const uint8_t* __restrict__ skipped, int H,
                                                      int* __restrict__ out) {
   bool all = true;
   for (int i = threadIdx.x; i < H; i += 64) all = all && skipped[i] != 0;
   const bool some_reordered = __builtin_amdgcn_ballot_w64(!all) != 0;
-  if (threadIdx.x == 0) out[0] = some_reordered ? WA_SCHED_XCD_SLICED : WA_SCHED_HEADS_INTERLEAVED;
+  if (threadIdx.x == 0) out[0] = some_reordered ? WA_SCHED_XCD_SLICED : WA_SCHED_DEFAULT;
 }
 }  // namespace
 

@@ -51,6 +51,13 @@ hipError_t launch_xcd_placement(int n_wg, int block, int32_t* out, hipStream_t s
 
 // The static device scratch of wa_sparse_attn_fwd_noalloc: its size, and the device
 // address of device `dev`'s copy (looked up once per device).
+// The schedule WA_SCHED_DEFAULT resolves to for heads that keep their original order.
+__host__ __device__ inline int default_schedule(int MB, int block, int head_dim) {
+  return (unsigned long long)MB * block * head_dim * 4 <= WA_ALL_HEADS_MAX_KV_BYTES
+             ? WA_SCHED_HEADS_INTERLEAVED
+             : WA_SCHED_XCD_SLICED;
+}
+
 constexpr size_t kStaticScratchBytes = 256;
 constexpr int kMaxDevices = 64;
 hipError_t static_scratch(int dev, void** out);

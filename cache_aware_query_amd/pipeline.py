@@ -21,7 +21,7 @@ import ctypes
 
 import torch
 
-from . import (WA_SCHED_AUTO, WA_SCHED_HEADS_INTERLEAVED, WA_SCHED_XCD_SLICED, WA_SKIP_ADAPTIVE,
+from . import (WA_SCHED_AUTO, WA_SCHED_DEFAULT, WA_SCHED_XCD_SLICED, WA_SKIP_ADAPTIVE,
                BlockIndex, ReorderParams, _check, _ptr, _stream, load_library, reorder_needs_csc,
                sparse_attn_workspace_size)
 
@@ -77,8 +77,9 @@ class HotPath:
         # The adaptive skip's size and work rules (WaveAlign §IV-E) bounded on the host:
         # when even a full mask (MB x NB selected blocks, or the capacity if smaller)
         # could not pass them, every head keeps its order whatever the mask, so the
-        # reorder is not launched and the attention runs the default path (what
-        # WA_SCHED_AUTO would choose), at no cost over not reordering.
+        # reorder is not launched and the attention runs the default path
+        # (WA_SCHED_DEFAULT, what WA_SCHED_AUTO would choose), at no cost over not
+        # reordering.
         r = self.reorder
         self.host_skip = False
         if r is None or r.skip_mode != WA_SKIP_ADAPTIVE:
@@ -132,8 +133,8 @@ class HotPath:
                                    _ptr(self.inv_perm), _ptr(self.skipped), _ptr(self.angles),
                                    _ptr(self.stats), s), "wa_reorder_rows")
         if self.schedule == WA_SCHED_AUTO:
-            # all heads skipped: the attention falls back to the default (all heads at
-            # once) path, chosen on the device (WaveAlign §VI-F)
+            # all heads skipped: the attention falls back to the default path
+            # (WA_SCHED_DEFAULT), chosen on the device (WaveAlign §VI-F)
             _check(lib.wa_attn_schedule_select(_ptr(self.skipped), self.H, _ptr(self.workspace),
                                                self.ws_bytes, s), "wa_attn_schedule_select")
 
@@ -142,7 +143,7 @@ class HotPath:
         perm = self.perm if self.reorder is not None and not self.host_skip else None
         schedule = self.schedule
         if self.host_skip and schedule == WA_SCHED_AUTO:
-            schedule = WA_SCHED_HEADS_INTERLEAVED
+            schedule = WA_SCHED_DEFAULT
         g = self.g if self.gsrs_p is not None else None
         slices = self.reorder.n_slices if perm is not None else 0
         args = (_ptr(q), _ptr(k), _ptr(v), self.H, self.L, self.d, self.b, _ptr(self.row_ptr),

@@ -52,8 +52,20 @@ extern "C" {
                                         at once, the concurrent-head execution that WaveAlign
                                         VI-B contrasts with sequential heads */
 #define WA_SCHED_AUTO 3 /* the schedule wa_attn_schedule_select wrote into the workspace:
-                           XCD-sliced if some head was reordered, all heads at once (the
+                           XCD-sliced if some head was reordered, WA_SCHED_DEFAULT (the
                            default path) if every head kept its order */
+#define WA_SCHED_DEFAULT 4 /* the default path for heads that all keep their original order
+                              (perm is not read): all heads at once when one head's K and V,
+                              MB * block * head_dim * 4 bytes, take at most
+                              WA_ALL_HEADS_MAX_KV_BYTES, XCD-sliced in the original order
+                              otherwise (wa_default_schedule) */
+
+/* Per-head K + V bytes up to which WA_SCHED_DEFAULT runs all heads at once.  Measured on
+   MI355X over Top-k, banded, Top-p and random masks: all heads at once is faster (up to
+   9%) while a head's K and V take at most 8.4 MB (128 blocks of 128 x 128), and slower
+   (4 to 37%) from 16.6 MB (254 blocks) on, where the XCD-sliced order lets the
+   workgroups of one XCD share one head's K/V blocks in its L2. */
+#define WA_ALL_HEADS_MAX_KV_BYTES (12u << 20)
 
 /* Skip modes of wa_reorder_rows. */
 #define WA_SKIP_ADAPTIVE 0
@@ -237,9 +249,10 @@ int wa_sparse_attn_workspace_size(int32_t H, int32_t L, int32_t head_dim, int32_
  *             reorder's parameter), 0 if unknown.  With perm != NULL and the
  *             XCD-sliced (or AUTO) schedule it must equal the device's XCD count
  *             (wa_schedule_info): slice x of each head's order runs on XCD x.
- *             Ignored when perm is NULL.
- *   schedule  WA_SCHED_NATURAL, WA_SCHED_XCD_SLICED, WA_SCHED_HEADS_INTERLEAVED or
- *             WA_SCHED_AUTO (reads the choice of wa_attn_schedule_select from workspace).
+ *             Ignored when perm is NULL or the schedule is WA_SCHED_DEFAULT.
+ *   schedule  WA_SCHED_NATURAL, WA_SCHED_XCD_SLICED, WA_SCHED_HEADS_INTERLEAVED,
+ *             WA_SCHED_AUTO (reads the choice of wa_attn_schedule_select from workspace)
+ *             or WA_SCHED_DEFAULT (resolved from the sizes, perm not read).
  *             XCD-sliced: workgroup w runs on XCD w mod n_xcd (round-robin dispatch,
  *             n_xcd = the device's XCD count, checked by wa_xcd_placement) and takes
  *             position floor(w / n_xcd) of slice (w mod n_xcd) of its head's order
@@ -295,10 +308,10 @@ int wa_xcd_placement(int32_t n_wg, int32_t block, int32_t* xcd_out, void* stream
 /*
  * wa_attn_schedule_select - [WA §VI-F, Fig. 13: when the adaptive skip leaves every
  * head in its order, execution falls back to the default sparse-attention path]
- * writes into workspace the schedule WA_SCHED_AUTO runs: WA_SCHED_XCD_SLICED if some
- * skipped[h] is 0, WA_SCHED_HEADS_INTERLEAVED (all heads at once) if every one is
- * non-zero.  One small kernel on the device, so the choice follows the reorder
- * without a host synchronisation.
+ * writes into workspace the schedule WA_SCHED_AUTO runs: WA_SCHED_XCD_SLICED (in the
+ * reordered order) if some skipped[h] is 0, WA_SCHED_DEFAULT (the permutation, all
+ * identity, is then not read) if every one is non-zero.  One small kernel on the
+ * device, so the choice follows the reorder without a host synchronisation.
  *   skipped   uint8 [H] from wa_reorder_rows
  *   workspace device buffer of at least wa_sparse_attn_workspace_size bytes, passed to
  *             the wa_sparse_attn_fwd calls that use WA_SCHED_AUTO afterwards
@@ -307,6 +320,17 @@ int wa_xcd_placement(int32_t n_wg, int32_t block, int32_t* xcd_out, void* stream
  */
 int wa_attn_schedule_select(const uint8_t* skipped, int32_t H, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * wa_default_schedule - [WA §VI-F: the default path when no head is reordered] the
+ * schedule WA_SCHED_DEFAULT runs for these sizes (host only, no device work):
+ * WA_SCHED_HEADS_INTERLEAVED if MB * block * head_dim * 4 <= WA_ALL_HEADS_MAX_KV_BYTES
+ * (MB = ceil(L / block)), else WA_SCHED_XCD_SLICED.
+ *   schedule  int32 host out
+ * Errors: WA_ERR_INVALID_ARG (null pointer, L < 1), WA_ERR_UNSUPPORTED (head_dim or
+ * block not 64/128).
+ */
+int wa_default_schedule(int32_t L, int32_t head_dim, int32_t block, int32_t* schedule);
 
 /*
  * wa_sparse_attn_fwd_diag - wa_sparse_attn_fwd that also writes per-row attention

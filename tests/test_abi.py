@@ -39,7 +39,23 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.wa_abi_version() == 3
+    assert lib.wa_abi_version() == 4
+
+
+def test_default_schedule_follows_the_head_size(lib):
+    # All heads at once while one head's K and V (MB * block * head_dim * 4 bytes) take
+    # at most 12 MiB; XCD-sliced in the original order beyond (a host-only call).
+    hi, xcd = caq.WA_SCHED_HEADS_INTERLEAVED, caq.WA_SCHED_XCD_SLICED
+    assert caq.default_schedule(192 * 128, 128, 128) == hi        # 192 blocks: exactly 12 MiB
+    assert caq.default_schedule(192 * 128 + 1, 128, 128) == xcd   # 193 blocks
+    assert caq.default_schedule(57 * 128, 128, 128) == hi
+    assert caq.default_schedule(75600, 128, 128) == xcd
+    assert caq.default_schedule(768 * 64, 64, 64) == hi           # 768 blocks of 64 x 64
+    assert caq.default_schedule(768 * 64 + 1, 64, 64) == xcd
+    out = ctypes.c_int32()
+    assert lib.wa_default_schedule(0, 128, 128, ctypes.byref(out)) == -1
+    assert lib.wa_default_schedule(100, 96, 128, ctypes.byref(out)) == -2
+    assert lib.wa_default_schedule(100, 128, 128, None) == -1
 
 
 def test_host_validation_rejects_bad_arguments(lib):
@@ -89,6 +105,8 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, -1, None, 0, 1,
                                   0.1, fake, fake, None, None, 0, None) == -1
     assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 0, 7,
+                                  0.1, fake, fake, None, None, 0, None) == -1
+    assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 0, 5,
                                   0.1, fake, fake, None, None, 0, None) == -1
     assert lib.wa_sparse_attn_fwd(fake, fake, fake, 1, 128, 128, 128, fake, fake, 1, None, 0, 1,
                                   -0.1, fake, fake, None, None, 0, None) == -1

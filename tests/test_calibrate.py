@@ -52,3 +52,27 @@ def test_stored_profile_loads():
     assert p.ws_min_bytes == c["ws_min_bytes"] and p.flops_min == c["flops_min"]
     assert 0.0 <= p.jaccard_max <= 1.0 + 1e-6
     assert caq.ReorderParams.calibrated(iters=3).iters == 3
+
+
+def test_fit_weighs_wrong_points_by_relative_time_lost():
+    # Two points cannot both be decided right by a work threshold: a small loss at more
+    # work than a large win.  The fit keeps the large win and names the inert cases.
+    pts = [_pt(1e7, 1e11, 0.3, -0.5), _pt(1e7, 2e11, 0.3, 5.0), _pt(1e7, 4e11, 0.3, -0.01)]
+    for p, t in zip(pts, (10.0, 50.0, 100.0)):
+        p["e2e_reordered_ms"] = t - p["gain_ms"] / 2
+        p["e2e_unreordered_ms"] = t + p["gain_ms"] / 2
+    thr = calibrate.fit(pts)
+    assert 1e11 < thr["flops_min"] <= 2e11
+    assert thr["points_correct"] == 2
+    assert set(thr["inert"]) == {"ws_min_bytes", "jaccard_max"}
+    assert calibrate.decide(pts[0], thr) == "work" and calibrate.decide(pts[1], thr) == "reorder"
+
+
+def test_stored_profile_names_its_deciding_cases():
+    path = os.path.join(os.path.dirname(caq.__file__), "calib_mi355x.json")
+    with open(path) as f:
+        c = json.load(f)
+    fams = {p["family"] for p in c["sweep"]}
+    assert {"topk-raster", "topk-hilbert", "neighbour", "random"} <= fams
+    for p in c["sweep"]:
+        assert p["decided_by"] == calibrate.decide(p, c)

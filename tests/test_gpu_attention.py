@@ -91,7 +91,8 @@ def test_output_is_independent_of_execution_order():
     o0, l0, g0, _ = _run(w, schedule=caq.WA_SCHED_NATURAL, with_g=True)
     gen = torch.Generator().manual_seed(5)
     perm = torch.stack([torch.randperm(mb, generator=gen) for _ in range(3)]).to(torch.int32)
-    for sched in (caq.WA_SCHED_NATURAL, caq.WA_SCHED_XCD_SLICED, caq.WA_SCHED_HEADS_INTERLEAVED):
+    for sched in (caq.WA_SCHED_NATURAL, caq.WA_SCHED_XCD_SLICED, caq.WA_SCHED_HEADS_INTERLEAVED,
+                  caq.WA_SCHED_DEFAULT):
         o1, l1, g1, _ = _run(w, perm=perm, schedule=sched, with_g=True)
         assert torch.equal(o0, o1) and torch.equal(l0, l1) and torch.equal(g0, g1)
     # repeated runs are bitwise identical
@@ -191,10 +192,10 @@ def test_distance_with_uniform_attention(shape):
             assert abs(ent[h, i] - np.log(keys.size)) < 1e-3
 
 
-@pytest.mark.parametrize("skip_mode,expect", [(caq.WA_SKIP_ALWAYS, caq.WA_SCHED_HEADS_INTERLEAVED),
+@pytest.mark.parametrize("skip_mode,expect", [(caq.WA_SKIP_ALWAYS, caq.WA_SCHED_DEFAULT),
                                               (caq.WA_SKIP_NEVER, caq.WA_SCHED_XCD_SLICED)])
 def test_auto_schedule_follows_the_skip_flags(skip_mode, expect):
-    """WA_SCHED_AUTO runs all heads at once when every head kept its order and the
+    """WA_SCHED_AUTO runs the default path when every head kept its order and the
     XCD-sliced schedule otherwise; the output is the same either way."""
     dev = gpu()
     w = synth.random_tiny_case(23, heads=3, seq_len=1500, head_dim=128, block=128, density=0.4,
@@ -309,7 +310,7 @@ def test_row_longer_than_the_staged_list():
 
 def test_host_skipped_path_runs_the_default_path():
     """A HotPath whose shape cannot pass the adaptive skip's work rule launches no
-    reorder and runs the all-heads-at-once default path: bitwise the plain call."""
+    reorder and runs the default path: bitwise the plain call."""
     from cache_aware_query_amd.pipeline import HotPath
 
     dev = gpu()
@@ -326,6 +327,6 @@ def test_host_skipped_path_runs_the_default_path():
     hp.reorder_rows(w.x0)
     hp.attention(w.q, w.k, w.v)
     o, lse, _ = caq.sparse_attn_fwd(w.q, w.k, w.v, w.seq_len, w.block, hp.row_ptr, hp.col_idx,
-                                    schedule=caq.WA_SCHED_HEADS_INTERLEAVED)
+                                    schedule=caq.WA_SCHED_DEFAULT)
     torch.cuda.synchronize()
     assert torch.equal(hp.o, o) and torch.equal(hp.lse, lse)
