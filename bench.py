@@ -649,7 +649,12 @@ def main():
                 _log(f"chain {name} not captured ({exc}); timed eagerly")
                 graphs[name] = fn
                 chain_mode = "graph replay where captured, else eager"
-        te = _time_interleaved(graphs, rounds=7, reps=max(2, reps // 2))
+        # Each timing window spans at least about 3 ms of replays, so that the
+        # shortest chains (tens of microseconds) are not timed at event resolution.
+        est = max(_time_calls(fn, 2) for fn in graphs.values())
+        chain_reps = int(min(200, max(2, reps // 2, -(-3.0 // max(est, 1e-3)))))
+        te = _time_interleaved(graphs, rounds=9, reps=chain_reps)
+        detail["e2e_timing_reps"] = chain_reps
         del graphs
         hp.schedule = main_sched
         hp.reorder_rows(w.x0)
