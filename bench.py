@@ -111,14 +111,21 @@ def _counter_profile(workload: str):
     return out
 
 
-def _time_interleaved(fns: dict, rounds: int, reps: int) -> dict:
-    """Median over rounds of the average ms of each fn, the fns taking turns."""
+def _time_interleaved(fns: dict, rounds: int, reps: int, label: str = "") -> dict:
+    """Median over rounds of the average ms of each fn, the fns taking turns.  The
+    order rotates from round to round and every timed window follows one untimed call
+    of the same fn, so that no fn always inherits the clock and cache state that one
+    particular other fn leaves behind."""
     import statistics
 
-    times = {k: [] for k in fns}
-    for _ in range(rounds):
-        for k, fn in fns.items():
-            times[k].append(_time_calls(fn, reps))
+    keys = list(fns)
+    times = {k: [] for k in keys}
+    for r in range(rounds):
+        for k in keys[r % len(keys):] + keys[:r % len(keys)]:
+            fns[k]()
+            times[k].append(_time_calls(fns[k], reps))
+        if label:
+            _log(f"{label}: round {r + 1} of {rounds} done")
     return {k: statistics.median(v) for k, v in times.items()}
 
 
@@ -491,7 +498,9 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    _log(f"{args.warmup} warmup steps done")
     ms_per_step, attn_ms, wall_ms = timed_steps(cold=True)
+    _log(f"{args.steps} timed steps done: {ms_per_step:.3f} ms per step")
     warm_step_ms, warm_attn_ms, _ = timed_steps(cold=False)
     del flush_buf
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -513,6 +522,7 @@ def main():
     if params.skip_mode == caq.WA_SKIP_ADAPTIVE:
         detail["skip_decisions"] = _skip_report(hp, w, params)
     if not args.no_variants:
+        _log("stage times and variants")
         reps = max(3, args.steps // 2)
         # Stage times of the reordered step.
         t_index = _time_calls(lambda: hp.build_index(w.mask), reps)
@@ -589,6 +599,7 @@ def main():
         del q_x, o_x
         ablation["minhash_order"] = hp_mh
         ablation["lsh_order"] = hp_lsh
+        _log("comparator orders built and timed")
 
         def with_schedule(path, sched):
             def run():
@@ -610,7 +621,7 @@ def main():
         }
         for name, hpa in ablation.items():
             variants[name] = with_schedule(hpa, caq.WA_SCHED_XCD_SLICED)
-        t = _time_interleaved(variants, rounds=5, reps=max(2, reps // 2))
+        t = _time_interleaved(variants, rounds=5, reps=max(2, reps // 2), label="attention variants")
         hp.schedule = main_sched
 
         # End to end, reorder cost included: each chain (index, order, attention) timed
@@ -653,7 +664,7 @@ def main():
         # shortest chains (tens of microseconds) are not timed at event resolution.
         est = max(_time_calls(fn, 2) for fn in graphs.values())
         chain_reps = int(min(200, max(2, reps // 2, -(-3.0 // max(est, 1e-3)))))
-        te = _time_interleaved(graphs, rounds=9, reps=chain_reps)
+        te = _time_interleaved(graphs, rounds=9, reps=chain_reps, label="end-to-end chains")
         detail["e2e_timing_reps"] = chain_reps
         del graphs
         hp.schedule = main_sched
@@ -666,13 +677,15 @@ def main():
         lru_heads = range(min(H, 8))
         orders = {"wavealign": hp.perm.cpu().numpy(), "identity": ident,
                   "minhash": hp_mh.perm.cpu().numpy(), "lsh": hp_lsh.perm.cpu().numpy()}
-        detail["locality_proxies"] = {
-            name: {"wave_objective": locality.wave_objective(mask_h, pm, n_xcd, wave),
-                   "distinct_kv_per_wave": round(locality.distinct_kv_per_wave(
-                       mask_h, pm, n_xcd, wave), 1),
-                   "lru_l2_hit_model": round(locality.lru_l2_model(
-                       mask_h, pm, n_xcd, wave, 64, heads=lru_heads), 4)}
-            for name, pm in orders.items()}
+        detail["locality_proxies"] = {}
+        for name, pm in orders.items():
+            detail["locality_proxies"][name] = {
+                "wave_objective": locality.wave_objective(mask_h, pm, n_xcd, wave),
+                "distinct_kv_per_wave": round(locality.distinct_kv_per_wave(
+                    mask_h, pm, n_xcd, wave), 1),
+                "lru_l2_hit_model": round(locality.lru_l2_model(
+                    mask_h, pm, n_xcd, wave, 64, heads=lru_heads), 4)}
+            _log(f"locality proxies of the {name} order done")
         detail["locality_proxies"]["lru_model_heads"] = len(lru_heads)
         del mask_h
         # Speedup gap (WaveAlign §III-A, Fig. 2): the ideal speedup 1/rho of the sparse
