@@ -232,18 +232,93 @@ __device__ void gather_lists(const double2* src, const int32_t* __restrict__ ptr
   }
 }
 
+// The same sums with the index lists read 16 bytes (four entries) per load, so that
+// each load in flight brings four entries: the entries before the list's first
+// 16-byte boundary and after its last one are taken one by one, the aligned
+// four-entry chunks in between go to the G lanes in turn (chunk m to lane m mod G).
+// Lane j adds its head entry (if any), its chunks in ascending order (each chunk's
+// entries in order) and its tail entry (if any); then the same shuffle tree.  The
+// index array must be 16-byte aligned.
+template <int G, int U, typename F>
+__device__ void gather_lists_v4(const double2* src, const int32_t* __restrict__ ptr,
+                                const int32_t* __restrict__ idx, int cap, int n, F emit) {
+  const int t = threadIdx.x, sub = t & (G - 1);
+  for (int r0 = 0; r0 < n; r0 += kThreads / G) {
+    const int r = r0 + t / G;
+    double ax = 0.0, ay = 0.0;
+    if (r < n) {
+      const int lo = min(ptr[r], cap), hi = min(ptr[r + 1], cap);
+      const int a = min((lo + 3) & ~3, hi);  // first 16-byte boundary in the list
+      const int b = max(a, hi & ~3);         // last one
+      for (int k = lo + sub; k < a; k += G) {
+        const double2 v = src[idx[k]];
+        ax += v.x;
+        ay += v.y;
+      }
+      const int4* chunk = reinterpret_cast<const int4*>(idx + a);
+      const int nch = (b - a) >> 2;
+      int m = sub;
+      for (; m + (U - 1) * G < nch; m += U * G) {
+        int4 i[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) i[j] = chunk[m + j * G];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          const double2 v0 = src[i[j].x], v1 = src[i[j].y], v2 = src[i[j].z], v3 = src[i[j].w];
+          ax += v0.x;
+          ay += v0.y;
+          ax += v1.x;
+          ay += v1.y;
+          ax += v2.x;
+          ay += v2.y;
+          ax += v3.x;
+          ay += v3.y;
+        }
+      }
+      for (; m < nch; m += G) {
+        const int4 i = chunk[m];
+        const double2 v0 = src[i.x], v1 = src[i.y], v2 = src[i.z], v3 = src[i.w];
+        ax += v0.x;
+        ay += v0.y;
+        ax += v1.x;
+        ay += v1.y;
+        ax += v2.x;
+        ay += v2.y;
+        ax += v3.x;
+        ay += v3.y;
+      }
+      for (int k = b + sub; k < hi; k += G) {
+        const double2 v = src[idx[k]];
+        ax += v.x;
+        ay += v.y;
+      }
+    }
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) {
+      ax += __shfl_xor(ax, off);
+      ay += __shfl_xor(ay, off);
+    }
+    if (r < n && sub == 0) emit(r, ax, ay);
+  }
+}
+
 // Lanes per list from the mean list length (uniform across the workgroup): four
 // lanes with eight loads each in flight unless the lists are very short (measured
-// on MI355X over 929..2841 blocks per side and 0.4%..20% density).
-__device__ inline int gather_lanes(long long entries, int lists) {
-  return lists > 0 && entries >= 8LL * lists ? 4 : 1;
+// on MI355X over 929..2841 blocks per side and 0.4%..20% density).  Bit 3 of the
+// result selects the four-entry loads (index arrays 16-byte aligned).
+__device__ inline int gather_lanes(long long entries, int lists, bool aligned16) {
+  return (lists > 0 && entries >= 8LL * lists ? 4 : 1) | (aligned16 ? 8 : 0);
 }
 
 template <typename F>
 __device__ void gather_any(int lanes, const double2* src, const int32_t* ptr,
                            const int32_t* idx, int cap, int n, F emit) {
-  if (lanes == 4) gather_lists<4, 8>(src, ptr, idx, cap, n, emit);
-  else gather_lists<1, 8>(src, ptr, idx, cap, n, emit);
+  switch (lanes) {
+    case 12: gather_lists_v4<4, 4>(src, ptr, idx, cap, n, emit); break;
+    case 9: gather_lists_v4<1, 4>(src, ptr, idx, cap, n, emit); break;
+    case 4: gather_lists<4, 8>(src, ptr, idx, cap, n, emit); break;
+    default: gather_lists<1, 8>(src, ptr, idx, cap, n, emit); break;
+  }
 }
 
 // Y = M^T X - c (1^T X) / MB, reading X and writing Y (LDS), from the CSC lists.
@@ -633,7 +708,9 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
   }
   inter = block_sum_i64(inter, redi);
   uni = block_sum_i64(uni, redi);
-  const int glists = gather_lanes(nnz, max(MB, NB));
+  const bool idx16 =
+      ((reinterpret_cast<uintptr_t>(col_idx) | reinterpret_cast<uintptr_t>(csc_idx)) & 15) == 0;
+  const int glists = gather_lanes(nnz, max(MB, NB), idx16);
   const double jac = uni == 0 ? 1.0 : (double)inter / (double)uni;
   if (p.skip_mode == WA_SKIP_ADAPTIVE && !(jac < p.jac_max)) {
     skip_head(jac);
