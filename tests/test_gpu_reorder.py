@@ -178,3 +178,37 @@ def test_dense_mask_keeps_identity_stage1():
     assert torch.isnan(ro.angles).all()
     ro = _gpu_reorder(m, x0, 128, 128, caq.ReorderParams(jaccard_max=0.9))
     assert ro.skipped.cpu().tolist() == [1, 1]
+
+
+@pytest.mark.parametrize("mb,density", [(300, 0.1), (1200, 0.05)])
+def test_unaligned_index_lists_take_the_single_entry_gathers(mb, density):
+    """Index arrays that are not 16-byte aligned are gathered one entry per load; the
+    result equals the four-entry gathers of the aligned copy up to summation order
+    (angles to 1e-12, the same statistics, skip flags and Stage-2 structure).  Both the
+    column-bitmask form (300 blocks) and the list form (1,200 blocks) are covered."""
+    dev = gpu()
+    w = synth.random_tiny_case(17, heads=2, seq_len=mb * 64, head_dim=64, block=64,
+                               density=density, empty_rows=(5,))
+    banner(f"reorder unaligned index lists MB={mb}")
+    idx = caq.build_block_index(w.mask.to(dev))
+
+    def shifted(t):
+        if t is None:
+            return None
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        buf[1:].copy_(t)
+        return buf[1:]   # data pointer 4 bytes past a 16-byte boundary
+    idx_u = caq.BlockIndex(idx.row_ptr, shifted(idx.col_idx), idx.row_nnz, idx.csc_ptr,
+                           shifted(idx.csc_idx), idx.heads, idx.mb, idx.nb)
+    assert idx_u.col_idx.data_ptr() % 16 == 4
+    p = caq.ReorderParams(wave=16, n_slices=4, skip_mode=caq.WA_SKIP_NEVER)
+    x0 = w.x0.to(dev)
+    a = caq.reorder_rows(idx, x0, w.block, w.head_dim, p)
+    b = caq.reorder_rows(idx_u, x0, w.block, w.head_dim, p)
+    torch.cuda.synchronize()
+    assert torch.equal(a.stats, b.stats) and torch.equal(a.skipped, b.skipped)
+    torch.testing.assert_close(a.angles, b.angles, atol=1e-12, rtol=0)
+    m = w.mask.numpy()
+    for h in range(2):
+        _check_structure(b.perm[h].cpu().numpy(), b.angles[h].cpu().numpy(),
+                         m[h].astype(np.int64).sum(1), bool(b.skipped[h]), p)
