@@ -448,7 +448,12 @@ def main():
     # the reordered order otherwise.  A forced skip rule keeps the XCD-sliced schedule, so that "always"
     # measures the identity order under the same schedule as the reordered one.
     main_sched = caq.WA_SCHED_AUTO if args.skip == "adaptive" else caq.WA_SCHED_XCD_SLICED
-    hp = HotPath(H, L, d, b, dev, capacity=nnz, reorder=params, schedule=main_sched, gsrs_p=0.9)
+    # The buffers are sized for this workload's masks: the CSR capacity is its total
+    # selected entries and the per-head capacity its largest head's, allocation bounds a
+    # caller knows from how its masks are made (they bound the skip rules on the host).
+    head_cap = int(w.mask.sum(dim=(1, 2)).max())
+    hp = HotPath(H, L, d, b, dev, capacity=nnz, reorder=params, schedule=main_sched, gsrs_p=0.9,
+                 head_capacity=head_cap)
     _log(f"H={H} L={L} d={d} b={b} MB={mb} nnz={nnz} density={nnz / (H * mb * mb):.4f} "
          f"xcd={n_xcd} cus/xcd={cus} wave={wave} T={args.iters} csc={hp.with_csc}")
 
@@ -515,6 +520,7 @@ def main():
               "skipped_heads": int(hp.skipped.sum().item()),
               "skip_per_head": "".join(str(int(x)) for x in hp.skipped.cpu().tolist()),
               "skip_rule": args.skip,
+              "head_capacity": head_cap,
               "reorder_iters": args.iters,
               "hbm_read_gb_per_launch": (round(prof["hbm_read_bytes_per_launch"] / 1e9, 3)
                                          if "hbm_read_bytes_per_launch" in prof else None),
@@ -601,23 +607,25 @@ def main():
         ablation["lsh_order"] = hp_lsh
         _log("comparator orders built and timed")
 
-        def with_schedule(path, sched):
+        def with_schedule(path, sched, permuted=True):
             def run():
                 path.schedule = sched
-                path.attention(w.q, w.k, w.v)
+                path.attention(w.q, w.k, w.v, permuted=permuted)
             return run
 
         # Attention variants timed in interleaved rounds (medians), so that clock
         # drift during the run does not favour whichever variant runs first.  The
         # head-interleaved order is the concurrent-head execution of WaveAlign
-        # §VI-B ("Original" on the A40).
+        # §VI-B ("Original" on the A40).  The unreordered variants run on the main
+        # path's own buffers (original order, no permutation read), so that buffer
+        # placement does not separate them from the reordered one.
         caq.attn_schedule_select(hp.skipped, hp.workspace)  # AUTO follows hp's skip flags
         variants = {
             "reordered_auto": with_schedule(hp, caq.WA_SCHED_AUTO),
             "reordered_xcd": with_schedule(hp, caq.WA_SCHED_XCD_SLICED),
-            "identity_xcd": with_schedule(hp_id, caq.WA_SCHED_XCD_SLICED),
-            "natural_order": with_schedule(hp_id, caq.WA_SCHED_NATURAL),
-            "heads_interleaved": with_schedule(hp_id, caq.WA_SCHED_HEADS_INTERLEAVED),
+            "identity_xcd": with_schedule(hp, caq.WA_SCHED_XCD_SLICED, False),
+            "natural_order": with_schedule(hp, caq.WA_SCHED_NATURAL, False),
+            "heads_interleaved": with_schedule(hp, caq.WA_SCHED_HEADS_INTERLEAVED, False),
         }
         for name, hpa in ablation.items():
             variants[name] = with_schedule(hpa, caq.WA_SCHED_XCD_SLICED)
@@ -626,21 +634,21 @@ def main():
 
         # End to end, reorder cost included: each chain (index, order, attention) timed
         # as one unit, the chains taking turns, medians over the rounds.
-        def chain(path, order, sched):
+        def chain(path, order, sched, permuted=True):
             def run():
-                path.build_index(w.mask)
+                path.build_index(w.mask, transposed=permuted)
                 order()
                 path.schedule = sched
-                path.attention(w.q, w.k, w.v)
+                path.attention(w.q, w.k, w.v, permuted=permuted)
             return run
         chains = {
             "reordered": chain(hp, lambda: hp.reorder_rows(w.x0), main_sched),
             "minhash": chain(hp_mh, minhash, caq.WA_SCHED_XCD_SLICED),
             "lsh": chain(hp_lsh, lsh, caq.WA_SCHED_XCD_SLICED),
-            "unreordered_identity_xcd": chain(hp_id, lambda: None, caq.WA_SCHED_XCD_SLICED),
-            "unreordered_natural": chain(hp_id, lambda: None, caq.WA_SCHED_NATURAL),
-            "unreordered_heads_interleaved": chain(hp_id, lambda: None,
-                                                   caq.WA_SCHED_HEADS_INTERLEAVED),
+            "unreordered_identity_xcd": chain(hp, lambda: None, caq.WA_SCHED_XCD_SLICED, False),
+            "unreordered_natural": chain(hp, lambda: None, caq.WA_SCHED_NATURAL, False),
+            "unreordered_heads_interleaved": chain(hp, lambda: None,
+                                                   caq.WA_SCHED_HEADS_INTERLEAVED, False),
         }
         # Each chain is captured once as a graph and replayed, so the comparison times
         # the GPU work of the chains, not the host's launch overhead (which dominates
@@ -660,14 +668,15 @@ def main():
                 _log(f"chain {name} not captured ({exc}); timed eagerly")
                 graphs[name] = fn
                 chain_mode = "graph replay where captured, else eager"
-        # Each timing window spans at least about 3 ms of replays, so that the
+        # Each timing window spans at least about 10 ms of replays, so that the
         # shortest chains (tens of microseconds) are not timed at event resolution.
         est = max(_time_calls(fn, 2) for fn in graphs.values())
-        chain_reps = int(min(200, max(2, reps // 2, -(-3.0 // max(est, 1e-3)))))
+        chain_reps = int(min(400, max(2, reps // 2, -(-10.0 // max(est, 1e-3)))))
         te = _time_interleaved(graphs, rounds=9, reps=chain_reps, label="end-to-end chains")
         detail["e2e_timing_reps"] = chain_reps
         del graphs
         hp.schedule = main_sched
+        hp.build_index(w.mask)
         hp.reorder_rows(w.x0)
         # Locality proxies of the orders on the host (WaveAlign §IV-B Problem (1) per
         # wave, distinct K/V blocks per XCD wave, an LRU model of each XCD's L2).

@@ -29,13 +29,20 @@ from . import (WA_SCHED_AUTO, WA_SCHED_DEFAULT, WA_SCHED_XCD_SLICED, WA_SKIP_ADA
 class HotPath:
     def __init__(self, heads: int, seq_len: int, head_dim: int, block: int, device,
                  capacity: int | None = None, reorder: ReorderParams | None = None,
-                 schedule: int = WA_SCHED_XCD_SLICED, gsrs_p: float | None = 0.9):
+                 schedule: int = WA_SCHED_XCD_SLICED, gsrs_p: float | None = 0.9,
+                 head_capacity: int | None = None):
+        # capacity: CSR entries the buffers hold (all heads); head_capacity: an upper
+        # bound on the selected blocks of any one head, if the caller knows one (from
+        # how its masks are made).  Both only bound the adaptive skip's size and work
+        # rules on the host; a head above head_capacity is still attended correctly,
+        # it may just keep its original order.
         self.lib = load_library()
         self.H, self.L, self.d, self.b = heads, seq_len, head_dim, block
         self.mb = -(-seq_len // block)
         self.lp = self.mb * block
         self.device = torch.device(device)
         self.cap = heads * self.mb * self.mb if capacity is None else int(capacity)
+        self.head_cap = None if head_capacity is None else int(head_capacity)
         self.reorder = reorder
         if schedule == WA_SCHED_AUTO and reorder is None:
             raise ValueError("WA_SCHED_AUTO follows the reorder's skip flags; give a reorder")
@@ -75,8 +82,9 @@ class HotPath:
 
     def _decide_on_host(self) -> None:
         # The adaptive skip's size and work rules (WaveAlign §IV-E) bounded on the host:
-        # when even a full mask (MB x NB selected blocks, or the capacity if smaller)
-        # could not pass them, every head keeps its order whatever the mask, so the
+        # when even a full mask (MB x NB selected blocks, or the capacity or the
+        # per-head capacity if smaller) could not pass them, every head keeps its order
+        # whatever the mask, so the
         # reorder is not launched and the attention runs the default path
         # (WA_SCHED_DEFAULT, what WA_SCHED_AUTO would choose), at no cost over not
         # reordering.
@@ -86,6 +94,8 @@ class HotPath:
             return
         ws = float(self.mb * self.b * self.d * 4)
         pairs = min(self.mb * self.mb, self.cap)
+        if self.head_cap is not None:
+            pairs = min(pairs, self.head_cap)
         fmax = 4.0 * self.b * self.b * self.d * pairs
         if not (ws > r.ws_min_bytes and fmax >= r.flops_min):
             self.host_skip = True
@@ -115,12 +125,16 @@ class HotPath:
                           self.H, self.mb, self.mb)
 
     # Individual stages (each enqueues its launches on the current stream).
-    def build_index(self, mask: torch.Tensor) -> None:
+    def build_index(self, mask: torch.Tensor, transposed: bool = True) -> None:
+        """CSR of the mask, and the transposed lists when the reorder needs them
+        (``transposed=False`` skips those: the index of the unreordered path)."""
         lib, s = self.lib, _stream(self.device)
+        csc = transposed and self.with_csc
         _check(lib.wa_build_block_index(_ptr(mask), self.H, self.mb, self.mb, _ptr(self.row_ptr),
                                         _ptr(self.col_idx), self.cap, _ptr(self.row_nnz),
-                                        _ptr(self.csc_ptr), _ptr(self.csc_idx),
-                                        self.cap if self.with_csc else 0, s),
+                                        _ptr(self.csc_ptr if csc else None),
+                                        _ptr(self.csc_idx if csc else None),
+                                        self.cap if csc else 0, s),
                "wa_build_block_index")
 
     def reorder_rows(self, x0: torch.Tensor) -> None:
@@ -138,11 +152,15 @@ class HotPath:
             _check(lib.wa_attn_schedule_select(_ptr(self.skipped), self.H, _ptr(self.workspace),
                                                self.ws_bytes, s), "wa_attn_schedule_select")
 
-    def attention(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
+    def attention(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  permuted: bool = True) -> None:
+        """The attention pass in the reordered order, or with ``permuted=False`` in the
+        original order (the unreordered path, on the same buffers)."""
         lib, s = self.lib, _stream(self.device)
-        perm = self.perm if self.reorder is not None and not self.host_skip else None
+        use_perm = permuted and self.reorder is not None and not self.host_skip
+        perm = self.perm if use_perm else None
         schedule = self.schedule
-        if self.host_skip and schedule == WA_SCHED_AUTO:
+        if not use_perm and schedule == WA_SCHED_AUTO:
             schedule = WA_SCHED_DEFAULT
         g = self.g if self.gsrs_p is not None else None
         slices = self.reorder.n_slices if perm is not None else 0

@@ -8,10 +8,10 @@ import cache_aware_query_amd as caq
 from cache_aware_query_amd.pipeline import HotPath
 
 
-def _path(heads, seq_len, d, b, capacity, **kw):
+def _path(heads, seq_len, d, b, capacity, head_capacity=None, **kw):
     params = caq.ReorderParams(wave=64, n_slices=8, skip_mode=caq.WA_SKIP_ADAPTIVE, **kw)
     return HotPath(heads, seq_len, d, b, "cpu", capacity=capacity, reorder=params,
-                   schedule=caq.WA_SCHED_AUTO, gsrs_p=None)
+                   schedule=caq.WA_SCHED_AUTO, gsrs_p=None, head_capacity=head_capacity)
 
 
 def test_small_shapes_are_skipped_on_the_host():
@@ -23,6 +23,16 @@ def test_small_shapes_are_skipped_on_the_host():
     assert int(hp.skipped.sum()) == 1
     # the capacity bounds the pairs too: 128 x 128 blocks but only 16,000 entries
     assert _path(12, 16384, 128, 128, 16000, flops_min=2.2e11).host_skip
+
+
+def test_a_per_head_capacity_tightens_the_bound():
+    # 929 x 929 blocks of 128 x 128 at d = 128 with 41,016 entries over 24 heads: the
+    # total alone allows a head 3.4e11 FLOP (above 3.17e11), a per-head bound of 2,000
+    # entries at most 1.7e10
+    params = dict(heads=24, seq_len=118800, d=128, b=128, capacity=41016, flops_min=3.17e11)
+    assert not _path(**params).host_skip
+    assert _path(**params, head_capacity=2000).host_skip
+    assert not _path(**params, head_capacity=40000).host_skip
 
 
 def test_large_or_unbounded_shapes_are_decided_on_the_device():
