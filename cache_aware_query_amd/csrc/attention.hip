@@ -43,7 +43,9 @@
 //    contiguous slice of each head's execution order, so each XCD's L2 sees one
 //    contiguous run of the (reordered) schedule and all XCDs stay on one head.  The
 //    head-interleaved order (position w / H of head w % H) runs all heads at once,
-//    the concurrent-head execution WaveAlign compares sequential heads with.
+//    the concurrent-head execution WaveAlign compares sequential heads with; the
+//    default path for unreordered heads takes it for small heads and the
+//    XCD-sliced original order for large ones (WA_SCHED_DEFAULT).
 #include <math.h>
 
 #include <mutex>

@@ -68,7 +68,7 @@ def _same(a, b, nnz):
 
 def test_noalloc_equals_the_workspace_entry_point_on_two_calls():
     lib = caq.load_library()
-    # first call: every head kept its order -> all heads at once; second call, fewer
+    # first call: every head kept its order -> the default path; second call, fewer
     # heads and tokens: heads reordered -> XCD-sliced, read from the same static word
     cases = [(41, 4, 2000, caq.WA_SKIP_ALWAYS), (42, 2, 900, caq.WA_SKIP_NEVER)]
     for seed, heads, seq_len, skip_mode in cases:
