@@ -1,6 +1,6 @@
 """Cache-locality proxies of a query-block execution order, on the host (NumPy).
 
-They judge an order before (or beside) GPU counters.  A head's order is cut, as the
+They rate an order before (or beside) GPU counters.  A head's order is cut, as the
 XCD-sliced schedule runs it, into ``n_slices`` contiguous slices (one per XCD) and
 each slice into waves of ``wave`` positions (the workgroups resident on one XCD at
 once).
