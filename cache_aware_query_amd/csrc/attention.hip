@@ -282,23 +282,15 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // from global memory there is a vector-memory load, and waiting for it waits
   // for every K/V copy in flight as well.
   const int ntiles = e1 - e0;
-  if constexpr (STAGED) {
-    // A well-formed row holds at most NB <= kListCap entries; entries past kListCap
-    // (a malformed, longer row) are read from global memory instead.
-    for (int i = threadIdx.x; i < min(ntiles, kListCap); i += BLOCK * 2) blist[i] = col_idx[e0 + i];
-  }
-  // Q rows (the B operand of S^T): lane holds q[qrow][16*ks + 8*g .. +7].  Their
-  // loads complete here, before any copy is in flight, for the same reason.
+  // Q rows (the B operand of S^T): lane holds q[qrow][16*ks + 8*g .. +7], loaded in
+  // the prologue below.
   bf16x8 qf[T::kKS];
-  {
-    const uint16_t* qp = Q + head_off + (size_t)qrow * D + 8 * g;
+  const uint16_t* qp = Q + head_off + (size_t)qrow * D + 8 * g;
+  auto load_q = [&]() {
 #pragma unroll
     for (int ks = 0; ks < T::kKS; ++ks)
       qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 16 * ks));
-#pragma unroll
-    for (int ks = 0; ks < T::kKS; ++ks) asm volatile("" ::"v"(qf[ks]));
-  }
-  __syncthreads();
+  };
   // List entry of tile t (wave-uniform; t is clamped into the list).
   auto list_entry = [&](int t) {
     t = min(t, ntiles - 1);
@@ -624,18 +616,33 @@ void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     pv(pb, P ? sv1 : sv0, MT);
   };
 
-  // Prologue: K of halves 0 and 1 and V of half 0; S of quarter 0.
+  // Prologue: K of halves 0 and 1 and V of half 0, the staged list and Q; S of
+  // quarter 0.  The first list entries are read straight from the CSR so that the
+  // first copies are issued before the list is staged and before Q is loaded: the
+  // three transfers overlap, and since vector-memory loads retire in issue order,
+  // Q having arrived means the copies have landed as well.  (The loop never waits
+  // on a global load of its own: the list is in LDS and Q in registers.)
   int ids[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ids[i] = list_entry(i);
+  for (int i = 0; i < 4; ++i) ids[i] = __builtin_amdgcn_readfirstlane(col_idx[e0 + min(i, ntiles - 1)]);
   issue_k(ids[0], 0, 0);
   issue_v(ids[0], 0, 0);
-  if (NH > 1) {
-    issue_k(ids[1 / T::kHalves], 1, 1);
-    wait_vmcnt<2 * T::kSubInst>();
+  if (NH > 1) issue_k(ids[1 / T::kHalves], 1, 1);
+  if constexpr (STAGED) {
+    // A well-formed row holds at most NB <= kListCap entries; entries past kListCap
+    // (a malformed, longer row) are read from global memory instead.
+    const int n_st = min(ntiles, kListCap);
+    const int t0 = threadIdx.x;
+    const int first = t0 < n_st ? col_idx[e0 + t0] : 0;
+    load_q();
+    if (t0 < n_st) blist[t0] = first;
+    for (int i = t0 + BLOCK * 2; i < n_st; i += BLOCK * 2) blist[i] = col_idx[e0 + i];
   } else {
-    wait_vmcnt<T::kSubInst>();
+    load_q();
   }
+#pragma unroll
+  for (int ks = 0; ks < T::kKS; ++ks) asm volatile("" ::"v"(qf[ks]));
+  wait_vmcnt<0>();
   __syncthreads();
   compute_s(acc[0], sk0, 0);
   mask_s(acc[0], ids[0], 0);
