@@ -3,8 +3,8 @@
 // i visits in the kernel's inner loop; the row sum is its workload.
 //
 // Integer work, bit-exact by construction: row and column lists are emitted in
-// ascending order with wavefront ballots, counts are exact and the prefix sums
-// are single-workgroup scans.
+// ascending order with wavefront scans and ballots, counts are exact and the
+// prefix sums are single-workgroup scans.
 #include "wa_internal.h"
 
 namespace wa {
@@ -17,45 +17,52 @@ __device__ inline uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
 }
 
-// The mask read four bytes per lane.  Words are counted from the 4-byte aligned
-// address at or below the mask (o = misalignment); a word that does not lie wholly
+// The mask read sixteen bytes per lane.  Chunks are counted from the 16-byte aligned
+// address at or below the mask (o = misalignment); a chunk that does not lie wholly
 // inside the mask is assembled from its in-range bytes, so no byte outside the
-// buffer is read.  Row r covers bytes [o + r*NB, o + r*NB + NB) of that word space.
-struct MaskWords {
-  const uint32_t* aligned;
+// buffer is read.  Row r covers bytes [o + r*NB, o + r*NB + NB) of that chunk space.
+struct MaskChunks {
+  const uint4* aligned;
   const uint8_t* bytes;  // == aligned as bytes
   int64_t o, total;      // misalignment and mask size in bytes
 
-  __device__ explicit MaskWords(const uint8_t* mask, int64_t size) {
+  __device__ explicit MaskChunks(const uint8_t* mask, int64_t size) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(mask);
-    aligned = reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
+    aligned = reinterpret_cast<const uint4*>(a & ~(uintptr_t)15);
     bytes = reinterpret_cast<const uint8_t*>(aligned);
-    o = (int64_t)(a & 3);
+    o = (int64_t)(a & 15);
     total = size;
   }
-  __device__ uint32_t word(int64_t w) const {
-    if (4 * w >= o && 4 * w + 4 <= o + total) return aligned[w];
-    uint32_t x = 0;
-    for (int b = 0; b < 4; ++b) {
-      const int64_t i = 4 * w + b;
-      if (i >= o && i < o + total) x |= (uint32_t)bytes[i] << (8 * b);
+  __device__ uint4 chunk(int64_t c) const {
+    if (16 * c >= o && 16 * c + 16 <= o + total) return aligned[c];
+    uint32_t x[4] = {0, 0, 0, 0};
+    for (int b = 0; b < 16; ++b) {
+      const int64_t i = 16 * c + b;
+      if (i >= o && i < o + total) x[b >> 2] |= (uint32_t)bytes[i] << (8 * (b & 3));
     }
-    return x;
+    return make_uint4(x[0], x[1], x[2], x[3]);
   }
 };
 
-// Flags (bit b) of the non-zero bytes of word w that belong to columns [0, NB) of
-// the row starting at byte rs; *v0 receives the column of byte 0 of the word.
-__device__ inline uint32_t row_word_flags(const MaskWords& mw, int64_t w, int64_t rs, int NB,
-                                          int64_t* v0) {
-  const uint32_t x = mw.word(w);
-  const int64_t c0 = 4 * w - rs;
-  uint32_t f = 0;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int64_t v = c0 + b;
-    if (v >= 0 && v < NB && ((x >> (8 * b)) & 0xffu) != 0) f |= 1u << b;
-  }
+// Bit b of the result: byte b of x is non-zero (b < 4).
+__device__ inline uint32_t nonzero_bytes4(uint32_t x) {
+  x |= x >> 4;
+  x |= x >> 2;
+  x |= x >> 1;
+  x &= 0x01010101u;
+  return (x | (x >> 7) | (x >> 14) | (x >> 21)) & 0xfu;
+}
+
+// Flags (bit b) of the non-zero bytes of chunk c that belong to columns [0, NB) of
+// the row starting at byte rs; *v0 receives the column of byte 0 of the chunk.
+__device__ inline uint32_t row_chunk_flags(const MaskChunks& mc, int64_t c, int64_t rs, int NB,
+                                           int64_t* v0) {
+  const uint4 x = mc.chunk(c);
+  uint32_t f = nonzero_bytes4(x.x) | (nonzero_bytes4(x.y) << 4) | (nonzero_bytes4(x.z) << 8) |
+               (nonzero_bytes4(x.w) << 12);
+  const int64_t c0 = 16 * c - rs;
+  if (c0 < 0) f &= 0xffffu << (int)(-c0);            // bytes before the row's first column
+  if (c0 + 16 > NB) f &= 0xffffu >> (int)(c0 + 16 - NB);  // bytes past its last column
   *v0 = c0;
   return f;
 }
@@ -66,13 +73,13 @@ __global__ __launch_bounds__(256) void k_row_counts(const uint8_t* __restrict__ 
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= rows) return;
-  const MaskWords mw(mask, (int64_t)rows * NB);
-  const int64_t rs = mw.o + (int64_t)r * NB;
-  const int64_t w_end = (rs + NB + 3) / 4;
+  const MaskChunks mc(mask, (int64_t)rows * NB);
+  const int64_t rs = mc.o + (int64_t)r * NB;
+  const int64_t c_end = (rs + NB + 15) / 16;
   int cnt = 0;
-  for (int64_t w = rs / 4 + lane; w < w_end; w += kWave) {
-    int64_t c0;
-    cnt += __popc(row_word_flags(mw, w, rs, NB, &c0));
+  for (int64_t c = rs / 16 + lane; c < c_end; c += kWave) {
+    int64_t v0;
+    cnt += __popc(row_chunk_flags(mc, c, rs, NB, &v0));
   }
   // wavefront sum (integers: exact in any order)
 #pragma unroll
@@ -113,29 +120,47 @@ __global__ __launch_bounds__(1024) void k_col_counts(const uint8_t* __restrict__
 }
 
 // Exclusive prefix sum of n counts into ptr[0..n] (ptr may alias cnt).  One
-// workgroup of 1024 threads walks the array in tiles of 4096 counts: each thread
-// holds four consecutive counts, wavefront shuffles and one LDS pass scan the
-// tile, and the running total carries into the next tile, whose counts are
-// loaded before the current tile is scanned.
+// workgroup of 1024 threads walks the array in tiles of 16,384 counts.  A tile is
+// loaded with coalesced reads (thread t takes counts t, t + 1024, ...) into LDS,
+// where thread t sums its contiguous run of sixteen; a wavefront shuffle scan and
+// one LDS pass give each run its offset, the run's prefixes go back into LDS and
+// leave with coalesced writes.  The next tile's counts are loaded into registers
+// while the current one is scanned; tiles are disjoint and each count is read
+// before its slot is written, so ptr may alias cnt.
 __global__ __launch_bounds__(1024) void k_exclusive_scan(const int32_t* cnt, int32_t* ptr, int n) {
+  constexpr int kPer = 16, kTile = 1024 * kPer;
+  __shared__ int32_t tile[kTile];
   __shared__ int32_t wsum[16];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  auto load4 = [&](int base) {
-    int4 v = make_int4(0, 0, 0, 0);
-    const int i = base + 4 * t;
-    if (i < n) v.x = cnt[i];
-    if (i + 1 < n) v.y = cnt[i + 1];
-    if (i + 2 < n) v.z = cnt[i + 2];
-    if (i + 3 < n) v.w = cnt[i + 3];
-    return v;
+  int32_t nxt[kPer];
+  auto load = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = base + j * 1024 + t;
+      nxt[j] = i < n ? cnt[i] : 0;
+    }
   };
+  load(0);
   int32_t carry = 0;
-  int4 cur = load4(0);
-  for (int base = 0; base < n; base += 4096) {
-    const int4 nxt = base + 4096 < n ? load4(base + 4096) : make_int4(0, 0, 0, 0);
-    const int32_t s4 = cur.x + cur.y + cur.z + cur.w;
-    // Inclusive scan of the per-thread sums across the wavefront.
-    int32_t incl = s4;
+  for (int base = 0; base < n; base += kTile) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) tile[j * 1024 + t] = nxt[j];
+    if (base + kTile < n) load(base + kTile);
+    __syncthreads();
+    // this thread's run: tile[kPer*t .. kPer*t + kPer), read four at a time
+    int32_t x[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer / 4; ++j) {
+      const int4 q = *reinterpret_cast<const int4*>(&tile[kPer * t + 4 * j]);
+      x[4 * j + 0] = q.x;
+      x[4 * j + 1] = q.y;
+      x[4 * j + 2] = q.z;
+      x[4 * j + 3] = q.w;
+    }
+    int32_t own = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) own += x[j];
+    int32_t incl = own;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int32_t y = __shfl_up(incl, off);
@@ -143,49 +168,69 @@ __global__ __launch_bounds__(1024) void k_exclusive_scan(const int32_t* cnt, int
     }
     if (lane == 63) wsum[w] = incl;
     __syncthreads();
-    int32_t before = carry;
+    int32_t run = carry + incl - own;
     int32_t total = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int32_t x = wsum[j];
-      before += j < w ? x : 0;
-      total += x;
+      const int32_t s = wsum[j];
+      run += j < w ? s : 0;
+      total += s;
     }
-    __syncthreads();  // wsum is rewritten by the next tile
-    int32_t run = before + incl - s4;  // exclusive prefix of this thread's first count
-    const int i = base + 4 * t;
-    if (i < n) ptr[i] = run;
-    run += cur.x;
-    if (i + 1 < n) ptr[i + 1] = run;
-    run += cur.y;
-    if (i + 2 < n) ptr[i + 2] = run;
-    run += cur.z;
-    if (i + 3 < n) ptr[i + 3] = run;
+    int32_t pre[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      pre[j] = run;
+      run += x[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kPer / 4; ++j)
+      *reinterpret_cast<int4*>(&tile[kPer * t + 4 * j]) =
+          make_int4(pre[4 * j], pre[4 * j + 1], pre[4 * j + 2], pre[4 * j + 3]);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = base + j * 1024 + t;
+      if (i < n) ptr[i] = tile[j * 1024 + t];
+    }
     carry += total;
-    cur = nxt;
+    __syncthreads();  // tile and wsum are rewritten by the next tile
   }
   if (t == 0) ptr[n] = carry;
 }
 
-// One wavefront per row: ascending column ids of the non-zero bytes.
+// One wavefront per row: ascending column ids of the non-zero bytes.  Each lane
+// takes one 16-byte chunk of the row per pass; an exclusive shuffle scan of the
+// lanes' counts places every lane's columns, in ascending order, after those of
+// the lanes before it.
 __global__ __launch_bounds__(256) void k_fill_rows(const uint8_t* __restrict__ mask, int rows,
                                                    int NB, const int32_t* __restrict__ row_ptr,
                                                    int32_t* __restrict__ col_idx, int64_t cap) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= rows) return;
-  const uint8_t* m = mask + (size_t)r * NB;
+  const MaskChunks mc(mask, (int64_t)rows * NB);
+  const int64_t rs = mc.o + (int64_t)r * NB;
+  const int64_t c_first = rs / 16, c_end = (rs + NB + 15) / 16;
   int64_t base = row_ptr[r];
-  const uint64_t lt = lanemask_lt();
-  for (int v0 = 0; v0 < NB; v0 += kWave) {
-    const int v = v0 + lane;
-    const bool bit = v < NB && m[v] != 0;
-    const uint64_t b = __ballot(bit);
-    if (bit) {
-      const int64_t idx = base + __popcll(b & lt);
-      if (idx < cap) col_idx[idx] = v;
+  for (int64_t c0 = c_first; c0 < c_end; c0 += kWave) {
+    const int64_t c = c0 + lane;
+    int64_t v0 = 0;
+    uint32_t f = c < c_end ? row_chunk_flags(mc, c, rs, NB, &v0) : 0u;
+    const int n = __popc(f);
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
     }
-    base += __popcll(b);
+    int64_t idx = base + (incl - n);
+    while (f != 0) {
+      const int b = __builtin_ctz(f);
+      f &= f - 1;
+      if (idx < cap) col_idx[idx] = (int32_t)(v0 + b);
+      ++idx;
+    }
+    base += __shfl(incl, 63);
   }
 }
 

@@ -12,54 +12,79 @@
 namespace wa {
 namespace {
 
-// One workgroup per query-block row u.  Eight consecutive threads share one CSR
-// entry and each sums a fixed slice of BLOCK/8 rows of it, so a wavefront reads
-// eight whole G rows (8 x BLOCK floats, contiguous in memory) with 16-byte loads;
-// the eight partial sums are combined by a fixed shuffle tree, so W is bitwise
-// reproducible.  exp(G - L) is evaluated as exp2((G - L) log2 e).
-template <int BLOCK>
+// Four consecutive query-block rows per workgroup, their CSR entries taken as one
+// run: eight consecutive threads share an entry and 32 entries are in flight per
+// pass, however the entries fall into the four rows, so long and short rows both
+// keep the workgroup busy.  Thread p of the eight takes the rows 32*j + 4*p + i
+// (i < 4) of its entry, so that each 16-byte load of the eight covers 128 contiguous
+// bytes of the entry's G row and of its query block's LSEs (the same LSEs for every
+// entry of a row, so they come from the cache).  Each thread sums its BLOCK/8 terms
+// in a fixed order and a fixed shuffle tree adds the eight partial sums, so W is
+// bitwise reproducible.  exp(G - L) is evaluated as exp2((G - L) log2 e).  UNROLL
+// passes have their loads issued together: two when rows are long (more bytes in
+// flight), one when they are short (fewer registers, more workgroups resident);
+// the arithmetic of an entry, and so W, is the same either way.
+template <int BLOCK, int UNROLL>
 __global__ __launch_bounds__(256) void k_block_importance(const float* __restrict__ G,
                                                           const float* __restrict__ lse,
                                                           const int32_t* __restrict__ row_ptr,
-                                                          int cap, int MB, int L,
+                                                          int cap, int rows, int MB, int L,
                                                           float* __restrict__ W) {
   constexpr int kParts = 8;                // threads per CSR entry
-  constexpr int kRows = BLOCK / kParts;    // rows per thread
+  constexpr int kVec = BLOCK / 32;         // 16-byte loads per thread, entry and array
   constexpr int kPerPass = 256 / kParts;   // entries per pass of the workgroup
+  constexpr int kUnroll = UNROLL;
   constexpr float kLog2e = 1.4426950408889634f;
-  const int row = blockIdx.x;  // h * MB + u
-  const int h = row / MB, u = row % MB;
+  const int r0 = blockIdx.x * 4;  // rows r0 .. r0+3 (h * MB + u)
   const int part = threadIdx.x % kParts, slot = threadIdx.x / kParts;
-  const int e0 = min(row_ptr[row], cap), e1 = min(row_ptr[row + 1], cap);
-  const int nvalid = min(BLOCK, L - u * BLOCK);
+  // entries of row r0 + k: [eb[k], eb[k + 1])
+  int eb[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) eb[k] = min(row_ptr[min(r0 + k, rows)], cap);
   const size_t lp = (size_t)MB * BLOCK;
-  float lsc[kRows];
-  bool live[kRows];
+  for (int e = eb[0] + slot; e < eb[4]; e += kUnroll * kPerPass) {
+    float4 gv[kUnroll][kVec], lv[kUnroll][kVec];
+    int nvalid[kUnroll];
 #pragma unroll
-  for (int k = 0; k < kRows; ++k) {
-    const int r = part * kRows + k;
-    const float x = r < nvalid ? lse[(size_t)h * lp + (size_t)u * BLOCK + r] : -INFINITY;
-    live[k] = r < nvalid && x != -INFINITY;
-    lsc[k] = live[k] ? x * kLog2e : 0.0f;
-  }
-  const float inv_b = 1.0f / (float)nvalid;
-  for (int e = e0 + slot; e < e1; e += kPerPass) {
-    const float4* gp = reinterpret_cast<const float4*>(G + (size_t)e * BLOCK + part * kRows);
-    float s = 0.0f;
+    for (int x = 0; x < kUnroll; ++x) {
+      const int ex = e + x * kPerPass;
+      const int k = (ex >= eb[1]) + (ex >= eb[2]) + (ex >= eb[3]);
+      const int row = r0 + k;
+      const int h = row / MB, u = row - h * MB;
+      nvalid[x] = min(BLOCK, L - u * BLOCK);
+      const float* gp = G + (size_t)ex * BLOCK + 4 * part;
+      const float* lr = lse + (size_t)h * lp + (size_t)u * BLOCK + 4 * part;
+      const bool in = ex < eb[4];
 #pragma unroll
-    for (int k4 = 0; k4 < kRows / 4; ++k4) {
-      const float4 v = gp[k4];
-      const float gv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = 4 * k4 + j;
-        if (live[k]) s += __builtin_amdgcn_exp2f(fmaf(gv[j], kLog2e, -lsc[k]));
+      for (int j = 0; j < kVec; ++j) {
+        gv[x][j] = in ? *reinterpret_cast<const float4*>(gp + 32 * j)
+                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        // rows at or past L (padding, inside [0, L_pad)) are read but not used
+        lv[x][j] = in ? *reinterpret_cast<const float4*>(lr + 32 * j)
+                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       }
     }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    if (part == 0) W[e] = s * inv_b;
+#pragma unroll
+    for (int x = 0; x < kUnroll; ++x) {
+      const int ex = e + x * kPerPass;
+      float s = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) {
+        const float g4[4] = {gv[x][j].x, gv[x][j].y, gv[x][j].z, gv[x][j].w};
+        const float l4[4] = {lv[x][j].x, lv[x][j].y, lv[x][j].z, lv[x][j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool live = 32 * j + 4 * part + i < nvalid[x] && l4[i] != -INFINITY;
+          if (live) s += __builtin_amdgcn_exp2f(fmaf(g4[i], kLog2e, -(l4[i] * kLog2e)));
+        }
+      }
+      // the eight threads of a group share ex, so they shuffle together even past the
+      // end of the run
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      if (part == 0 && ex < eb[4]) W[ex] = s * (1.0f / (float)nvalid[x]);
+    }
   }
 }
 
@@ -320,12 +345,20 @@ hipError_t launch_block_importance(const float* g, const float* lse, const int32
                                    int64_t cap64, int H, int MB, int L, int block, float* w,
                                    hipStream_t s) {
   const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
-  if (block == 128)
-    hipLaunchKernelGGL(k_block_importance<128>, dim3(H * MB), dim3(256), 0, s, g, lse, row_ptr,
-                       cap, MB, L, w);
-  else
-    hipLaunchKernelGGL(k_block_importance<64>, dim3(H * MB), dim3(256), 0, s, g, lse, row_ptr,
-                       cap, MB, L, w);
+  const int rows = H * MB;
+  const dim3 grid((rows + 3) / 4);
+  // The capacity bounds the entries: at 16 or more per row the rows are long.
+  const bool long_rows = cap >= 16LL * rows;
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, g, lse, row_ptr, cap, rows, MB, L, w);
+  };
+  if (block == 128) {
+    if (long_rows) launch(k_block_importance<128, 2>);
+    else launch(k_block_importance<128, 1>);
+  } else {
+    if (long_rows) launch(k_block_importance<64, 2>);
+    else launch(k_block_importance<64, 1>);
+  }
   return hipGetLastError();
 }
 

@@ -64,14 +64,17 @@ def test_block_index_capacity_truncation():
     assert idx.col_idx.cpu().tolist()[:10] == list(range(8)) + [0, 1]
 
 
-@pytest.mark.parametrize("offset", [1, 2, 3])
+@pytest.mark.parametrize("offset", [1, 2, 3, 7, 8, 15])
 def test_block_index_unaligned_mask_and_odd_rows(offset):
-    """The kernels read the mask four bytes per lane: a mask that starts off a 4-byte
-    boundary, rows whose length is not a multiple of 4, non-zero values other than 1
-    and non-zero bytes right outside the mask must all give the oracle's lists."""
+    """The kernels read the mask four and sixteen bytes per lane: a mask that starts
+    off a 16-byte boundary, rows whose length is not a multiple of 16 (or that take
+    a wavefront two passes), non-zero values other than 1 and non-zero bytes right
+    outside the mask must all give the oracle's lists; 2,100 rows give the prefix
+    sum runs of three counts per thread."""
     dev = gpu()
     rng = np.random.default_rng(offset)
-    for H, MB, NB in ((1, 3, 5), (2, 7, 131), (3, 33, 2), (1, 2, 1)):
+    for H, MB, NB in ((1, 3, 5), (2, 7, 131), (3, 33, 2), (1, 2, 1), (1, 3, 16), (1, 4, 17),
+                      (2, 5, 1100), (3, 700, 4)):
         m = (rng.random((H, MB, NB)) < 0.4).astype(np.uint8) * rng.integers(1, 255, (H, MB, NB),
                                                                              dtype=np.uint8)
         n = H * MB * NB
