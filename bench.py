@@ -362,7 +362,8 @@ def _skip_report(hp, w, params) -> dict:
 
     The rule is run once more on the device with every head's statistics reported,
     whatever the host-side bound decided: s = size (K/V bytes), w = work (selected
-    FLOP), j = similarity (adjacent-row Jaccard), r = reordered."""
+    FLOP of the heaviest head: the work case is decided per call), j = similarity
+    (adjacent-row Jaccard), r = reordered."""
     import numpy as np
 
     import cache_aware_query_amd as caq
@@ -371,10 +372,11 @@ def _skip_report(hp, w, params) -> dict:
     st = ro.stats.cpu().double().numpy()
     skipped = ro.skipped.cpu().numpy().astype(bool)
     by = []
+    call_flops = float(st[:, 3].max())
     for h in range(st.shape[0]):
         if not st[h, 2] > params.ws_min_bytes:
             by.append("s")
-        elif not st[h, 3] >= params.flops_min:
+        elif not call_flops >= params.flops_min:
             by.append("w")
         elif not st[h, 4] < params.jaccard_max:
             by.append("j")

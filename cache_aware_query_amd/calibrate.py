@@ -8,8 +8,12 @@ reorder cost but gives no formula.  This module measures those profiles on the
 local GPU and fits the three thresholds of the skip rule used by wa_reorder_rows:
 
     reorder a head  iff  K/V bytes > ws_min_bytes
-                    and  selected FLOP >= flops_min
+                    and  selected FLOP of the call's heaviest head >= flops_min
                     and  adjacent-row Jaccard < jaccard_max
+
+(the work case is decided per call: the heads of one call are reordered side by
+side, so the call costs what its slowest head costs.  Every head of a sweep point
+has the same density, so there the per-head and per-call work coincide.)
 
 The sweep has a locality axis besides length and density, so that the similarity
 case has something to separate:
@@ -244,8 +248,8 @@ def main(argv=None) -> int:
            "iters": args.iters, "heads": args.heads,
            "timing": "median of 7 calls, caches flushed (1 GiB streamed) before each; a chain "
                      "is index + reorder + attention, or index + attention",
-           "rule": "reorder iff ws_bytes > ws_min_bytes and flops >= flops_min and "
-                   "jaccard < jaccard_max", **thr, "sweep": points}
+           "rule": "reorder iff ws_bytes > ws_min_bytes and flops (of the call's heaviest "
+                   "head) >= flops_min and jaccard < jaccard_max", **thr, "sweep": points}
     with open(args.out, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps({k: v for k, v in out.items() if k != "sweep"}), flush=True)

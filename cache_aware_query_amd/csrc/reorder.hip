@@ -144,6 +144,19 @@ __device__ inline long long block_sum_i64(long long v, long long* red) {
   return s;
 }
 
+__device__ inline long long block_max_i64(long long v, long long* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, (long long)__shfl_xor(v, off));
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  long long s = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) s = max(s, red[i]);
+  return s;
+}
+
 __device__ inline int block_min_i32(int v, int* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
@@ -547,12 +560,23 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
   double* ang_h = angles ? angles + (size_t)h * MB : nullptr;
 
   // ---- statistics and the skip decision (§IV-E) ----
-  // The size and work rules need only the head's NNZ: when they (or WA_SKIP_ALWAYS)
+  // The size and work rules need only NNZ counts: when they (or WA_SKIP_ALWAYS)
   // decide, the head is skipped at once and the adjacent-row similarity, which the
-  // decision did not need, is reported as NaN.
+  // decision did not need, is reported as NaN.  The work rule looks at the heaviest
+  // head of the launch: the heads are reordered side by side, one workgroup each, so
+  // the launch costs what its slowest head costs, and once one head's work pays for
+  // it the other heads are reordered at no extra cost.
   const long long nnz = (long long)rp[MB] - (long long)rp[0];
   const double ws = (double)NB * (double)block * (double)head_dim * 4.0;
   const double flops = 4.0 * (double)block * (double)block * (double)head_dim * (double)nnz;
+  double call_flops = flops;
+  if (p.skip_mode == WA_SKIP_ADAPTIVE) {
+    long long most = 0;
+    for (int hh = t; hh < (int)gridDim.x; hh += kThreads)
+      most = max(most, (long long)row_ptr[(size_t)(hh + 1) * MB] - (long long)row_ptr[(size_t)hh * MB]);
+    most = block_max_i64(most, redi);
+    call_flops = 4.0 * (double)block * (double)block * (double)head_dim * (double)most;
+  }
   auto skip_head = [&](double jac_) {
     if (stats != nullptr && t == 0) {
       double* s_ = stats + (size_t)h * 5;
@@ -570,7 +594,7 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
     }
   };
   if (p.skip_mode == WA_SKIP_ALWAYS ||
-      (p.skip_mode == WA_SKIP_ADAPTIVE && !(ws > p.ws_min && flops >= p.flops_min))) {
+      (p.skip_mode == WA_SKIP_ADAPTIVE && !(ws > p.ws_min && call_flops >= p.flops_min))) {
     skip_head(__longlong_as_double(0x7ff8000000000000ll));
     return;
   }

@@ -127,7 +127,9 @@ typedef struct wa_reorder_params {
   int32_t stage2;      /* 1: NNZ-descending order inside buckets, 0: off                  */
   int32_t skip_mode;   /* WA_SKIP_ADAPTIVE / WA_SKIP_NEVER / WA_SKIP_ALWAYS              */
   double ws_min_bytes; /* reorder only if the head's K/V bytes exceed this               */
-  double flops_min;    /* ... and its selected FLOP are at least this                    */
+  double flops_min;    /* ... and the selected FLOP of the heaviest head of the call
+                          are at least this (the heads are reordered side by side, so
+                          the call costs what its slowest head costs)                    */
   double jaccard_max;  /* ... and its adjacent-row Jaccard similarity is below this      */
 } wa_reorder_params;
 
@@ -143,9 +145,11 @@ typedef struct wa_reorder_params {
  * by modified Gram-Schmidt; a second basis vector whose norm falls to <= 1e-12 of
  * the first is set to zero; each basis vector's sign makes its sum of cubes
  * positive (first entry > 1e-6 positive if |sum| < 1e-6); a mask whose rows are
- * all identical keeps the identity Stage-1 order; the skip rule reorders only if
- * K/V bytes NB*b*d*4 > ws_min_bytes, 4*b*b*d*nnz >= flops_min and the pooled
- * Jaccard similarity of adjacent rows < jaccard_max.
+ * all identical keeps the identity Stage-1 order; the skip rule reorders a head only
+ * if K/V bytes NB*b*d*4 > ws_min_bytes, 4*b*b*d*max_h(nnz_h) >= flops_min (the work
+ * of the call's heaviest head: one head's work pays for the call, and the other
+ * heads are reordered alongside it at no extra cost) and the head's pooled Jaccard
+ * similarity of adjacent rows < jaccard_max.
  *   row_ptr, col_idx, csc_ptr, csc_idx  from wa_build_block_index.  The CSC may be
  *             NULL when the head's mask fits in LDS as column bitmasks:
  *             (MB+NB)*16 + (NB*ceil(MB/32) + NB)*4 <= 155648 bytes (about

@@ -32,11 +32,15 @@ open:
   keep their Stage-1 order (as rows r0, r2, r7 and r5, r6 do in Fig. 7(b)).
 * Adaptive skip (§IV-E names three cases and offline profiles, no formula):
   reorder a head only if (i) its K/V working set NB*b*d*2 bytes * 2 exceeds
-  ``ws_min_bytes`` (the K/V set does not fit the cache), (ii) its selected work
-  4*b*b*d*nnz FLOP is at least ``flops_min`` (enough work to amortise the
-  reorder), and (iii) the pooled Jaccard similarity of adjacent rows,
-  sum_u |R_u & R_u+1| / sum_u |R_u | R_u+1|, is below ``jaccard_max`` (rows are
-  not already local).  An empty pooled union counts as similarity 1.
+  ``ws_min_bytes`` (the K/V set does not fit the cache), (ii) the selected work
+  4*b*b*d*nnz FLOP of the heaviest head reordered in the same call is at least
+  ``flops_min`` (enough work to amortise the reorder), and (iii) the pooled
+  Jaccard similarity of adjacent rows, sum_u |R_u & R_u+1| / sum_u |R_u | R_u+1|,
+  is below ``jaccard_max`` (rows are not already local).  An empty pooled union
+  counts as similarity 1.  The work case is read per call rather than per head:
+  the heads of one call are reordered side by side, so the call costs what its
+  slowest head costs, and once one head's work pays for it the other heads are
+  reordered at no extra cost.  With a single head the two readings agree.
 """
 
 from __future__ import annotations
@@ -175,19 +179,21 @@ def skip_statistics(mask_h: np.ndarray, block: int, head_dim: int) -> np.ndarray
     return np.array([float(nnz), nnz / float(mb * nb), ws, flops, jac])
 
 
-def skip_decision(stats: np.ndarray, p: ReorderParams) -> bool:
-    """True if the head keeps its original order."""
+def skip_decision(stats: np.ndarray, p: ReorderParams, call_flops: float | None = None) -> bool:
+    """True if the head keeps its original order.  ``call_flops`` is the selected
+    FLOP of the heaviest head of the call (the head's own, stats[3], by default)."""
     if p.skip_mode == SKIP_ALWAYS:
         return True
     if p.skip_mode == SKIP_NEVER:
         return False
-    reorder = stats[2] > p.ws_min_bytes and stats[3] >= p.flops_min and stats[4] < p.jaccard_max
+    work = stats[3] if call_flops is None else call_flops
+    reorder = stats[2] > p.ws_min_bytes and work >= p.flops_min and stats[4] < p.jaccard_max
     return not reorder
 
 
 def reorder_head(mask_h: np.ndarray, x0_h: np.ndarray, block: int, head_dim: int,
-                 p: ReorderParams):
-    """WaveAlign Algorithm 2 for one head.
+                 p: ReorderParams, call_flops: float | None = None):
+    """WaveAlign Algorithm 2 for one head (``call_flops``: as in skip_decision).
 
     Returns (perm, skipped, angles, stats); ``perm[pos]`` is the query block run
     at position ``pos``; angles are NaN where Stage 1 did not run.
@@ -196,7 +202,7 @@ def reorder_head(mask_h: np.ndarray, x0_h: np.ndarray, block: int, head_dim: int
     nnz = np.asarray(mask_h).astype(np.int64).sum(axis=1)
     stats = skip_statistics(mask_h, block, head_dim)
     angles = np.full(mb, np.nan)
-    if skip_decision(stats, p):
+    if skip_decision(stats, p, call_flops):
         return np.arange(mb, dtype=np.int64), True, angles, stats
     order = np.arange(mb, dtype=np.int64)
     if p.stage1:
@@ -219,7 +225,11 @@ def reorder_rows(mask: np.ndarray, x0: np.ndarray, block: int, head_dim: int,
     skipped = np.zeros(H, dtype=bool)
     angles = np.full((H, mb), np.nan)
     stats = np.zeros((H, 5))
+    # the work case of the adaptive skip looks at the heaviest head of the call
+    call_flops = max(4.0 * block * block * head_dim * float(np.count_nonzero(mask[h]))
+                     for h in range(H))
     for h in range(H):
-        perm[h], skipped[h], angles[h], stats[h] = reorder_head(mask[h], x0[h], block, head_dim, p)
+        perm[h], skipped[h], angles[h], stats[h] = reorder_head(mask[h], x0[h], block, head_dim, p,
+                                                                call_flops)
         inv[h, perm[h]] = np.arange(mb)
     return perm, inv, skipped, angles, stats

@@ -205,6 +205,33 @@ def test_identical_rows_and_skip_rule():
                                     oracle.ReorderParams(skip_mode=SKIP_NEVER, jaccard_max=0.0))
 
 
+def test_work_case_is_decided_per_call():
+    """The work case looks at the heaviest head of the call: a light head is
+    reordered when a heavier head of the same call pays for the launch, and every
+    head keeps its order when none does."""
+    rng = np.random.default_rng(11)
+    heavy = (rng.random((24, 24)) < 0.5).astype(np.uint8)
+    light = np.zeros((24, 24), dtype=np.uint8)
+    light[np.arange(24), rng.integers(0, 24, 24)] = 1     # one block per row
+    light[np.arange(0, 24, 2), rng.integers(0, 24, 12)] = 1
+    mask = np.stack([heavy, light])
+    x0 = rng.standard_normal((2, 24, 2))
+    f_heavy = 4.0 * 64 * 64 * 64 * int(heavy.sum())
+    f_light = 4.0 * 64 * 64 * 64 * int(light.sum())
+    assert f_light < f_heavy
+    p = oracle.ReorderParams(wave=8, n_slices=1, flops_min=(f_light + f_heavy) / 2, jaccard_max=1.0)
+    # alone, the light head is below the threshold ...
+    assert oracle.skip_decision(oracle.skip_statistics(light, 64, 64), p)
+    assert oracle.reorder_head(light, x0[1], 64, 64, p)[1]
+    # ... beside the heavy head, in one call, it is reordered
+    _, _, skipped, _, st = oracle.reorder_rows(mask, x0, 64, 64, p)
+    assert st[1, 3] == f_light and st[0, 3] == f_heavy
+    assert skipped.tolist() == [False, False]
+    # a threshold above the heaviest head skips both
+    p_hi = oracle.ReorderParams(wave=8, n_slices=1, flops_min=f_heavy + 1, jaccard_max=1.0)
+    assert oracle.reorder_rows(mask, x0, 64, 64, p_hi)[2].tolist() == [True, True]
+
+
 def test_jaccard_is_pooled_over_adjacent_rows():
     m = np.array([[1, 1, 0, 0], [0, 1, 1, 0], [0, 0, 0, 0], [1, 1, 1, 1]], dtype=np.uint8)
     st = oracle.skip_statistics(m, 64, 64)
