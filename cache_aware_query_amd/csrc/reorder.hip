@@ -401,6 +401,7 @@ struct MaskBits {
   const uint32_t* cm;
   const int32_t* cc;
   int MW;
+  int8_t* digits;  // room for the fixed-point digits of apply_mt_mfma, or null
 };
 
 // Y = M^T X - c (1^T X) / MB from the column bitmasks.
@@ -437,6 +438,111 @@ __device__ void apply_mt_bits(const double2* x, double2* y, const MaskBits& mb, 
   __syncthreads();
 }
 
+
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+
+// Rows of the digit table of apply_mt_mfma (seven digits per basis vector).
+constexpr int kDigits = 7;
+
+// Bytes of that table: 2 * kDigits rows of max(MB, NB) rounded up to 16 bytes.
+__host__ __device__ inline size_t mfma_digit_bytes(int MB, int NB) {
+  return (size_t)2 * kDigits * (size_t)(((MB > NB ? MB : NB) + 15) & ~15);
+}
+
+// Y = M^T X - c (1^T X) / MB from the column bitmasks on the matrix cores, exactly.
+// Each basis entry is taken in fixed point, r = x * 2^53 rounded to the nearest
+// integer (|x| <= 1 for the orthonormal basis, so |r| <= 2^53), and written as seven
+// signed base-256 digits d_k, r = sum_k d_k 256^k.  The products sum_u M[u][v] d_k[u]
+// are int8 MFMAs (v_mfma_i32_32x32x16_i8: the 14 digit rows times a 16-row slice of
+// 32 mask columns, the mask bits spread to 0/1 bytes), exact in int32, and the
+// digits are recombined in 64-bit integers: sum_u M[u][v] r_u exactly (at most MB *
+// 2^53 < 2^63), whatever the order.  Y is that sum times 2^-53.  A wavefront takes
+// 32 columns at a time; lane l holds digit row l % 32 and mask column l % 32 of the
+// tile, and rows 8 (l / 32) .. + 7 of each 16-row slice.
+__device__ void apply_mt_mfma(const double2* x, double2* y, const MaskBits& mb, int MB, int NB,
+                              Reducer& red) {
+  const int t = threadIdx.x;
+  double2 s = make_double2(0.0, 0.0);
+  for (int u = t; u < MB; u += kThreads) {
+    s.x += x[u].x;
+    s.y += x[u].y;
+  }
+  s = block_sum2(s, red);
+  const double inv = 1.0 / (double)MB;
+  const int MBp = (MB + 15) & ~15;
+  int8_t* dg = mb.digits;  // [2 * kDigits][MBp]
+  for (int u = t; u < MBp; u += kThreads) {
+    long long r0 = 0, r1 = 0;
+    if (u < MB) {
+      r0 = __double2ll_rn(x[u].x * 0x1p53);
+      r1 = __double2ll_rn(x[u].y * 0x1p53);
+    }
+#pragma unroll
+    for (int k = 0; k < kDigits; ++k) {
+      const long long d0 = ((r0 + 128) & 255) - 128;
+      const long long d1 = ((r1 + 128) & 255) - 128;
+      dg[(size_t)k * MBp + u] = (int8_t)d0;
+      dg[(size_t)(kDigits + k) * MBp + u] = (int8_t)d1;
+      r0 = (r0 - d0) >> 8;
+      r1 = (r1 - d1) >> 8;
+    }
+  }
+  __syncthreads();
+  const int w = t >> 6, l = t & 63;
+  const int g = l >> 5, n = l & 31;
+  const int tiles = (NB + 31) / 32;
+  for (int ct = w; ct < tiles; ct += kWaves) {
+    const int v = ct * 32 + n;
+    // lanes past the last column read column NB - 1; their sums are not stored
+    const uint32_t* col = mb.cm + (size_t)min(v, NB - 1) * mb.MW;
+    const int8_t* arow = dg + (size_t)min(n, 2 * kDigits - 1) * MBp + 8 * g;
+    // A: digits of row n of the table at rows u0 + 8 g .. + 7 (rows 14..31 are zero);
+    // B: mask bits M[u0 + 8 g .. + 7][v] (bits of rows >= MB are 0), one per byte
+    auto operands = [&](int u0, long& a, long& b) {
+      a = n < 2 * kDigits ? *reinterpret_cast<const long*>(arow + u0) : 0l;
+      const uint32_t byte = (col[(u0 + 8 * g) >> 5] >> ((u0 + 8 * g) & 31)) & 0xffu;
+      const uint32_t lo = ((byte & 0xfu) * 0x00204081u) & 0x01010101u;
+      const uint32_t hi = ((byte >> 4) * 0x00204081u) & 0x01010101u;
+      b = (long)(((unsigned long)hi << 32) | lo);
+    };
+    // two accumulators (even and odd row slices) so that consecutive MFMAs do not
+    // wait for each other; integer sums, so the split changes nothing
+    i32x16_t acc = {}, acc1 = {};
+    int u0 = 0;
+    // four row slices per step, their operand reads issued together
+    for (; u0 + 64 <= MBp; u0 += 64) {
+      long a[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) operands(u0 + 16 * q, a[q], b[q]);
+      acc = __builtin_amdgcn_mfma_i32_32x32x16_i8(a[0], b[0], acc, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a[1], b[1], acc1, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_32x32x16_i8(a[2], b[2], acc, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a[3], b[3], acc1, 0, 0, 0);
+    }
+    for (; u0 < MBp; u0 += 16) {
+      long a0, b0;
+      operands(u0, a0, b0);
+      acc = __builtin_amdgcn_mfma_i32_32x32x16_i8(a0, b0, acc, 0, 0, 0);
+    }
+    acc += acc1;
+    // register r holds digit row 8 (r / 4) + 4 g + r % 4 of column v
+    long long px = 0, py = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = 8 * (r / 4) + 4 * g + (r % 4);
+      if (j < kDigits) px += (long long)acc[r] * (1ll << (8 * j));
+      else if (j < 2 * kDigits) py += (long long)acc[r] * (1ll << (8 * (j - kDigits)));
+    }
+    px += __shfl_xor(px, 32);
+    py += __shfl_xor(py, 32);
+    if (g == 0 && v < NB) {
+      const double c = (double)mb.cc[v];
+      y[v] = make_double2((double)px * 0x1p-53 - c * s.x * inv,
+                          (double)py * 0x1p-53 - c * s.y * inv);
+    }
+  }
+  __syncthreads();
+}
 
 // Ascending sort of n (a power of two, at most 4 * kThreads) (key, val) pairs in
 // LDS, ordered by key and then by val; the pairs must be distinct.  Runs of 64 are
@@ -544,6 +650,7 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ csc_ptr, const int32_t* __restrict__ csc_idx, int cap,
     const float* __restrict__ x0, int MB, int NB, int block, int head_dim, DevParams p, int rowbits,
+    int mfma,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm, uint8_t* __restrict__ skipped,
     double* __restrict__ angles, double* __restrict__ stats) {
   extern __shared__ double2 lds[];
@@ -607,14 +714,48 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
     const int MW = (MB + 31) / 32;
     uint32_t* cm = reinterpret_cast<uint32_t*>(lds + MB + NB);
     int32_t* cc = reinterpret_cast<int32_t*>(cm + (size_t)NB * MW);
+    // mfma: the launch left room after the bitmasks for the digit table of the
+    // matrix-core product (16-byte aligned)
+    const size_t digit_off =
+        ((size_t)(MB + NB) * sizeof(double2) + ((size_t)NB * MW + NB) * 4 + 15) & ~(size_t)15;
+    int8_t* digits = mfma ? reinterpret_cast<int8_t*>(reinterpret_cast<char*>(lds) + digit_off)
+                          : nullptr;
     for (int i = t; i < NB * MW; i += kThreads) cm[i] = 0u;
     __syncthreads();
+    // Each wavefront sets the bits of four of its rows at a time, the first 128 entries
+    // of each of the four loaded together (the lists sit in L2: their latency, not
+    // their bytes, is the cost); OR is order-free, so the bitmasks do not depend on it.
     const int w = t >> 6, lane = t & 63;
-    for (int u = w; u < MB; u += kWaves) {
-      const int lo = min(rp[u], cap), hi = min(rp[u + 1], cap);
-      for (int k = lo + lane; k < hi; k += 64) {
-        const int v = col_idx[k];
-        if ((unsigned)v < (unsigned)NB) atomicOr(&cm[(size_t)v * MW + (u >> 5)], 1u << (u & 31));
+    for (int u = w; u < MB; u += 4 * kWaves) {
+      int lo[4], hi[4], vv[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int uu = u + j * kWaves;
+        lo[j] = uu < MB ? min(rp[uu], cap) : 0;
+        hi[j] = uu < MB ? min(rp[uu + 1], cap) : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int k = lo[j] + lane + 64 * m;
+          vv[j][m] = k < hi[j] ? col_idx[k] : -1;
+        }
+      auto set_bit = [&](int uu, int v) {
+        atomicOr(&cm[(size_t)v * MW + (uu >> 5)], 1u << (uu & 31));
+      };
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int uu = u + j * kWaves;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int v = vv[j][m];
+          if ((unsigned)v < (unsigned)NB) set_bit(uu, v);
+        }
+        for (int k = lo[j] + 128 + lane; k < hi[j]; k += 64) {
+          const int v = col_idx[k];
+          if ((unsigned)v < (unsigned)NB) set_bit(uu, v);
+        }
       }
     }
     __syncthreads();
@@ -630,7 +771,7 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
       cc[v] = c;
     }
     __syncthreads();
-    bits = MaskBits{cm, cc, MW};
+    bits = MaskBits{cm, cc, MW, digits};
   }
 
   long long inter = 0, uni = 0;
@@ -771,7 +912,8 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
     qr2_inplace(X, MB, red);
     for (int it = 0; it < p.iters; ++it) {
       if constexpr (BITS) {
-        apply_mt_bits(X, Y, bits, MB, NB, red);
+        if (bits.digits) apply_mt_mfma(X, Y, bits, MB, NB, red);
+        else apply_mt_bits(X, Y, bits, MB, NB, red);
         apply_m_rows(Y, bits.cc, rp, col_idx, cap, MB, NB, glists, red,
                      [&](int u, double2 z) { X[u] = z; });
       } else {
@@ -792,7 +934,8 @@ __global__ __launch_bounds__(kThreads) void k_reorder(
       b11 += xu.y * z.y;
     };
     if constexpr (BITS) {
-      apply_mt_bits(X, Y, bits, MB, NB, red);
+      if (bits.digits) apply_mt_mfma(X, Y, bits, MB, NB, red);
+      else apply_mt_bits(X, Y, bits, MB, NB, red);
       apply_m_rows(Y, bits.cc, rp, col_idx, cap, MB, NB, glists, red, ritz_acc);
     } else {
       apply_mt(X, Y, cp, csc_idx, cap, MB, NB, glists, red);
@@ -1037,6 +1180,11 @@ hipError_t launch_reorder(const int32_t* row_ptr, const int32_t* col_idx, const 
   const size_t stats_bytes = (size_t)kWaves * 2 * ((NB + 31) / 32) * sizeof(uint32_t);
   size_t embed_bytes = use_bits ? reorder_bits_lds_bytes(MB, NB)
                                 : (size_t)(MB + NB) * sizeof(double2);
+  // The column product on the matrix cores when its digit table fits beside the
+  // bitmasks.
+  const size_t mfma_bytes = ((embed_bytes + 15) & ~(size_t)15) + mfma_digit_bytes(MB, NB);
+  const int mfma = use_bits && mfma_bytes <= kBitsLdsLimit ? 1 : 0;
+  if (mfma) embed_bytes = mfma_bytes;
   if (!use_bits && stats_bytes > embed_bytes) embed_bytes = stats_bytes;
   // Row bitmasks for the pair statistics of the transposed-list form, when they fit.
   const size_t rowbits_bytes = (size_t)MB * ((NB + 31) / 32) * sizeof(uint32_t);
@@ -1055,11 +1203,11 @@ hipError_t launch_reorder(const int32_t* row_ptr, const int32_t* col_idx, const 
   const int cap = cap64 > 0x7fffffff ? 0x7fffffff : (int)cap64;
   if (use_bits) {
     hipLaunchKernelGGL(k_reorder<true>, dim3(H), dim3(kThreads), lds, s, row_ptr, col_idx, csc_ptr,
-                       csc_idx, cap, x0, MB, NB, block, head_dim, dp, 0, perm, inv_perm, skipped,
+                       csc_idx, cap, x0, MB, NB, block, head_dim, dp, 0, mfma, perm, inv_perm, skipped,
                        angles, stats);
   } else {
     hipLaunchKernelGGL(k_reorder<false>, dim3(H), dim3(kThreads), lds, s, row_ptr, col_idx,
-                       csc_ptr, csc_idx, cap, x0, MB, NB, block, head_dim, dp, rowbits, perm,
+                       csc_ptr, csc_idx, cap, x0, MB, NB, block, head_dim, dp, rowbits, 0, perm,
                        inv_perm,
                        skipped, angles, stats);
   }
