@@ -201,13 +201,17 @@ __global__ __launch_bounds__(1024) void k_exclusive_scan(const int32_t* cnt, int
 // One wavefront per row: ascending column ids of the non-zero bytes.  Each lane
 // takes one 16-byte chunk of the row per pass; an exclusive shuffle scan of the
 // lanes' counts places every lane's columns, in ascending order, after those of
-// the lanes before it.
+// the lanes before it.  The pass's ids are first placed in the wavefront's own LDS
+// run and then written out 64 consecutive ids per store, so that dense rows leave
+// with coalesced stores.
 __global__ __launch_bounds__(256) void k_fill_rows(const uint8_t* __restrict__ mask, int rows,
                                                    int NB, const int32_t* __restrict__ row_ptr,
                                                    int32_t* __restrict__ col_idx, int64_t cap) {
+  __shared__ int32_t stage[4][kWave * 16];
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= rows) return;
+  int32_t* st = stage[threadIdx.x >> 6];
   const MaskChunks mc(mask, (int64_t)rows * NB);
   const int64_t rs = mc.o + (int64_t)r * NB;
   const int64_t c_first = rs / 16, c_end = (rs + NB + 15) / 16;
@@ -223,14 +227,22 @@ __global__ __launch_bounds__(256) void k_fill_rows(const uint8_t* __restrict__ m
       const int y = __shfl_up(incl, off);
       if (lane >= off) incl += y;
     }
-    int64_t idx = base + (incl - n);
+    int pos = incl - n;  // at most 16 * 63: inside the run
     while (f != 0) {
       const int b = __builtin_ctz(f);
       f &= f - 1;
-      if (idx < cap) col_idx[idx] = (int32_t)(v0 + b);
-      ++idx;
+      st[pos++] = (int32_t)(v0 + b);
     }
-    base += __shfl(incl, 63);
+    const int total = __shfl(incl, 63);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int i = lane; i < total; i += kWave)
+      if (base + i < cap) col_idx[base + i] = st[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the run is rewritten by the next pass
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    base += total;
   }
 }
 
