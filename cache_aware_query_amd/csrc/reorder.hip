@@ -618,7 +618,33 @@ __device__ void stage2_and_write(uint64_t* key, uint32_t* val, int n2, const int
                                  int MB, int NB, int wave, int n_slices, bool stage2,
                                  int32_t* perm_h, int32_t* inv_h) {
   const int t = threadIdx.x;
-  if (stage2) {
+  if (stage2 && wave <= 64) {
+    // Buckets of at most 64 positions: one wavefront sorts a bucket by ranking its
+    // (NB - nnz, position) keys across the lanes, the same order as the sort below.
+    const int s = (MB + n_slices - 1) / n_slices;
+    const int per_slice = (s + wave - 1) / wave;
+    const int w = t >> 6, lane = t & 63;
+    for (int bk = w; bk < n_slices * per_slice; bk += kWaves) {
+      const int x = bk / per_slice, j = bk - x * per_slice;
+      const int lo = x * s + j * wave;
+      const int hi = min(min(lo + wave, (x + 1) * s), MB);
+      const int n = hi - lo;  // uniform; <= 0 past the last row
+      if (n <= 0) continue;
+      const bool has = lane < n;
+      const uint32_t row = has ? val[lo + lane] : 0u;
+      const int nnz_row = has ? min(rp[row + 1], cap) - min(rp[row], cap) : 0;
+      const uint64_t k = has ? ((uint64_t)(NB - nnz_row) << 32) | (uint32_t)(lo + lane) : ~0ull;
+      const uint32_t klo = (uint32_t)k, khi = (uint32_t)(k >> 32);
+      int rank = 0;
+      for (int i = 0; i < n; ++i) {
+        const uint64_t ki = ((uint64_t)__builtin_amdgcn_readlane(khi, i) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane(klo, i);
+        rank += ki < k;
+      }
+      if (has) val[lo + rank] = row;
+    }
+    __syncthreads();
+  } else if (stage2) {
     const int s = (MB + n_slices - 1) / n_slices;
     const int per_slice = (s + wave - 1) / wave;
     for (int pos = t; pos < n2; pos += kThreads) {
