@@ -363,7 +363,10 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len: 
 
     ``out`` may hold preallocated (O, LSE, G) tensors and ``workspace`` a uint8
     buffer of sparse_attn_workspace_size bytes, so that repeated calls allocate
-    nothing.  With ``entropy_out`` and/or ``distance_out`` (float [H, L_pad]) the same
+    nothing and never wait on the device.  Without ``out`` and with ``with_g``, G is
+    sized from the CSR's total, ``row_ptr[-1]``, which is read back to the host: that
+    call synchronises with the stream (the C entry point itself never does).  With
+    ``entropy_out`` and/or ``distance_out`` (float [H, L_pad]) the same
     pass also writes each row's attention entropy and mean attention distance in
     tokens (wa_sparse_attn_fwd_diag).  ``perm_slices`` is the n_slices ``perm`` was
     built with (``Reorder.n_slices``); the XCD-sliced and AUTO schedules need it and
