@@ -221,3 +221,29 @@ def test_unaligned_index_lists_take_the_single_entry_gathers(mb, density):
     for h in range(2):
         _check_structure(b.perm[h].cpu().numpy(), b.angles[h].cpu().numpy(),
                          m[h].astype(np.int64).sum(1), bool(b.skipped[h]), p)
+
+
+@pytest.mark.parametrize("kind,mb,nb", [("hub", 97, 97), ("hub", 300, 300), ("rect", 70, 200),
+                                        ("rect", 200, 70), ("rect", 33, 17)])
+def test_reorder_fixed_point_products_at_their_edges(kind, mb, nb):
+    """The column products of the bitmask form run on the int8 matrix cores in fixed
+    point (basis entries times 2^53, |x| <= 1).  A hub row selecting every block puts
+    most of a basis vector on one row (entries near 1, the top of the digit range);
+    rectangular masks leave partial 16-row slices and 32-column tiles on both sides.
+    Angles to 1e-9 of the oracle, as everywhere."""
+    from types import SimpleNamespace
+    rng = np.random.default_rng(mb * 1000 + nb)
+    m = np.zeros((2, mb, nb), dtype=np.uint8)
+    for h in range(2):
+        if kind == "hub":
+            m[h, 0] = 1
+            m[h, np.arange(mb), rng.integers(0, nb, mb)] = 1
+            m[h, np.arange(mb), np.arange(mb) % nb] = 1
+        else:
+            m[h] = (rng.random((mb, nb)) < 0.15 + 0.1 * h).astype(np.uint8)
+            m[h, np.arange(mb), np.arange(mb) % nb] = 1
+    w = SimpleNamespace(mask=torch.from_numpy(m), x0=torch.from_numpy(rng.uniform(-1, 1, (2, mb, 2)).astype(np.float32)),
+                        block=64, head_dim=64)
+    banner(f"reorder fixed-point products {kind} MB={mb} NB={nb}")
+    assert not caq.reorder_needs_csc(mb, nb)
+    _compare_with_oracle(w, caq.ReorderParams(wave=16, n_slices=4, skip_mode=caq.WA_SKIP_NEVER))
