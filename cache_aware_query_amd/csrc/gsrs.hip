@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void k_block_importance(const float* __restric
     for (int x = 0; x < kUnroll; ++x) {
       const int ex = e + x * kPerPass;
       const int k = (ex >= eb[1]) + (ex >= eb[2]) + (ex >= eb[3]);
-      const int row = r0 + k;
+      const int row = min(r0 + k, rows - 1);  // past the run: a valid row, not read
       const int h = row / MB, u = row - h * MB;
       nvalid[x] = min(BLOCK, L - u * BLOCK);
       const float* gp = G + (size_t)ex * BLOCK + 4 * part;
