@@ -416,7 +416,7 @@ def main():
                          "(a known-size reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(heads would shard across GPUs with no exchange); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
