@@ -77,3 +77,30 @@ def test_lsh_order_structured_and_largest():
                                  density=0.001, empty_rows=(3,))
     banner("lsh order MB=4096")
     _check_lsh(big.mask, 4, wave=64, n_slices=8, stage2=True, seed=9)
+
+
+def _sweep_case(seed):
+    rng = np.random.default_rng(9500 + seed)
+    mb = int(rng.choice([int(rng.integers(1, 40)), int(rng.integers(40, 600)),
+                         int(rng.integers(600, 1500))], p=[0.4, 0.4, 0.2]))
+    w = synth.random_tiny_case(800 + seed, heads=int(rng.integers(1, 4)), seq_len=mb * 64,
+                               head_dim=64, block=64,
+                               density=float(rng.choice([0.005, 0.02, 0.1, 0.4, 0.9])),
+                               diagonal=bool(rng.random() < 0.7),
+                               empty_rows=tuple(int(x) for x in rng.choice(
+                                   mb, size=min(mb, int(rng.integers(0, 3))), replace=False)))
+    return (w, int(rng.choice([1, 2])), int(rng.integers(1, 5)),
+            int(rng.choice([1, 7, 32, 64, 100])), int(rng.choice([1, 2, 3, 8, 16])),
+            bool(rng.random() < 0.7))
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_comparator_random_sweep(seed):
+    """Seeded random sizes (1 to 1,499 blocks), densities, hash and band counts, wave
+    sizes, slice counts (more slices than blocks included) and Stage 2 on or off."""
+    w, n_hash, n_bands, wave, n_slices, stage2 = _sweep_case(seed)
+    banner(f"comparator sweep seed={seed} H={w.mask.shape[0]} MB={w.mask.shape[1]} "
+           f"nnz={int(w.mask.sum())} n_hash={n_hash} n_bands={n_bands} wave={wave} "
+           f"n_slices={n_slices} stage2={stage2}")
+    _check(w.mask, n_hash, wave=wave, n_slices=n_slices, stage2=stage2, seed=seed)
+    _check_lsh(w.mask, n_bands, wave=wave, n_slices=n_slices, stage2=stage2, seed=seed)
