@@ -92,3 +92,49 @@ def test_block_index_unaligned_mask_and_odd_rows(offset):
         assert np.array_equal(idx.col_idx.cpu().numpy()[:total], ci)
         assert np.array_equal(idx.csc_ptr.cpu().numpy(), cp)
         assert np.array_equal(idx.csc_idx.cpu().numpy()[:total], csi)
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_block_index_random_sweep(seed):
+    """Seeded random shapes (rectangular, 1 to 900 blocks a side), densities, byte
+    values, mask offsets and capacities: the CSR and CSC bit-exact up to the capacity,
+    the true totals always, and nothing written at or past the capacity (the output
+    buffers are longer and pre-filled with a sentinel)."""
+    dev = gpu()
+    rng = np.random.default_rng(9900 + seed)
+    H = int(rng.integers(1, 4))
+    MB = int(rng.choice([int(rng.integers(1, 20)), int(rng.integers(20, 900))]))
+    NB = int(rng.choice([int(rng.integers(1, 20)), int(rng.integers(20, 900))]))
+    dens = float(rng.choice([0.0, 0.01, 0.1, 0.5, 1.0]))
+    m = ((rng.random((H, MB, NB)) < dens) *
+         rng.integers(1, 256, (H, MB, NB))).astype(np.uint8)
+    rp, ci, nnz, cp, csi = oracle.block_index((m != 0).astype(np.uint8))
+    total = int(rp[-1])
+    cap = int(rng.choice([total, int(rng.integers(0, total + 1)), H * MB * NB]))
+    offset = int(rng.integers(0, 16))
+    n = H * MB * NB
+    buf = torch.full((offset + n + 16,), 255, dtype=torch.uint8, device=dev)
+    buf[offset:offset + n] = torch.from_numpy(m.reshape(-1)).to(dev)
+    mask = buf[offset:offset + n].view(H, MB, NB)
+    i32 = dict(dtype=torch.int32, device=dev)
+    row_ptr = torch.empty(H * MB + 1, **i32)
+    row_nnz = torch.empty(H * MB, **i32)
+    csc_ptr = torch.empty(H * NB + 1, **i32)
+    col_idx = torch.full((cap + 64,), -7, **i32)
+    csc_idx = torch.full((cap + 64,), -7, **i32)
+    banner(f"block_index sweep seed={seed} H={H} MB={MB} NB={NB} density={dens} "
+           f"total={total} cap={cap} offset={offset}")
+    lib = caq.load_library()
+    caq._check(lib.wa_build_block_index(caq._ptr(mask), H, MB, NB, caq._ptr(row_ptr),
+                                        caq._ptr(col_idx), cap, caq._ptr(row_nnz),
+                                        caq._ptr(csc_ptr), caq._ptr(csc_idx), cap,
+                                        caq._stream(dev)), "wa_build_block_index")
+    torch.cuda.synchronize()
+    kept = min(cap, total)
+    np.testing.assert_array_equal(row_ptr.cpu().numpy(), rp)
+    np.testing.assert_array_equal(row_nnz.cpu().numpy(), nnz)
+    np.testing.assert_array_equal(csc_ptr.cpu().numpy(), cp)
+    got_c, got_t = col_idx.cpu().numpy(), csc_idx.cpu().numpy()
+    np.testing.assert_array_equal(got_c[:kept], ci[:kept])
+    np.testing.assert_array_equal(got_t[:kept], csi[:kept])
+    assert (got_c[kept:] == -7).all() and (got_t[kept:] == -7).all()

@@ -369,3 +369,27 @@ def test_gsrs_schedule_matches_the_oracle_step_by_step():
     from helpers import assert_attention_close
     assert_attention_close(np64(gs.sparse.o)[:, :L], gs.sparse.lse.cpu().numpy().astype(np.float64)[:, :L],
                            o_ref[:, :L], lse_ref[:, :L], "last schedule step")
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_topp_random_sweep(seed):
+    """Seeded random shapes (rows of up to 1,600 candidates: every register-sort size and
+    the LDS sort), densities, thresholds p in (0, 1] and weights with ties, one-hot,
+    uniform and peaked rows: the kept sets bit-exact for the same W."""
+    dev = gpu()
+    rng = np.random.default_rng(9700 + seed)
+    H = int(rng.integers(1, 4))
+    mb = int(rng.integers(1, 40))
+    nb = int(rng.choice([int(rng.integers(1, 70)), int(rng.integers(70, 600)),
+                         int(rng.integers(600, 1600))]))
+    dens = float(rng.choice([0.02, 0.2, 0.6, 1.0]))
+    p = float(rng.choice([float(rng.uniform(0.05, 1.0)), 1.0, 0.9]))
+    mask = (rng.random((H, mb, nb)) < dens).astype(np.uint8)
+    mask[0, 0, 0] = 1  # at least one candidate, so that the index arrays are not empty
+    rp, ci, _, _, _ = oracle.block_index(mask)
+    w = _random_weights(rng, rp)
+    banner(f"topp sweep seed={seed} H={H} MB={mb} NB={nb} density={dens} p={p}")
+    sel = caq.topp_select(torch.from_numpy(w).to(dev), torch.from_numpy(rp.astype(np.int32)).to(dev),
+                          torch.from_numpy(ci.astype(np.int32)).to(dev), H, mb, nb, p)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), oracle.topp_select(w, rp, ci, H, mb, nb, p))
