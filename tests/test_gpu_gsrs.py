@@ -318,11 +318,15 @@ def test_gsrs_schedule_matches_the_oracle_step_by_step():
     the sets compare bit for bit), W at every search within the dense-pass tolerance
     of the oracle's W over the same candidates, and the last step's O and LSE against
     the oracle's attention under the last mask."""
-    dev = gpu()
     w = synth.make_workload("gsrs75k", device="cuda", heads=2, grid=(2, 45, 80))
+    _schedule_vs_oracle(w, (2, 4, 6), (0.95, 0.9, 0.8), 8)
+
+
+def _schedule_vs_oracle(w, search, thresholds, steps):
+    dev = gpu()
     H, mb = w.mask.shape[0], w.mask.shape[1]
-    search, thresholds, steps = (2, 4, 6), (0.95, 0.9, 0.8), 8
-    banner(f"gsrs schedule vs oracle H={H} MB={mb} searches={search}")
+    banner(f"gsrs schedule vs oracle H={H} MB={mb} steps={steps} searches={search} "
+           f"p={thresholds}")
     states = synth.drift_states(w, len(search) + 1)
     n_xcd = caq.schedule_info(0, w.head_dim)[0]
     params = caq.ReorderParams(wave=64, n_slices=n_xcd, iters=5, skip_mode=caq.WA_SKIP_NEVER)
@@ -369,6 +373,22 @@ def test_gsrs_schedule_matches_the_oracle_step_by_step():
     from helpers import assert_attention_close
     assert_attention_close(np64(gs.sparse.o)[:, :L], gs.sparse.lse.cpu().numpy().astype(np.float64)[:, :L],
                            o_ref[:, :L], lse_ref[:, :L], "last schedule step")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_gsrs_schedule_random_sweep(seed):
+    """Seeded random schedules against oracle.gsrs_schedule: grid, head count, step
+    count, search steps (a first search at step 0, no warmup, included) and thresholds."""
+    rng = np.random.default_rng(9300 + seed)
+    grid = [(1, 20, 40), (2, 30, 40), (3, 24, 40), (2, 45, 80)][int(rng.integers(0, 4))]
+    steps = int(rng.integers(2, 10))
+    # searches before the last step, so that the last step reuses a mask (the step whose
+    # output is compared with the oracle's attention)
+    n_search = int(rng.integers(1, min(4, steps - 1) + 1))
+    search = tuple(sorted(int(x) for x in rng.choice(steps - 1, size=n_search, replace=False)))
+    thresholds = tuple(round(float(x), 3) for x in rng.uniform(0.5, 0.99, size=n_search))
+    w = synth.make_workload("gsrs75k", device="cuda", heads=int(rng.integers(1, 3)), grid=grid)
+    _schedule_vs_oracle(w, search, thresholds, steps)
 
 
 @pytest.mark.parametrize("seed", range(48))
