@@ -8,7 +8,11 @@ head count, diagonal and empty rows from its seed, then checks:
 - the block weights W, and each query block's weights summing to 1;
 - the Top-p sets for the GPU's own W, bit for bit;
 - the reorder's permutations (each a permutation of the head's query blocks);
-- O, LSE and G under those permutations, bitwise the same as in the original order.
+- O, LSE and G under those permutations, bitwise the same as in the original order;
+- the explicit path (Q blocks and mask rows gathered into the new order, O and LSE
+  scattered back), bitwise the same as the fused path;
+- the row entropy and mean attention distance of the diagnostics pass, with O and LSE
+  unchanged by asking for them.
 """
 
 import numpy as np
@@ -108,3 +112,30 @@ def test_random_case_through_the_path(seed):
         torch.cuda.synchronize()
         assert torch.equal(o1, o) and torch.equal(lse1, lse)
         assert torch.equal(g1[:nnz], g[:nnz])
+
+    # the explicit path: gather, run in the new order, scatter back
+    o_plain, lse_plain, _ = caq.sparse_attn_fwd(q, k, v, L, b, idx.row_ptr, idx.col_idx)
+    qg = caq.gather_blocks(q, ro.perm, b)
+    idx_g = caq.build_block_index(caq.gather_blocks(mask, ro.perm, 1))
+    o_g, lse_g, _ = caq.sparse_attn_fwd(qg, k, v, L, b, idx_g.row_ptr, idx_g.col_idx)
+    o_e = caq.scatter_blocks(o_g, ro.perm, b)
+    lse_e = caq.scatter_blocks(lse_g, ro.perm, b)
+    torch.cuda.synchronize()
+    assert torch.equal(o_e, o_plain) and torch.equal(lse_e, lse_plain)
+
+    # diagnostics: entropy LSE - E[z] and mean distance E|i - j| of every row
+    ent = torch.empty(H, mb * b, dtype=torch.float32, device=dev)
+    dist = torch.empty_like(ent)
+    o_d, lse_d, _ = caq.sparse_attn_fwd(q, k, v, L, b, idx.row_ptr, idx.col_idx,
+                                        entropy_out=ent, distance_out=dist)
+    torch.cuda.synchronize()
+    assert torch.equal(o_d, o_plain) and torch.equal(lse_d, lse_plain)
+    m = w.mask.numpy()
+    ref_e = oracle.attention_entropy(np64(w.q), np64(w.k), m, L, b, w.scale)[:, :L]
+    ref_d = oracle.attention_distance(np64(w.q), np64(w.k), m, L, b, w.scale)[:, :L]
+    ent_g, dist_g = ent.cpu().numpy()[:, :L], dist.cpu().numpy()[:, :L]
+    assert np.all(np.isfinite(ent_g)) and np.all(np.isfinite(dist_g))
+    np.testing.assert_allclose(ent_g, ref_e, rtol=0, atol=2e-2, err_msg=f"seed {seed} entropy")
+    # bf16 probabilities: |error| < 2^-8 L per row (the bound of the diagnostics test)
+    err = np.abs(dist_g - ref_d)
+    assert err.max() < 2.0 ** -8 * max(L, 1), (seed, err.max())
