@@ -56,6 +56,12 @@ def _attn_compulsory_bytes(H: int, lp: int, d: int, b: int, nnz: int, with_g: bo
             + 4.0 * (H * (lp // b) + 1) + 4.0 * nnz)
 
 
+def _importance_bytes(H: int, lp: int, b: int, nnz: int, mb: int) -> float:
+    """Compulsory HBM bytes of one block-importance launch: G read (b floats per CSR
+    entry), the row LSE read, W written (one float per entry) and the CSR row pointers."""
+    return 4.0 * (nnz * b + H * lp + nnz + H * mb + 1)
+
+
 def _roofline(flops: float, alg_bytes: float, attn_ms: float, traffic) -> dict:
     """The roofline of the attention launch: its operational intensity (FLOP over
     compulsory bytes) decides the roof.  Above the ridge (312.5 FLOP/B) the bound is the
@@ -536,6 +542,7 @@ def main():
         t_index = _time_calls(lambda: hp.build_index(w.mask), reps)
         t_reorder = _time_calls(lambda: hp.reorder_rows(w.x0), reps)
         t_select = _time_calls(hp.select, reps)
+        t_importance = _time_calls(hp.importance, reps)
         # The same kernel without reordering (identity order; its index has no
         # transposed lists), and the stage ablation (WaveAlign Fig. 12, every head
         # reordered), each with buffers of its own.
@@ -726,6 +733,11 @@ def main():
                        "reorder_ms": round(t_reorder, 4),
                        "gsrs_select_ms": round(t_select, 4),
                        "index_ms_without_reorder": round(t_index_id, 4)})
+        imp_gbs = _importance_bytes(H, mb * b, b, nnz, mb) / (t_importance * 1e-3) / 1e9
+        detail["block_importance"] = {"ms": round(t_importance, 4), "bound": "hbm",
+                                      "achieved_gb_per_s": round(imp_gbs, 1),
+                                      "peak_gb_per_s": PEAK_HBM_GBS,
+                                      "frac": round(imp_gbs / PEAK_HBM_GBS, 4)}
         detail.update({f"attn_ms_{k}": round(v, 4) for k, v in t.items()})
         detail["minhash_order_ms"] = round(t_minhash, 4)
         detail["lsh_order_ms"] = round(t_lsh, 4)

@@ -60,3 +60,9 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_importance_bytes_by_hand():
+    # H = 2, L_pad = 256, b = 128, nnz = 5, MB = 2: G 5 * 128 * 4 B, LSE 2 * 256 * 4 B,
+    # W 5 * 4 B, row_ptr (2 * 2 + 1) * 4 B
+    assert bench._importance_bytes(2, 256, 128, 5, 2) == 2560 + 2048 + 20 + 20
