@@ -94,6 +94,71 @@ def test_full_size_gsrs_dense_pass_sampled():
             banner(f"gsrs75k h={h} u={u} kept {int(sel[h, u].sum())} of {mb}")
 
 
+def _row_csr(cols, mb):
+    """One-row CSR of the given block ids (ascending) for the oracle's per-row calls."""
+    sub = np.zeros((1, 1, mb), dtype=np.uint8)
+    sub[0, 0, cols] = 1
+    rp, ci, _, _, _ = oracle.block_index(sub)
+    return rp, ci
+
+
+def test_full_size_gsrs_search_step_sampled():
+    """The GSRS search step at full size, in the configuration the bench times (the
+    calibrated reorder), checked on sampled query blocks: S1 is Top-p at 0.9 of the
+    dense pass's W (bit-exact); the pass over S1 gives W within tolerance of the
+    oracle's over the same candidates; S2 is Top-p at 0.8 of that W (bit-exact) and
+    lies inside S1 everywhere; the pass over S2 matches the oracle's attention."""
+    from cache_aware_query_amd.pipeline import GsrsSearch
+    dev = gpu()
+    banner("full-size gsrs75k search step: generating")
+    w = synth.make_workload("gsrs75k", device=dev)
+    H, mb = w.mask.shape[0], w.mask.shape[1]
+    L, b, d = w.seq_len, w.block, w.head_dim
+    n_xcd, _, wave = caq.schedule_info(0, d)
+    params = caq.ReorderParams.calibrated(wave=wave, n_slices=n_xcd, iters=5)
+    gs = GsrsSearch(H, L, d, b, dev, reorder=params, p1=0.9, p2=0.8)
+    banner(f"full-size gsrs75k search step: H={H} MB={mb}")
+    gs.step(w.q, w.k, w.v, w.x0)
+    torch.cuda.synchronize()
+    m1, m2 = gs.mask1.cpu().numpy(), gs.mask2.cpu().numpy()
+    assert not (m2 > m1).any(), "S2 must lie inside S1"
+    rp_d, rp_1 = gs.dense.row_ptr.cpu().numpy(), gs.s1.row_ptr.cpu().numpy()
+    rng = np.random.default_rng(13)
+    for h in sorted(set([0, H - 1, int(rng.integers(H))])):
+        qh, kh, vh = (np64(t[h:h + 1]) for t in (w.q, w.k, w.v))
+        for u in sorted(set([mb - 1, int(rng.integers(mb)), int(rng.integers(mb))])):
+            r = h * mb + u
+            # S1: Top-p of the dense pass's W, every block a candidate
+            w_d = gs.dense.w[rp_d[r]:rp_d[r + 1]].cpu().numpy()
+            rp, ci = _row_csr(np.arange(mb), mb)
+            np.testing.assert_array_equal(m1[h, u], oracle.topp_select(w_d, rp, ci, 1, 1, mb,
+                                                                       0.9)[0, 0])
+            # the pass over S1: W over the S1 candidates
+            cols1 = np.flatnonzero(m1[h, u])
+            w_1 = gs.s1.w[rp_1[r]:rp_1[r + 1]].cpu().numpy()
+            assert w_1.size == cols1.size
+            rp, ci = _row_csr(cols1, mb)
+            sub = np.zeros((1, mb, mb), dtype=np.uint8)
+            sub[0, u, cols1] = 1
+            srp, sci, _, _, _ = oracle.block_index(sub)
+            g_ref, lse_ref = oracle.block_lse(qh, kh, srp, sci, L, b, w.scale)
+            w_ref = oracle.block_importance(g_ref, lse_ref, srp, L, b)
+            np.testing.assert_allclose(w_1.astype(np.float64), w_ref, atol=2e-4, rtol=1e-3,
+                                       err_msg=f"W over S1 h={h} u={u}")
+            # S2: Top-p at 0.8 of the GPU's W over S1
+            np.testing.assert_array_equal(m2[h, u], oracle.topp_select(w_1, rp, ci, 1, 1, mb,
+                                                                       0.8)[0, 0])
+            # the pass over S2
+            r0, r1 = u * b, min((u + 1) * b, L)
+            rows = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, size=6)]))
+            o_ref, l_ref = oracle.masked_attention_rows(qh[0], kh[0], vh[0], m2[h], rows, L, b,
+                                                        w.scale)
+            assert_attention_close(np64(gs.s2.o[h])[rows],
+                                   gs.s2.lse[h].cpu().numpy().astype(np.float64)[rows],
+                                   o_ref, l_ref, f"S2 pass h={h} u={u}")
+            banner(f"gsrs75k search h={h} u={u}: S1 {cols1.size}, S2 {int(m2[h, u].sum())} of {mb}")
+
+
 def test_more_blocks_than_the_staged_list_cap():
     """2,100 query blocks (block 64): the attention kernel reads its lists from global
     memory, the reorder gathers through the transposed lists and sorts 4,096 keys."""
